@@ -1,0 +1,241 @@
+"""fp64 CPU oracle for exact softmax attention.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the ``smoke()`` check and
+by the CPU-baseline leg of ``bench.py``.  The product path (the HIP library
+and its binding) never imports, links or calls anything here, and this module
+imports nothing from it.
+
+The arithmetic lives in ``ref_attn.c`` (plain C, OpenMP over rows, no BLAS);
+this file only compiles it with gcc and marshals numpy arrays.  All functions
+take and return float64 arrays of shape [B, H, N, d] (lse: [B, H, N]) and an
+optional uint8 block mask [nb, nb], nb = ceil(N / 128).
+
+Every function is pinned by tests/test_oracle.py against facts that do not
+come from this code: a brute-force evaluation with a different softmax
+formula, closed forms, invariances and central finite differences.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ref_attn.c")
+_LIB = os.path.join(_HERE, "libref_attn.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = False) -> str:
+    """Compile ref_attn.c into libref_attn.so with gcc (fp64, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Lib:
+    """ctypes view of one compiled copy of ref_attn.c."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        c_int, c_double = ctypes.c_int, ctypes.c_double
+        lib.ref_num_threads.restype = c_int
+        lib.ref_attn_probs.argtypes = [_dp, _dp, c_int, c_int, c_double, c_int, _u8p, _dp, _dp]
+        lib.ref_attn_fwd.argtypes = [_dp, _dp, _dp, c_int, c_int, c_int, c_int, c_double, c_int,
+                                     _u8p, _dp, _dp]
+        lib.ref_attn_fwd_rows.argtypes = [_dp, _dp, _dp, c_int, c_int, c_int, c_int, c_double,
+                                          c_int, _u8p, _i64p, c_int, _dp, _dp]
+        lib.ref_attn_fwd_online.argtypes = [_dp, _dp, _dp, c_int, c_int, c_int, c_int, c_double,
+                                            c_int, _u8p, c_int, _dp, _dp]
+        lib.ref_attn_bwd.argtypes = [_dp, _dp, _dp, _dp, c_int, c_int, c_int, c_int, c_double,
+                                     c_int, _u8p, _dp, _dp, _dp, _dp, _dp, _dp]
+        for f in ("ref_attn_probs", "ref_attn_fwd", "ref_attn_fwd_rows", "ref_attn_fwd_online",
+                  "ref_attn_bwd"):
+            getattr(lib, f).restype = c_int
+        self.lib = lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = _Lib(_LIB).lib
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all cores)."""
+    return int(_load().ref_num_threads())
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a: Optional[np.ndarray], t=_dp):
+    if a is None:
+        return ctypes.cast(None, t)
+    return a.ctypes.data_as(t)
+
+
+def _mask(mask, N: int):
+    if mask is None:
+        return None
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    nb = (N + 127) // 128
+    if m.shape != (nb, nb):
+        raise ValueError(f"mask must be [{nb}, {nb}], got {m.shape}")
+    return m
+
+
+def _shape(q):
+    if q.ndim != 4:
+        raise ValueError("expected [B, H, N, d]")
+    return q.shape
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise MemoryError(f"oracle {what} failed (allocation)")
+
+
+def attn_fwd(q, k, v, scale: float, causal: bool = False, mask=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact attention forward: (O [B,H,N,d], lse [B,H,N]) from the definition."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = _shape(q)
+    m = _mask(mask, N)
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    rc = _load().ref_attn_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(causal),
+                              _ptr(m, _u8p), _ptr(o), _ptr(lse))
+    _check(rc, "fwd")
+    return o, lse
+
+
+def attn_fwd_rows(q, k, v, scale: float, rows, causal: bool = False, mask=None):
+    """Output rows only: rows is [R, 2] of (b*H + h, i).  Returns (O [R, d], lse [R])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = _shape(q)
+    m = _mask(mask, N)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    if r.ndim != 2 or r.shape[1] != 2:
+        raise ValueError("rows must be [R, 2]")
+    if r.size and (r[:, 0].min() < 0 or r[:, 0].max() >= B * H or r[:, 1].min() < 0 or r[:, 1].max() >= N):
+        raise ValueError("row index out of range")
+    o = np.empty((r.shape[0], d), dtype=np.float64)
+    lse = np.empty((r.shape[0],), dtype=np.float64)
+    rc = _load().ref_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(causal),
+                                   _ptr(m, _u8p), _ptr(r, _i64p), r.shape[0], _ptr(o), _ptr(lse))
+    _check(rc, "fwd_rows")
+    return o, lse
+
+
+def attn_fwd_online(q, k, v, scale: float, chunk: int, causal: bool = False, mask=None):
+    """Online-softmax forward scanning keys in chunks of ``chunk`` (same outputs as attn_fwd)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = _shape(q)
+    m = _mask(mask, N)
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    rc = _load().ref_attn_fwd_online(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale),
+                                     int(causal), _ptr(m, _u8p), int(chunk), _ptr(o), _ptr(lse))
+    _check(rc, "fwd_online")
+    return o, lse
+
+
+def attn_probs(q_head, k_head, scale: float, causal: bool = False, mask=None):
+    """P [N, N] and lse [N] of one head (q_head, k_head: [N, d])."""
+    q, k = _f64(q_head), _f64(k_head)
+    N, d = q.shape
+    m = _mask(mask, N)
+    P = np.empty((N, N), dtype=np.float64)
+    lse = np.empty((N,), dtype=np.float64)
+    rc = _load().ref_attn_probs(_ptr(q), _ptr(k), N, d, float(scale), int(causal), _ptr(m, _u8p),
+                                _ptr(P), _ptr(lse))
+    _check(rc, "probs")
+    return P, lse
+
+
+def attn_bwd(q, k, v, do, scale: float, causal: bool = False, mask=None, return_fwd: bool = False):
+    """Gradients (dQ, dK, dV) of sum(dO * O) with O the exact attention output.
+
+    With ``return_fwd`` also returns (O, lse, D) where D_i = sum_j P_ij dP_ij.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, d = _shape(q)
+    m = _mask(mask, N)
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    o = np.empty_like(q) if return_fwd else None
+    lse = np.empty((B, H, N)) if return_fwd else None
+    D = np.empty((B, H, N)) if return_fwd else None
+    rc = _load().ref_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), B, H, N, d, float(scale),
+                              int(causal), _ptr(m, _u8p), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(o),
+                              _ptr(lse), _ptr(D))
+    _check(rc, "bwd")
+    if return_fwd:
+        return dq, dk, dv, o, lse, D
+    return dq, dk, dv
+
+
+class Oracle:
+    """The functions above bound to a given compiled copy of the oracle.
+
+    ``Oracle()`` is the oracle itself.  ``Oracle(path)`` loads another build of
+    a (possibly modified) ref_attn.c; tests use it to plant mistakes in the
+    oracle and show that the pins catch them.
+    """
+
+    def __init__(self, path: Optional[str] = None):
+        self._path = path
+
+    def _swap(self, fn, *a, **kw):
+        global _lib
+        if self._path is None:
+            return fn(*a, **kw)
+        saved = _lib
+        _lib = _Lib(self._path).lib
+        try:
+            return fn(*a, **kw)
+        finally:
+            _lib = saved
+
+    def attn_fwd(self, *a, **kw):
+        return self._swap(attn_fwd, *a, **kw)
+
+    def attn_fwd_rows(self, *a, **kw):
+        return self._swap(attn_fwd_rows, *a, **kw)
+
+    def attn_fwd_online(self, *a, **kw):
+        return self._swap(attn_fwd_online, *a, **kw)
+
+    def attn_probs(self, *a, **kw):
+        return self._swap(attn_probs, *a, **kw)
+
+    def attn_bwd(self, *a, **kw):
+        return self._swap(attn_bwd, *a, **kw)
+
+
+def build_variant(src_text: str, out_path: str) -> str:
+    """Compile a modified copy of ref_attn.c (given as text) to ``out_path``."""
+    src = out_path + ".c"
+    with open(src, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+                    src, "-o", out_path, "-lm"], check=True)
+    return out_path
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()

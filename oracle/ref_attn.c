@@ -1,0 +1,342 @@
+/*
+ * Reference implementation of exact softmax attention, fp64, CPU only.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links or calls this
+ * file; it exists so the HIP kernels can be checked against the plain
+ * definition.  It shares no code, header or table with them.
+ *
+ * What it computes is the definition of attention that FlashAttention keeps
+ * exactly ("FlashAttention: Fast and Memory-Efficient Exact Attention with
+ * IO-Awareness" section 1.1, Attn = softmax(QK^T)V, with the numerically
+ * stable softmax of its section 2.4), with a scale on the scores and two masks
+ * ("FlashAttention 深度解析" section 五 names the causal mask as built in;
+ * the block-sparse variant of the IO-Awareness page section 4 attends only the
+ * kept 128x128 blocks).  For every (batch, head) it materializes the full
+ * score matrix S and probability matrix P ("FlashAttention 深度解析"
+ * section 一 describes exactly this standard route), then O = P V.
+ *
+ * Layout: q, k, v, o, dO, dq, dk, dv are [B][H][N][d] row-major doubles;
+ * lse is [B][H][N]; mask (optional) is [nb][nb] uint8 with nb = ceil(N/128),
+ * shared by all (b, h); nonzero = block kept.
+ *
+ * Conventions (choices where the pages are silent):
+ *   S_ij = scale * sum_k q_ik k_jk
+ *   allowed(i, j) = (!causal || j <= i) && (mask == NULL || mask[i/128][j/128])
+ *   m_i = max over allowed j of S_ij;  Z_i = sum over allowed j of exp(S_ij - m_i)
+ *   P_ij = exp(S_ij - m_i) / Z_i if allowed else 0
+ *   O_i = sum_j P_ij v_j;  lse_i = m_i + log(Z_i)
+ *   a row with no allowed key: O_i = 0, lse_i = -inf.
+ *
+ * The backward is the chain rule of the same definition (the recompute
+ * backward of "FlashAttention原理概览" section 3.2 and the IO-Awareness page
+ * section 2.5 produces the same numbers without storing P):
+ *   dV = P^T dO;  dP = dO V^T;  D_i = sum_j P_ij dP_ij;
+ *   dS_ij = P_ij (dP_ij - D_i);  dQ = scale * dS K;  dK = scale * dS^T Q.
+ *
+ * An online-softmax variant (the running max / running sum loop of
+ * "FlashAttention 深度解析" section 二) is provided separately so tests can
+ * check that chunked evaluation reaches the one-shot result.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define REF_MASK_BLOCK 128
+
+int ref_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static int ref_allowed(long i, long j, int causal, const uint8_t* mask, long nb) {
+    if (causal && j > i) return 0;
+    if (mask && !mask[(i / REF_MASK_BLOCK) * nb + (j / REF_MASK_BLOCK)]) return 0;
+    return 1;
+}
+
+/* Scores, probabilities and lse of one head.  S and P are N*N doubles each. */
+static void ref_head_probs(const double* q, const double* k, long N, long d, double scale,
+                           int causal, const uint8_t* mask, double* S, double* P, double* lse) {
+    long nb = (N + REF_MASK_BLOCK - 1) / REF_MASK_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < N; i++) {
+        /* 1. scores */
+        for (long j = 0; j < N; j++) {
+            double acc = 0.0;
+            for (long c = 0; c < d; c++) acc += q[i * d + c] * k[j * d + c];
+            S[i * N + j] = scale * acc;
+        }
+        /* 2. stable softmax over the allowed keys */
+        double m = -INFINITY;
+        long count = 0;
+        for (long j = 0; j < N; j++)
+            if (ref_allowed(i, j, causal, mask, nb)) {
+                if (S[i * N + j] > m) m = S[i * N + j];
+                count++;
+            }
+        if (count == 0) {
+            for (long j = 0; j < N; j++) P[i * N + j] = 0.0;
+            lse[i] = -INFINITY;
+            continue;
+        }
+        double z = 0.0;
+        for (long j = 0; j < N; j++)
+            if (ref_allowed(i, j, causal, mask, nb)) z += exp(S[i * N + j] - m);
+        for (long j = 0; j < N; j++)
+            P[i * N + j] = ref_allowed(i, j, causal, mask, nb) ? exp(S[i * N + j] - m) / z : 0.0;
+        lse[i] = m + log(z);
+    }
+}
+
+/* O = P V for one head. */
+static void ref_head_pv(const double* P, const double* v, long N, long d, double* o) {
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < N; i++) {
+        for (long c = 0; c < d; c++) o[i * d + c] = 0.0;
+        for (long j = 0; j < N; j++) {
+            double p = P[i * N + j];
+            if (p == 0.0) continue;
+            for (long c = 0; c < d; c++) o[i * d + c] += p * v[j * d + c];
+        }
+    }
+}
+
+/* Probabilities of a single head (exposed so tests can inspect P). */
+int ref_attn_probs(const double* q, const double* k, int N, int d, double scale, int causal,
+                   const uint8_t* mask, double* P, double* lse) {
+    double* S = (double*)malloc(sizeof(double) * (size_t)N * N);
+    if (!S) return 1;
+    ref_head_probs(q, k, N, d, scale, causal, mask, S, P, lse);
+    free(S);
+    return 0;
+}
+
+int ref_attn_fwd(const double* q, const double* k, const double* v, int B, int H, int N, int d,
+                 double scale, int causal, const uint8_t* mask, double* o, double* lse) {
+    size_t nn = (size_t)N * N, nd = (size_t)N * d;
+    double* S = (double*)malloc(sizeof(double) * nn);
+    double* P = (double*)malloc(sizeof(double) * nn);
+    if (!S || !P) { free(S); free(P); return 1; }
+    for (long bh = 0; bh < (long)B * H; bh++) {
+        ref_head_probs(q + bh * nd, k + bh * nd, N, d, scale, causal, mask, S, P, lse + bh * N);
+        ref_head_pv(P, v + bh * nd, N, d, o + bh * nd);
+    }
+    free(S);
+    free(P);
+    return 0;
+}
+
+/*
+ * Selected rows only: rows[r] = {bh, i}.  Each row's scores, probabilities and
+ * output follow the same definition; nothing is shared between rows.
+ */
+int ref_attn_fwd_rows(const double* q, const double* k, const double* v, int B, int H, int N, int d,
+                      double scale, int causal, const uint8_t* mask, const int64_t* rows, int nrows,
+                      double* o_rows, double* lse_rows) {
+    size_t nd = (size_t)N * d;
+    long nb = (N + REF_MASK_BLOCK - 1) / REF_MASK_BLOCK;
+    int err = 0;
+    (void)B; (void)H;
+#pragma omp parallel
+    {
+        double* srow = (double*)malloc(sizeof(double) * (size_t)N);
+        double* prow = (double*)malloc(sizeof(double) * (size_t)N);
+        if (!srow || !prow) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int r = 0; r < nrows; r++) {
+                long bh = rows[2 * r], i = rows[2 * r + 1];
+                const double* qi = q + bh * nd + i * d;
+                const double* kh = k + bh * nd;
+                const double* vh = v + bh * nd;
+                for (long j = 0; j < N; j++) {
+                    double acc = 0.0;
+                    for (long c = 0; c < d; c++) acc += qi[c] * kh[j * d + c];
+                    srow[j] = scale * acc;
+                }
+                double m = -INFINITY;
+                long count = 0;
+                for (long j = 0; j < N; j++)
+                    if (ref_allowed(i, j, causal, mask, nb)) {
+                        if (srow[j] > m) m = srow[j];
+                        count++;
+                    }
+                double* orow = o_rows + (size_t)r * d;
+                for (long c = 0; c < d; c++) orow[c] = 0.0;
+                if (count == 0) { lse_rows[r] = -INFINITY; continue; }
+                double z = 0.0;
+                for (long j = 0; j < N; j++)
+                    if (ref_allowed(i, j, causal, mask, nb)) z += exp(srow[j] - m);
+                for (long j = 0; j < N; j++) {
+                    prow[j] = ref_allowed(i, j, causal, mask, nb) ? exp(srow[j] - m) / z : 0.0;
+                    if (prow[j] == 0.0) continue;
+                    for (long c = 0; c < d; c++) orow[c] += prow[j] * vh[j * d + c];
+                }
+                lse_rows[r] = m + log(z);
+            }
+        }
+        free(srow);
+        free(prow);
+    }
+    return err;
+}
+
+/*
+ * Online softmax ("FlashAttention 深度解析" section 二): scan the keys of each
+ * row in chunks of `chunk`; keep the running max m, the running sum l and the
+ * unnormalized output o; when the max grows, rescale l and o by exp(m - m_new);
+ * divide once at the end.  Keys a mask removes are skipped.
+ */
+int ref_attn_fwd_online(const double* q, const double* k, const double* v, int B, int H, int N,
+                        int d, double scale, int causal, const uint8_t* mask, int chunk,
+                        double* o, double* lse) {
+    if (chunk < 1) return 1;
+    size_t nd = (size_t)N * d;
+    long nb = (N + REF_MASK_BLOCK - 1) / REF_MASK_BLOCK;
+    int err = 0;
+    for (long bh = 0; bh < (long)B * H; bh++) {
+        const double* qh = q + bh * nd;
+        const double* kh = k + bh * nd;
+        const double* vh = v + bh * nd;
+#pragma omp parallel
+        {
+            double* sblk = (double*)malloc(sizeof(double) * (size_t)chunk);
+            if (!sblk) {
+#pragma omp atomic write
+                err = 1;
+            }
+#pragma omp for schedule(static)
+            for (long i = 0; i < N; i++) {
+                if (!sblk) continue;
+                double m = -INFINITY, l = 0.0;
+                double* oi = o + bh * nd + i * d;
+                for (long c = 0; c < d; c++) oi[c] = 0.0;
+                for (long j0 = 0; j0 < N; j0 += chunk) {
+                    long j1 = j0 + chunk < N ? j0 + chunk : N;
+                    /* scores of this chunk and the chunk's max over allowed keys */
+                    double bmax = -INFINITY;
+                    for (long j = j0; j < j1; j++) {
+                        double acc = 0.0;
+                        for (long c = 0; c < d; c++) acc += qh[i * d + c] * kh[j * d + c];
+                        sblk[j - j0] = scale * acc;
+                        if (ref_allowed(i, j, causal, mask, nb) && sblk[j - j0] > bmax) bmax = sblk[j - j0];
+                    }
+                    if (bmax == -INFINITY) continue; /* nothing allowed in this chunk */
+                    double m_new = m > bmax ? m : bmax;
+                    double corr = exp(m - m_new); /* 0 while m is still -inf */
+                    l *= corr;
+                    for (long c = 0; c < d; c++) oi[c] *= corr;
+                    for (long j = j0; j < j1; j++) {
+                        if (!ref_allowed(i, j, causal, mask, nb)) continue;
+                        double p = exp(sblk[j - j0] - m_new);
+                        l += p;
+                        for (long c = 0; c < d; c++) oi[c] += p * vh[j * d + c];
+                    }
+                    m = m_new;
+                }
+                if (l == 0.0) {
+                    lse[bh * N + i] = -INFINITY;
+                    continue;
+                }
+                for (long c = 0; c < d; c++) oi[c] /= l;
+                lse[bh * N + i] = m + log(l);
+            }
+            free(sblk);
+        }
+    }
+    return err;
+}
+
+/*
+ * Backward of the definition above for every (b, h).  Optionally returns the
+ * forward's O and lse and the row terms D (pointers may be NULL).
+ */
+int ref_attn_bwd(const double* q, const double* k, const double* v, const double* dO, int B, int H,
+                 int N, int d, double scale, int causal, const uint8_t* mask, double* dq, double* dk,
+                 double* dv, double* o_out, double* lse_out, double* D_out) {
+    size_t nn = (size_t)N * N, nd = (size_t)N * d;
+    double* S = (double*)malloc(sizeof(double) * nn);
+    double* P = (double*)malloc(sizeof(double) * nn);
+    double* dP = (double*)malloc(sizeof(double) * nn);
+    double* lse = (double*)malloc(sizeof(double) * (size_t)N);
+    double* D = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!S || !P || !dP || !lse || !D) {
+        free(S); free(P); free(dP); free(lse); free(D);
+        return 1;
+    }
+    double* dS = S; /* S is not needed once P exists */
+    for (long bh = 0; bh < (long)B * H; bh++) {
+        const double* qh = q + bh * nd;
+        const double* kh = k + bh * nd;
+        const double* vh = v + bh * nd;
+        const double* doh = dO + bh * nd;
+        ref_head_probs(qh, kh, N, d, scale, causal, mask, S, P, lse);
+        if (o_out) ref_head_pv(P, vh, N, d, o_out + bh * nd);
+        if (lse_out) memcpy(lse_out + bh * N, lse, sizeof(double) * (size_t)N);
+        /* dP = dO V^T */
+#pragma omp parallel for schedule(static)
+        for (long i = 0; i < N; i++)
+            for (long j = 0; j < N; j++) {
+                double acc = 0.0;
+                for (long c = 0; c < d; c++) acc += doh[i * d + c] * vh[j * d + c];
+                dP[i * N + j] = acc;
+            }
+        /* D_i = sum_j P_ij dP_ij;  dS = P o (dP - D) */
+#pragma omp parallel for schedule(static)
+        for (long i = 0; i < N; i++) {
+            double acc = 0.0;
+            for (long j = 0; j < N; j++) acc += P[i * N + j] * dP[i * N + j];
+            D[i] = acc;
+            for (long j = 0; j < N; j++) dS[i * N + j] = P[i * N + j] * (dP[i * N + j] - acc);
+        }
+        if (D_out) memcpy(D_out + bh * N, D, sizeof(double) * (size_t)N);
+        /* dQ = scale * dS K */
+        double* dqh = dq + bh * nd;
+#pragma omp parallel for schedule(static)
+        for (long i = 0; i < N; i++) {
+            for (long c = 0; c < d; c++) dqh[i * d + c] = 0.0;
+            for (long j = 0; j < N; j++) {
+                double s = dS[i * N + j];
+                if (s == 0.0) continue;
+                for (long c = 0; c < d; c++) dqh[i * d + c] += s * kh[j * d + c];
+            }
+            for (long c = 0; c < d; c++) dqh[i * d + c] *= scale;
+        }
+        /* dV = P^T dO and dK = scale * dS^T Q; each thread owns a range of keys j
+         * and sums over i in increasing order. */
+        double* dvh = dv + bh * nd;
+        double* dkh = dk + bh * nd;
+#pragma omp parallel
+        {
+            long nt = 1, t = 0;
+#ifdef _OPENMP
+            nt = omp_get_num_threads();
+            t = omp_get_thread_num();
+#endif
+            long j0 = (long)N * t / nt, j1 = (long)N * (t + 1) / nt;
+            for (long j = j0; j < j1; j++)
+                for (long c = 0; c < d; c++) dvh[j * d + c] = dkh[j * d + c] = 0.0;
+            for (long i = 0; i < N; i++)
+                for (long j = j0; j < j1; j++) {
+                    double p = P[i * N + j], s = dS[i * N + j];
+                    if (p != 0.0)
+                        for (long c = 0; c < d; c++) dvh[j * d + c] += p * doh[i * d + c];
+                    if (s != 0.0)
+                        for (long c = 0; c < d; c++) dkh[j * d + c] += s * qh[i * d + c];
+                }
+            for (long j = j0; j < j1; j++)
+                for (long c = 0; c < d; c++) dkh[j * d + c] *= scale;
+        }
+    }
+    free(S); free(P); free(dP); free(lse); free(D);
+    return 0;
+}

@@ -1,0 +1,320 @@
+"""Pins for the fp64 oracle: facts about exact attention that do not come from it.
+
+Each ``pin_*`` takes an oracle object (the ``oracle`` module or an
+``oracle.Oracle`` bound to a modified build) and raises AssertionError when
+the oracle disagrees with the fact.  tests/test_oracle.py runs them on the
+oracle; tests/test_oracle_mutants.py plants mistakes in copies of the oracle
+and checks that some pin fails for each.
+
+Sources of truth used here:
+  * brute force with a *different* softmax formula: exp(s_j) / fsum(exp(s)),
+    no max subtraction, pure Python scalars (the plain softmax of
+    "FlashAttention: ... IO-Awareness" section 1.1 instead of the stable form
+    of its section 2.4 that the oracle uses);
+  * closed forms and invariances of softmax attention;
+  * the running-max/running-sum loop of "FlashAttention 深度解析" section 二
+    must reach the one-shot result (that page and the IO-Awareness page
+    section 2.4 state that the chunked result is identical);
+  * central finite differences of L = sum(dO * O) for the backward.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+MB = 128  # block-mask granularity
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _allowed(i, j, causal, mask):
+    if causal and j > i:
+        return False
+    if mask is not None and not mask[i // MB, j // MB]:
+        return False
+    return True
+
+
+def brute_force_head(q, k, v, scale, causal=False, mask=None):
+    """Pure-Python scalar attention for one head with exp(s)/fsum(exp(s))."""
+    N, d = q.shape
+    o = [[0.0] * d for _ in range(N)]
+    lse = [0.0] * N
+    for i in range(N):
+        cols = [j for j in range(N) if _allowed(i, j, causal, mask)]
+        if not cols:
+            lse[i] = -math.inf
+            continue
+        e = []
+        for j in cols:
+            s = scale * math.fsum(float(q[i, c]) * float(k[j, c]) for c in range(d))
+            e.append(math.exp(s))
+        z = math.fsum(e)
+        for c in range(d):
+            o[i][c] = math.fsum(e[t] / z * float(v[cols[t], c]) for t in range(len(cols)))
+        lse[i] = math.log(z)
+    return np.array(o), np.array(lse)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin), f"{what}: non-finite pattern differs"
+    assert np.array_equal(a[~fin], b[~fin]), f"{what}: infinities differ"
+    if fin.any():
+        err = np.max(np.abs(a[fin] - b[fin]) / np.maximum(1.0, np.abs(b[fin])))
+        assert err <= tol, f"{what}: rel err {err:.3e} > {tol:.1e}"
+
+
+# ----------------------------------------------------------------------------
+# Forward
+# ----------------------------------------------------------------------------
+
+def pin_brute_force(orc):
+    """Tiny dense/causal cases and >128-row block-mask cases vs the brute force."""
+    cases = []
+    for seed, (N, d, scale, causal) in enumerate(
+            [(1, 1, 1.0, False), (5, 3, 0.5, False), (8, 4, 1.0, True), (7, 2, 0.5, True),
+             (8, 4, 0.5, False)]):
+        cases.append((N, d, scale, causal, None, seed))
+    # block masks need N > 128 to have more than one block
+    r = _rng(99)
+    for seed, (N, causal) in enumerate([(200, False), (260, True), (257, False)]):
+        nb = (N + MB - 1) // MB
+        mask = (r.random((nb, nb)) < 0.6).astype(np.uint8)
+        mask[0, 0] = 1
+        cases.append((N, 2, 0.7, causal, mask, 100 + seed))
+    # a row with no allowed key at all
+    mask = np.array([[1, 0], [0, 0]], dtype=np.uint8)
+    cases.append((150, 2, 1.0, False, mask, 200))
+    for N, d, scale, causal, mask, seed in cases:
+        g = _rng(seed)
+        q, k, v = (g.standard_normal((1, 1, N, d)) for _ in range(3))
+        o, lse = orc.attn_fwd(q, k, v, scale, causal, mask)
+        ob, lb = brute_force_head(q[0, 0], k[0, 0], v[0, 0], scale, causal, mask)
+        _close(o[0, 0], ob, 1e-12, f"O N={N} d={d} causal={causal} mask={mask is not None}")
+        _close(lse[0, 0], lb, 1e-12, f"lse N={N}")
+
+
+def pin_rows_sum_to_one(orc):
+    """Rows of P are a probability distribution over exactly the allowed keys."""
+    g = _rng(1)
+    N, d = 300, 8
+    q, k = g.standard_normal((N, d)), g.standard_normal((N, d))
+    nb = 3
+    mask = (g.random((nb, nb)) < 0.7).astype(np.uint8)
+    np.fill_diagonal(mask, 1)
+    for causal in (False, True):
+        for m in (None, mask):
+            P, lse = orc.attn_probs(q, k, 0.35, causal, m)
+            allowed = np.array([[_allowed(i, j, causal, m) for j in range(N)] for i in range(N)])
+            assert np.all(P[~allowed] == 0.0)
+            assert np.all(P[allowed] > 0.0)
+            assert np.max(np.abs(P.sum(axis=1) - 1.0)) <= 1e-12
+
+
+def pin_constant_v(orc):
+    """V_j = c for every key makes every output row equal c (convex combination)."""
+    g = _rng(2)
+    B, H, N, d = 2, 2, 96, 16
+    q, k = g.standard_normal((B, H, N, d)), g.standard_normal((B, H, N, d))
+    c = g.standard_normal(d)
+    v = np.broadcast_to(c, (B, H, N, d)).copy()
+    for causal in (False, True):
+        o, _ = orc.attn_fwd(q, k, v, 0.25, causal)
+        assert np.max(np.abs(o - c)) <= 1e-12
+
+
+def pin_causal_first_row(orc):
+    """With a causal mask row 0 sees only key 0: O_0 = V_0 and lse_0 = s q_0.k_0."""
+    g = _rng(3)
+    B, H, N, d = 1, 3, 64, 32
+    q, k, v = (g.standard_normal((B, H, N, d)) for _ in range(3))
+    s = 0.125
+    o, lse = orc.attn_fwd(q, k, v, s, causal=True)
+    assert np.max(np.abs(o[:, :, 0] - v[:, :, 0])) <= 1e-12
+    want = s * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0])
+    assert np.max(np.abs(lse[:, :, 0] - want)) <= 1e-12
+
+
+def pin_chunked_equals_one_shot(orc):
+    """The online loop with any chunk size reaches the one-shot result."""
+    g = _rng(4)
+    B, H, N, d = 1, 2, 300, 16
+    q, k, v = (g.standard_normal((B, H, N, d)) * 1.5 for _ in range(3))
+    nb = 3
+    mask = (g.random((nb, nb)) < 0.7).astype(np.uint8)
+    np.fill_diagonal(mask, 1)
+    for causal, m in ((False, None), (True, None), (False, mask), (True, mask)):
+        o, lse = orc.attn_fwd(q, k, v, 0.3, causal, m)
+        for chunk in (1, 7, 64, 128, N):
+            o2, l2 = orc.attn_fwd_online(q, k, v, 0.3, chunk, causal, m)
+            _close(o2, o, 1e-12, f"online chunk={chunk}")
+            _close(l2, lse, 1e-12, f"online lse chunk={chunk}")
+
+
+def pin_closed_forms(orc):
+    g = _rng(5)
+    # N = 1: O = V_0, lse = s q.k
+    q, k, v = (g.standard_normal((2, 1, 1, 8)) for _ in range(3))
+    o, lse = orc.attn_fwd(q, k, v, 0.7)
+    assert np.max(np.abs(o - v)) <= 1e-15
+    assert np.max(np.abs(lse - 0.7 * np.einsum("bhnd,bhnd->bhn", q, k))) <= 1e-12
+    # scale = 0: uniform weights over the allowed set
+    B, H, N, d = 1, 1, 200, 4
+    q, k, v = (g.standard_normal((B, H, N, d)) for _ in range(3))
+    mask = np.array([[1, 0], [1, 1]], dtype=np.uint8)
+    for causal, m in ((False, None), (True, None), (False, mask), (True, mask)):
+        o, lse = orc.attn_fwd(q, k, v, 0.0, causal, m)
+        for i in range(N):
+            cols = [j for j in range(N) if _allowed(i, j, causal, m)]
+            assert abs(lse[0, 0, i] - math.log(len(cols))) <= 1e-12
+            want = v[0, 0, cols].mean(axis=0)
+            assert np.max(np.abs(o[0, 0, i] - want)) <= 1e-12
+    # one-hot: one score exceeds every other by more than 60 -> O_i = V_j*.
+    # Key j carries a unit marker in coordinate j; query i puts 100 on the marker
+    # of its chosen key star[i]; the remaining coordinates are small noise.
+    N = 32
+    star = g.integers(0, N, size=N)
+    noise = 0.1 * g.standard_normal((1, 1, N, 4))
+    q = np.concatenate([noise, np.zeros((1, 1, N, N))], axis=3)
+    k = np.concatenate([0.1 * g.standard_normal((1, 1, N, 4)), np.eye(N)[None, None]], axis=3)
+    v = g.standard_normal((1, 1, N, 4 + N))
+    for i in range(N):
+        q[0, 0, i, 4 + star[i]] = 100.0
+    o, _ = orc.attn_fwd(q, k, v, 1.0)
+    for i in range(N):
+        assert np.max(np.abs(o[0, 0, i] - v[0, 0, star[i]])) <= 1e-12
+
+
+def pin_invariances(orc):
+    g = _rng(6)
+    B, H, N, d = 1, 2, 260, 8
+    q, k, v = (g.standard_normal((B, H, N, d)) for _ in range(3))
+    s = 0.4
+    # shifting every key by the same vector shifts each score row by a constant
+    shift = g.standard_normal(d)
+    for causal in (False, True):
+        o, lse = orc.attn_fwd(q, k, v, s, causal)
+        o2, lse2 = orc.attn_fwd(q, k + shift, v, s, causal)
+        _close(o2, o, 1e-12, "key shift O")
+        _close(lse2, lse + s * np.einsum("bhnd,d->bhn", q, shift), 1e-12, "key shift lse")
+    # jointly permuting keys and values leaves a non-causal, unmasked output unchanged
+    perm = g.permutation(N)
+    o, lse = orc.attn_fwd(q, k, v, s)
+    o2, lse2 = orc.attn_fwd(q, k[:, :, perm], v[:, :, perm], s)
+    _close(o2, o, 1e-12, "perm O")
+    _close(lse2, lse, 1e-12, "perm lse")
+    # an all-ones block mask is the dense case
+    nb = 3
+    ones = np.ones((nb, nb), dtype=np.uint8)
+    for causal in (False, True):
+        o, lse = orc.attn_fwd(q, k, v, s, causal)
+        o2, lse2 = orc.attn_fwd(q, k, v, s, causal, ones)
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    # a block mask equals dense attention with an additive -inf bias (numpy route)
+    mask = (g.random((nb, nb)) < 0.5).astype(np.uint8)
+    mask[:, 0] = 1
+    o, lse = orc.attn_fwd(q, k, v, s, False, mask)
+    bias = np.where(np.kron(mask, np.ones((MB, MB)))[:N, :N] > 0, 0.0, -np.inf)
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        S = s * q[b, h] @ k[b, h].T + bias
+        mx = S.max(axis=1, keepdims=True)
+        E = np.exp(S - mx)
+        Z = E.sum(axis=1, keepdims=True)
+        _close(o[b, h], (E / Z) @ v[b, h], 1e-12, "additive mask O")
+        _close(lse[b, h], (mx + np.log(Z))[:, 0], 1e-12, "additive mask lse")
+
+
+def pin_rows_match_full(orc):
+    """The sampled-row entry point agrees with the full forward on those rows."""
+    g = _rng(7)
+    B, H, N, d = 2, 2, 270, 8
+    q, k, v = (g.standard_normal((B, H, N, d)) for _ in range(3))
+    nb = 3
+    mask = (g.random((nb, nb)) < 0.6).astype(np.uint8)
+    mask[2, :] = 0  # rows of the last block see nothing
+    rows = np.array([[0, 0], [1, 5], [3, 269], [2, 128], [3, 127], [0, 256]], dtype=np.int64)
+    for causal, m in ((False, None), (True, None), (True, mask)):
+        o, lse = orc.attn_fwd(q, k, v, 0.3, causal, m)
+        orow, lrow = orc.attn_fwd_rows(q, k, v, 0.3, rows, causal, m)
+        of = o.reshape(B * H, N, d)
+        lf = lse.reshape(B * H, N)
+        for r, (bh, i) in enumerate(rows):
+            assert np.array_equal(orow[r], of[bh, i])
+            assert lrow[r] == lf[bh, i] or (np.isinf(lrow[r]) and np.isinf(lf[bh, i]))
+
+
+# ----------------------------------------------------------------------------
+# Backward
+# ----------------------------------------------------------------------------
+
+def pin_finite_differences(orc):
+    """dQ, dK, dV equal central differences of L = sum(dO * O)."""
+    g = _rng(8)
+    h = 1e-6
+    for N, d, causal, m in ((6, 3, False, None), (9, 4, True, None), (16, 8, True, None),
+                            (140, 2, False, np.array([[1, 0], [1, 1]], dtype=np.uint8))):
+        q, k, v, do = (g.standard_normal((1, 1, N, d)) for _ in range(4))
+        s = 0.6
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, s, causal, m)
+
+        def loss(qq, kk, vv):
+            o, _ = orc.attn_fwd(qq, kk, vv, s, causal, m)
+            return float(np.sum(do * o))
+
+        # every coordinate on the tiny cases, a seeded subset on the bigger one
+        coords = [(i, c) for i in range(N) for c in range(d)]
+        if N > 32:
+            pick = g.choice(len(coords), size=24, replace=False)
+            coords = [coords[t] for t in pick]
+        for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            for i, c in coords:
+                xp, xm = x.copy(), x.copy()
+                xp[0, 0, i, c] += h
+                xm[0, 0, i, c] -= h
+                args_p = {"q": q, "k": k, "v": v}
+                args_m = {"q": q, "k": k, "v": v}
+                args_p[name], args_m[name] = xp, xm
+                fd = (loss(args_p["q"], args_p["k"], args_p["v"]) -
+                      loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+                an = grad[0, 0, i, c]
+                assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, N, i, c, fd, an)
+
+
+def pin_backward_identities(orc):
+    g = _rng(9)
+    B, H, N, d = 1, 2, 200, 8
+    q, k, v, do = (g.standard_normal((B, H, N, d)) for _ in range(4))
+    nb = 2
+    mask = np.array([[1, 1], [0, 1]], dtype=np.uint8)
+    for causal, m in ((False, None), (True, None), (True, mask)):
+        dq, dk, dv, o, lse, D = orc.attn_bwd(q, k, v, do, 0.3, causal, m, return_fwd=True)
+        o_f, lse_f = orc.attn_fwd(q, k, v, 0.3, causal, m)
+        assert np.max(np.abs(o - o_f)) <= 1e-14 and np.max(np.abs(lse - lse_f)) <= 1e-14
+        # D_i = sum_j P_ij dP_ij equals rowsum(dO * O)
+        _close(D, np.sum(do * o, axis=-1), 1e-10, "D = rowsum(dO*O)")
+        # sum_j dK_j = 0 (softmax rows are shift invariant)
+        assert np.max(np.abs(dk.sum(axis=2))) <= 1e-10
+        # sum_j dV_j = sum_i dO_i (rows of P sum to 1)
+        assert np.max(np.abs(dv.sum(axis=2) - do.sum(axis=2))) <= 1e-10
+
+
+ALL_PINS = [
+    pin_brute_force,
+    pin_rows_sum_to_one,
+    pin_constant_v,
+    pin_causal_first_row,
+    pin_chunked_equals_one_shot,
+    pin_closed_forms,
+    pin_invariances,
+    pin_rows_match_full,
+    pin_finite_differences,
+    pin_backward_identities,
+]

@@ -1,0 +1,53 @@
+"""Plant plausible mistakes in copies of the oracle; some pin must catch each.
+
+The mistakes are textual edits of ref_attn.c compiled to a temporary library
+(the oracle's own source is untouched).  This shows the pins are strong
+enough: a dropped term, a wrong sign or index, or a transposed operand makes
+at least one pin fail.
+"""
+import os
+
+import pytest
+
+import oracle
+from tests import oracle_pins as P
+
+MUTANTS = {
+    "drop_scale": ("S[i * N + j] = scale * acc;", "S[i * N + j] = acc;"),
+    "causal_strict": ("if (causal && j > i) return 0;", "if (causal && j >= i) return 0;"),
+    "mask_transposed": ("mask[(i / REF_MASK_BLOCK) * nb + (j / REF_MASK_BLOCK)]",
+                        "mask[(j / REF_MASK_BLOCK) * nb + (i / REF_MASK_BLOCK)]"),
+    "no_normalize": ("exp(S[i * N + j] - m) / z : 0.0;", "exp(S[i * N + j] - m) : 0.0;"),
+    "lse_no_log": ("lse[i] = m + log(z);", "lse[i] = m + z;"),
+    "lse_no_max": ("lse[i] = m + log(z);", "lse[i] = log(z);"),
+    "qk_transposed": ("for (long c = 0; c < d; c++) acc += q[i * d + c] * k[j * d + c];\n            S[i * N + j]",
+                      "for (long c = 0; c < d; c++) acc += q[j * d + c] * k[i * d + c];\n            S[i * N + j]"),
+    "bwd_drop_D": ("dS[i * N + j] = P[i * N + j] * (dP[i * N + j] - acc);",
+                   "dS[i * N + j] = P[i * N + j] * dP[i * N + j];"),
+    "bwd_dk_no_scale": ("dkh[j * d + c] *= scale;", "dkh[j * d + c] *= 1.0;"),
+    "bwd_dq_no_scale": ("dqh[i * d + c] *= scale;", "dqh[i * d + c] *= 1.0;"),
+    "bwd_dv_uses_dS": ("dvh[j * d + c] += p * doh[i * d + c];", "dvh[j * d + c] += s * doh[i * d + c];"),
+    "bwd_dP_transposed": ("acc += doh[i * d + c] * vh[j * d + c];", "acc += doh[j * d + c] * vh[i * d + c];"),
+    "online_no_rescale": ("oi[c] *= corr;", "oi[c] *= 1.0;"),
+}
+
+
+@pytest.fixture(scope="module")
+def src():
+    return oracle.source_text()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, src, tmp_path):
+    old, new = MUTANTS[name]
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    text = src.replace(old, new, 1)
+    path = oracle.build_variant(text, os.path.join(str(tmp_path), f"mut_{name}.so"))
+    orc = oracle.Oracle(path)
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches mutant {name}"

@@ -1,0 +1,105 @@
+"""Work and traffic accounting for exact attention (FLOPs and algorithmic bytes).
+
+FLOP convention (FlashAttention-2's, restated on "FlashAttention 深度解析"
+section 四): the forward does two matrix products of 2*N*N*d each per head,
+so 4*B*H*N^2*d; a causal mask halves it; a block mask scales it by the
+fraction of blocks kept.  The backward does five such products (S recompute,
+dV, dP, dK, dQ), i.e. 2.5x the forward.
+
+Algorithmic bytes are the O(N*d) floor: every tensor crosses HBM exactly once.
+The N*N score/probability traffic of unfused attention ("FlashAttention原理概览"
+section 3.4) is what the method removes and is reported separately by
+``naive_score_bytes``.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import Workload, MASK_BLOCK
+
+BF16_BYTES = 2
+F32_BYTES = 4
+
+
+def elem_bytes(dtype: str) -> int:
+    return {"bf16": BF16_BYTES, "f32": F32_BYTES}[dtype]
+
+
+def fwd_flops(B: int, H: int, N: int, d: int, causal: bool = False,
+              mask: Optional[np.ndarray] = None) -> float:
+    """4*B*H*N^2*d, halved if causal, scaled by the kept-block fraction if masked."""
+    dense = 4.0 * B * H * N * N * d
+    if mask is None:
+        return dense * (0.5 if causal else 1.0)
+    return float(dense * _mask_factor(mask, causal))
+
+
+def _mask_factor(mask: np.ndarray, causal: bool) -> float:
+    """Block density; with causal, blocks on the diagonal count half."""
+    m = mask.astype(np.float64)
+    nb = m.shape[0]
+    if not causal:
+        return m.sum() / (nb * nb)
+    lower = np.tril(m, -1).sum()
+    diag = np.trace(m)
+    return (lower + 0.5 * diag) / (nb * nb)
+
+
+def bwd_flops(B: int, H: int, N: int, d: int, causal: bool = False,
+              mask: Optional[np.ndarray] = None) -> float:
+    return 2.5 * fwd_flops(B, H, N, d, causal, mask)
+
+
+def fwd_bytes(B: int, H: int, N: int, d: int, dtype: str, nb_mask: int = 0) -> int:
+    """Read q, k, v; write o (each B*H*N*d) and lse (fp32 per row); read the mask."""
+    e = elem_bytes(dtype)
+    return 4 * B * H * N * d * e + F32_BYTES * B * H * N + nb_mask * nb_mask
+
+
+def bwd_bytes(B: int, H: int, N: int, d: int, dtype: str, nb_mask: int = 0) -> int:
+    """The backward's floor: read q, k, v, o, do and lse; write dq, dk and dv."""
+    e = elem_bytes(dtype)
+    return 8 * B * H * N * d * e + F32_BYTES * B * H * N + nb_mask * nb_mask
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    """Extra traffic of this implementation's backward beyond the floor.
+
+    D = rowsum(dO*O) is written once and read once (fp32 per row); the fp32 dQ
+    accumulator is cleared once and read once by the final conversion (the
+    atomic read-modify-writes into it are on-chip L2 traffic when they hit).
+    """
+    return 2 * F32_BYTES * B * H * N + 2 * F32_BYTES * B * H * N * d
+
+
+def naive_score_bytes(B: int, H: int, N: int, dtype_bytes: int) -> int:
+    """Size of one materialized N x N score matrix over all heads."""
+    return B * H * N * N * dtype_bytes
+
+
+def qkv_bytes_one_head(N: int, d: int, dtype_bytes: int) -> int:
+    """Q, K and V of a single head."""
+    return 3 * N * d * dtype_bytes
+
+
+def tile_sram_bytes(Br: int, Bc: int, d: int, dtype_bytes: int) -> int:
+    """SRAM for a Q tile, one K/V tile and the S tile: (Br*d + Bc*d + Br*Bc) elements."""
+    return (Br * d + Bc * d + Br * Bc) * dtype_bytes
+
+
+def workload_flops(w: Workload, mask: Optional[np.ndarray] = None) -> dict:
+    f = fwd_flops(w.B, w.H, w.N, w.d, w.causal, mask)
+    out = {"fwd": f}
+    if w.backward:
+        out["bwd"] = 2.5 * f
+    return out
+
+
+def workload_bytes(w: Workload, mask: Optional[np.ndarray] = None) -> dict:
+    nbm = mask.shape[0] if mask is not None else 0
+    out = {"fwd": fwd_bytes(w.B, w.H, w.N, w.d, w.dtype, nbm)}
+    if w.backward:
+        out["bwd"] = bwd_bytes(w.B, w.H, w.N, w.d, w.dtype, nbm)
+    return out
