@@ -1,0 +1,185 @@
+"""Exact IO-aware attention on AMD MI355X (gfx950): Python binding of libfa.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libfa.so`` (built in-tree by ``exact_io_aware_59_amd.build``).
+The functions named like the C ABI (``fa_fwd``, ``fa_bwd``, ...) take torch
+tensors that already live on the GPU, pass their device pointers and the
+current HIP stream, and raise ``FAError`` on a non-zero status.  ``forward``
+and ``backward`` additionally allocate the outputs (and the backward's
+workspace) with torch.  There is no fallback: without the built library every
+call raises.
+
+Tensors are [B, H, N, d], contiguous; bf16 for fa_fwd/fa_bwd, float32 for the
+_f32 entry points; lse is float32 [B, H, N]; the optional block mask is a
+uint8 tensor [ceil(N/128), ceil(N/128)] on the same device.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "FAError", "library_path", "load", "fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32",
+    "fa_bwd_workspace_size", "fa_status_string", "fa_version", "forward", "backward",
+    "MASK_BLOCK",
+]
+
+MASK_BLOCK = 128
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libfa.so")
+
+
+def load():
+    """Load libfa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m exact_io_aware_59_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    lib.fa_fwd_f32.argtypes = lib.fa_fwd.argtypes
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
+    lib.fa_bwd_f32.argtypes = lib.fa_bwd.argtypes
+    for name in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_version"):
+        getattr(lib, name).restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def fa_version() -> int:
+    return int(load().fa_version())
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(load().fa_bwd_workspace_size(B, H, N, d))
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dims(q) -> Tuple[int, int, int, int]:
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d]")
+    B, H, N, d = q.shape
+    return int(B), int(H), int(N), int(d)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise FAError(status, where)
+
+
+# ----------------------------------------------------------------------------
+# C ABI mirrors
+# ----------------------------------------------------------------------------
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool = False, blockmask=None, stream=None):
+    B, H, N, d = _dims(q)
+    _check(load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                         int(bool(causal)), _ptr(blockmask), _stream(stream)), "fa_fwd")
+
+
+def fa_fwd_f32(q, k, v, o, lse, scale: float, causal: bool = False, blockmask=None, stream=None):
+    B, H, N, d = _dims(q)
+    _check(load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                             int(bool(causal)), _ptr(blockmask), _stream(stream)), "fa_fwd_f32")
+
+
+def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, blockmask=None,
+           workspace=None, stream=None):
+    B, H, N, d = _dims(q)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                         _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(blockmask),
+                         _ptr(workspace), nbytes, _stream(stream)), "fa_bwd")
+
+
+def fa_bwd_f32(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, blockmask=None,
+               workspace=None, stream=None):
+    B, H, N, d = _dims(q)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().fa_bwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                             _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                             _ptr(blockmask), _ptr(workspace), nbytes, _stream(stream)), "fa_bwd_f32")
+
+
+# ----------------------------------------------------------------------------
+# allocating wrappers
+# ----------------------------------------------------------------------------
+
+def _default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def forward(q, k, v, scale: Optional[float] = None, causal: bool = False, blockmask=None, stream=None):
+    """Returns (o, lse).  bf16 inputs use fa_fwd, float32 inputs fa_fwd_f32."""
+    import torch
+    B, H, N, d = _dims(q)
+    scale = _default_scale(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+    fn(q, k, v, o, lse, scale, causal, blockmask, stream)
+    return o, lse
+
+
+def workspace(B: int, H: int, N: int, d: int, device):
+    """A backward workspace of the size fa_bwd needs (256-byte aligned by torch's allocator)."""
+    import torch
+    return torch.empty(fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=device)
+
+
+def backward(q, k, v, o, do, lse, scale: Optional[float] = None, causal: bool = False, blockmask=None,
+             ws=None, stream=None):
+    """Returns (dq, dk, dv).  bf16 inputs use fa_bwd, float32 inputs fa_bwd_f32."""
+    import torch
+    B, H, N, d = _dims(q)
+    scale = _default_scale(d) if scale is None else scale
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if ws is None:
+        ws = workspace(B, H, N, d, q.device)
+    fn = fa_bwd if q.dtype == torch.bfloat16 else fa_bwd_f32
+    fn(q, k, v, o, do, lse, dq, dk, dv, scale, causal, blockmask, ws, stream)
+    return dq, dk, dv

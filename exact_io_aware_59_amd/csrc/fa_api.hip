@@ -1,0 +1,151 @@
+// C ABI of libfa.so: argument validation, workspace layout and dispatch.
+// The contract (layouts, ownership, errors) is stated in include/fa.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxMaskN = 4194304;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Half-open byte ranges [p, p+n) overlap?
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+int check_sizes(int B, int H, int N, int d, float scale, const uint8_t* mask) {
+    if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    const long long total = (long long)B * H * N * d;
+    if (total >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (mask && N > kMaxMaskN) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+template <typename T>
+int fwd_common(const T* q, const T* k, const T* v, T* o, float* lse, int B, int H, int N, int d, float scale,
+               int causal, const uint8_t* mask, void* stream, bool bf16) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3))
+        return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    int st = check_sizes(B, H, N, d, scale, mask);
+    if (st != FA_OK) return st;
+    const size_t tb = (size_t)B * H * N * d * sizeof(T), lb = (size_t)B * H * N * sizeof(float);
+    if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb) || overlap(lse, lb, o, tb) ||
+        overlap(lse, lb, q, tb) || overlap(lse, lb, k, tb) || overlap(lse, lb, v, tb))
+        return FA_ERR_INVALID_ARG;
+    fa::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.BH = B * H; a.N = N; a.d = d;
+    a.scale = scale;
+    a.c = fabsf(scale) * fa::kLog2eHost;
+    a.qsign = (bf16 && scale < 0.f) ? 0x80008000u : 0u;
+    a.causal = causal;
+    a.mask = mask;
+    a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+    a.stream = (hipStream_t)stream;
+    hipError_t e = bf16 ? fa::launch_fwd_bf16(a) : fa::launch_fwd_f32(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <typename T>
+int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, const float* lse, T* dq, T* dk, T* dv,
+               int B, int H, int N, int d, float scale, int causal, const uint8_t* mask, void* ws, size_t ws_bytes,
+               void* stream, bool bf16) {
+    if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3))
+        return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    int st = check_sizes(B, H, N, d, scale, mask);
+    if (st != FA_OK) return st;
+    const size_t tb = (size_t)B * H * N * d * sizeof(T);
+    const void* ins[] = {q, k, v, o, dO};
+    void* outs[] = {dq, dk, dv};
+    for (void* x : outs) {
+        for (const void* y : ins)
+            if (overlap(x, tb, y, tb)) return FA_ERR_INVALID_ARG;
+        if (overlap(x, tb, lse, (size_t)B * H * N * sizeof(float))) return FA_ERR_INVALID_ARG;
+    }
+    if (overlap(dq, tb, dk, tb) || overlap(dq, tb, dv, tb) || overlap(dk, tb, dv, tb)) return FA_ERR_INVALID_ARG;
+    const size_t need = fa_bwd_workspace_size(B, H, N, d);
+    if (!ws || ws_bytes < need || ((uintptr_t)ws % kAlign) != 0) return FA_ERR_WORKSPACE;
+    for (void* x : outs)
+        if (overlap(x, tb, ws, need)) return FA_ERR_INVALID_ARG;
+    for (const void* y : ins)
+        if (overlap(ws, need, y, tb)) return FA_ERR_INVALID_ARG;
+    fa::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.BH = B * H; a.N = N; a.d = d;
+    a.scale = scale;
+    a.causal = causal;
+    a.mask = mask;
+    a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+    a.ws_D = (float*)ws;
+    a.ws_dq = (float*)((char*)ws + align_up((size_t)B * H * N * sizeof(float)));
+    a.stream = (hipStream_t)stream;
+    hipError_t e = bf16 ? fa::launch_bwd_bf16(a) : fa::launch_bwd_f32(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, const uint8_t* blockmask, void* stream) {
+    return fwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, B,
+                                H, N, d, scale, causal, blockmask, stream, true);
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, const uint8_t* blockmask, void* stream) {
+    return fwd_common<float>(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, stream, false);
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+    if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+    const size_t rows = (size_t)B * H * N;
+    return align_up(rows * sizeof(float)) + align_up(rows * (size_t)d * sizeof(float));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
+           void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+           void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+                                (const uint16_t*)dO, lse, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, B, H, N, d,
+                                scale, causal, blockmask, workspace, workspace_bytes, stream, true);
+}
+
+int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dO, const float* lse,
+               float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+               const uint8_t* blockmask, void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_common<float>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, blockmask, workspace,
+                             workspace_bytes, stream, false);
+}
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_INVALID_ARG: return "invalid argument";
+        case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case FA_ERR_HIP: return "HIP runtime error while enqueueing";
+        default: return "unknown status";
+    }
+}
+
+int fa_version(void) { return FA_VERSION; }
+
+}  // extern "C"

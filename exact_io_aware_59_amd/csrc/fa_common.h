@@ -1,0 +1,147 @@
+// Device-side building blocks shared by the attention kernels (gfx950 / CDNA4).
+//
+// Matrix-core conventions used throughout (checked on the device):
+//   v_mfma_f32_32x32x16_bf16  C[32x32] += A[32x16] * B[16x32], wave64.
+//     lane l holds A[l%32][8*(l/32) + i] and B[8*(l/32) + i][l%32], i = 0..7;
+//     accumulator register r of lane l is C[8*(r/4) + 4*(l/32) + r%4][l%32].
+//   ds_read_tr16_b64 (transposing LDS read): inside each group of 16 lanes,
+//     lane s supplies the address of 4 consecutive 16-bit elements; the lane i
+//     of the group receives element i%4 of the rows supplied by lanes
+//     4*j + i/4, j = 0..3.  With lane s = 4*j + q pointing at row(j), column
+//     c0 + 4*q, lane i obtains M[row(j)][c0 + i] for j = 0..3.
+//   v_permlane32_swap exchanges the upper half-wave of its first operand with
+//     the lower half-wave of its second.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kMaskBlock = 128;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) (v_log_f32); log2(0) = -inf.
+__device__ __forceinline__ float log2f_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of x in the other half-wave (lane l <-> lane l^32).
+__device__ __forceinline__ float xhalf_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Pack registers [base, base+8) of an accumulator into MFMA bf16 operands (RNE).
+template <int BASE>
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; i++) r[i] = (bf16)s[BASE + i];
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Swizzled row-major tiles in LDS.
+// A tile row holds D bf16 = D/8 chunks of 16 bytes.  Chunk c of row r lives at
+// chunk position c ^ sigma(r).  sigma makes both access patterns the kernels
+// use conflict-free on the 64-bank LDS:
+//   * 16 consecutive rows, same chunk (ds_read_b128 of an MFMA operand);
+//   * 4 consecutive rows, 64 contiguous bytes each (ds_read_tr16_b64 of a
+//     half-wave).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz_sigma(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+// Element offset of logical (row, col) in a D-wide swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+    return row * D + ((((col >> 3) ^ swz_sigma<D>(row))) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ bf16x8 lds_read8(const bf16* base, int off) {
+    return *reinterpret_cast<const bf16x8*>(base + off);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* base, int off) {
+    typedef short __attribute__((address_space(3))) * lds_i16x4_ptr;
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (i16x4 __attribute__((address_space(3)))*)((__attribute__((address_space(3))) bf16*)(base + off)));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// MFMA A-operand (rows m = 32 columns of the tile starting at col0, k = 16 tile
+// rows starting at row0, in the key/query order produced by the accumulator
+// layout) read from a row-major swizzled tile with two transposing reads.
+// Lane l obtains tile[row0 + 8*(i/4) + 4*(l/32) + i%4][col0 + l%32], i = 0..7,
+// which is exactly the order in which registers 0..7 (or 8..15) of a 32x32
+// accumulator hold their 16 rows.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_read_tr_operand(const bf16* tile, int row0, int col0, int lane) {
+    const int s = lane & 15, j = s >> 2, q = s & 3;
+    const int g = (lane >> 4) & 1, h = lane >> 5;
+    const int col = col0 + 16 * g + 4 * q;
+    const bf16x4 lo = lds_read_tr4(tile, swz<D>(row0 + 4 * h + j, col));
+    const bf16x4 hi = lds_read_tr4(tile, swz<D>(row0 + 8 + 4 * h + j, col));
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+// Workgroup id -> logical work item such that consecutive logical items land
+// on the same XCD (the hardware deals workgroups round-robin over the 8 XCDs),
+// so tiles of one (batch, head) share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int wg, int n) {
+    constexpr int kXcd = 8;
+    const int x = wg % kXcd, per = n / kXcd, rem = n % kXcd;
+    return x * per + (x < rem ? x : rem) + wg / kXcd;
+}
+
+// Compact, in LDS, the indices idx in [lo, hi] whose mask byte base[idx*stride]
+// is nonzero (increasing order).  All threads of the workgroup must call it.
+// Returns the count.  `list` needs room for hi - lo + 1 entries.
+template <int WAVES>
+__device__ int build_block_list(const uint8_t* __restrict__ base, size_t stride, int lo, int hi,
+                                uint16_t* list, int* wave_cnt) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int total = 0;
+    for (int start = lo; start <= hi; start += 64 * WAVES) {
+        const int idx = start + tid;
+        const bool keep = idx <= hi && base[(size_t)idx * stride] != 0;
+        const uint64_t bal = __ballot(keep);
+        if (lane == 0) wave_cnt[wave] = __popcll(bal);
+        __syncthreads();
+        int off = total, sum = 0;
+        for (int w = 0; w < WAVES; w++) {
+            if (w < wave) off += wave_cnt[w];
+            sum += wave_cnt[w];
+        }
+        if (keep) list[off + __popcll(bal & ((1ull << lane) - 1))] = (uint16_t)idx;
+        total += sum;
+        __syncthreads();
+    }
+    return total;
+}
+
+}  // namespace fa

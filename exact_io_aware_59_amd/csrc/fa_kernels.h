@@ -1,0 +1,53 @@
+// Host-side launchers of the attention kernels (internal to libfa.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int BH, N, d;
+    float scale;      // signed softmax scale
+    float c;          // |scale| * log2(e)
+    uint32_t qsign;   // 0x80008000 when scale < 0 (bf16 path negates Q), else 0
+    int causal;
+    const uint8_t* mask;
+    int nb;           // ceil(N / 128)
+    hipStream_t stream;
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dO;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    int BH, N, d;
+    float scale;      // signed softmax scale
+    int causal;
+    const uint8_t* mask;
+    int nb;
+    float* ws_D;      // [BH*N] fp32
+    float* ws_dq;     // [BH*N*d] fp32
+    hipStream_t stream;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_bwd_bf16(const BwdArgs& a);
+hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_bwd_f32(const BwdArgs& a);
+
+}  // namespace fa

@@ -1,0 +1,123 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact IO-aware softmax attention on AMD MI355X (gfx950).
+ *
+ * The library computes exact attention, O = softmax(scale * Q K^T [masked]) V,
+ * without ever writing the N x N score or probability matrices to HBM: a
+ * fused forward kernel tiles Q by rows and K/V by columns, keeps a running
+ * row max and row sum (online softmax), rescales an unnormalized output
+ * accumulator and divides once at the end ("FlashAttention 深度解析" sections
+ * 二 and 四; "FlashAttention原理概览" section 3.1; "FlashAttention: Fast and
+ * Memory-Efficient Exact Attention with IO-Awareness" sections 2.3, 2.4, 2.6).
+ * The backward recomputes the scores and probabilities tile by tile from the
+ * saved per-row logsumexp instead of storing them ("FlashAttention原理概览"
+ * section 3.2; IO-Awareness page section 2.5).
+ *
+ * Definition computed (per batch b, head h, row i):
+ *   S_ij  = scale * sum_c q_ic k_jc
+ *   allowed(i, j) = (!causal || j <= i) && (blockmask == NULL || blockmask[i/128][j/128] != 0)
+ *   lse_i = log sum_{allowed j} exp(S_ij)         (natural log; -inf if no j is allowed)
+ *   O_i   = sum_{allowed j} exp(S_ij - lse_i) v_j (0 if no j is allowed)
+ * The causal mask is the lower triangle including the diagonal ("FlashAttention
+ * 深度解析" section 五 lists it as built in).  The block mask is the
+ * block-sparse variant (IO-Awareness page section 4): a zero entry removes a
+ * whole 128 x 128 block and the kernels skip it; causal and block mask combine
+ * by intersection.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout    q, k, v, o, dO, dq, dk, dv: [B][H][N][d], row-major, d fastest,
+ *           densely packed (element (b,h,i,c) at ((b*H + h)*N + i)*d + c),
+ *           base addresses 16-byte aligned (lse: 4-byte aligned).
+ *           lse: float [B][H][N].  blockmask: uint8 [nb][nb], nb = ceil(N/128),
+ *           row-major, one mask shared by all (b, h).
+ * Types     fa_fwd / fa_bwd: bfloat16 tensors (raw 16-bit storage), fp32
+ *           accumulation, fp32 softmax statistics, outputs rounded to bfloat16
+ *           (round to nearest even).  fa_fwd_f32 / fa_bwd_f32: float tensors.
+ * Memory    every pointer is device memory owned by the caller.  The library
+ *           never allocates, frees or synchronizes, holds no global state and
+ *           is re-entrant.  Outputs must not alias inputs.
+ * Streams   `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *           enqueue work and return; results are ready once the stream is
+ *           synchronized.  Kernel faults surface at the caller's next sync.
+ * Limits    B, H, N >= 1; d in {64, 128} (the pages allow any multiple of 16 up
+ *           to 256; other values return FA_ERR_UNSUPPORTED); B*H*N*d < 2^31;
+ *           scale finite; with a blockmask, N <= 4194304.
+ * Errors    arguments are validated before anything is enqueued; on any
+ *           error nothing is enqueued and the outputs are untouched.
+ *           FA_ERR_HIP reports a failed kernel launch (hipGetLastError).
+ * Inputs    NaN/Inf in q, k, v or dO propagate; they are not checked.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, non-finite scale, aliasing, too large */
+    FA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. head dimension not 64 or 128) */
+    FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than fa_bwd_workspace_size() */
+    FA_ERR_HIP = 4          /* the HIP runtime reported an error while enqueueing */
+} fa_status;
+
+#define FA_MASK_BLOCK 128 /* block-mask granularity in rows and columns */
+#define FA_VERSION 1
+
+/*
+ * Forward, bfloat16.  q, k, v: const bf16 [B][H][N][d] (read).  o: bf16
+ * [B][H][N][d] (written).  lse: float [B][H][N] (written; natural-log
+ * logsumexp of the scaled, masked score row -- the saved statistic the
+ * backward needs).  causal: 0 or 1.  blockmask: NULL for dense.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int causal, const uint8_t* blockmask, void* stream);
+
+/* Forward, float32 tensors; same semantics as fa_fwd. */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, const uint8_t* blockmask, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd and fa_bwd_f32 need: an fp32 row vector
+ * D_i = sum_c dO_ic O_ic per (b, h, i) and an fp32 dQ accumulator
+ * [B][H][N][d], each 256-byte aligned.  Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward, bfloat16.  Inputs: q, k, v, o (the forward's output), dO (gradient
+ * of the loss w.r.t. o) as bf16 [B][H][N][d]; lse as written by fa_fwd.
+ * Outputs: dq, dk, dv bf16 [B][H][N][d] (written, rounded to bf16).  The
+ * scores and probabilities are recomputed from q, k and lse; nothing N x N is
+ * stored.  workspace: device buffer of at least fa_bwd_workspace_size() bytes,
+ * 256-byte aligned, contents ignored on entry and clobbered.  dQ is summed in
+ * fp32 with atomic adds, so dq may differ between runs in the last bits;
+ * dk and dv are deterministic.  scale, causal and blockmask must be the ones
+ * the forward used.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+           int causal, const uint8_t* blockmask, void* workspace, size_t workspace_bytes,
+           void* stream);
+
+/* Backward, float32 tensors; same semantics as fa_bwd (deterministic). */
+int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dO,
+               const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+               float scale, int causal, const uint8_t* blockmask, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* FA_VERSION of the loaded library. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,113 @@
+"""The C ABI library loads, exports what include/fa.h declares, and validates
+arguments before touching the GPU (CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_59_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# fake, never dereferenced device addresses (validation returns before any HIP call)
+P1, P2, P3, P4, P5, P6, P7, P8, P9 = (0x10000 * (i + 1) for i in range(9))
+BIG = 1 << 40  # spacing so that fake tensors do not overlap
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(fa_[a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.library_path()):
+        from exact_io_aware_59_amd import build
+        build.build()
+    return fa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_bwd_workspace_size",
+                          "fa_status_string", "fa_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status(lib):
+    assert fa.fa_version() == 1
+    for s in range(5):
+        assert fa.fa_status_string(s)
+    assert fa.fa_status_string(99) == "unknown status"
+
+
+def test_workspace_size(lib):
+    ws = fa.fa_bwd_workspace_size(2, 16, 4096, 128)
+    rows = 2 * 16 * 4096
+    assert ws == rows * 4 + rows * 128 * 4  # both parts already 256-byte multiples
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 64) == 256 + 768
+    assert fa.fa_bwd_workspace_size(0, 1, 1, 64) == 0
+
+
+def _fwd(lib, q=P1, k=P1 + BIG, v=P1 + 2 * BIG, o=P1 + 3 * BIG, lse=P1 + 4 * BIG, B=1, H=1, N=128, d=64,
+         scale=0.125, causal=0, mask=None, f32=False):
+    fn = lib.fa_fwd_f32 if f32 else lib.fa_fwd
+    return fn(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), causal, mask, None)
+
+
+def test_fwd_validation(lib):
+    nan = float("nan")
+    for f32 in (False, True):
+        assert _fwd(lib, q=None, f32=f32) == 1
+        assert _fwd(lib, lse=None, f32=f32) == 1
+        assert _fwd(lib, B=0, f32=f32) == 1
+        assert _fwd(lib, N=-5, f32=f32) == 1
+        assert _fwd(lib, scale=nan, f32=f32) == 1
+        assert _fwd(lib, scale=float("inf"), f32=f32) == 1
+        assert _fwd(lib, causal=2, f32=f32) == 1
+        assert _fwd(lib, d=96, f32=f32) == 2
+        assert _fwd(lib, d=256, f32=f32) == 2
+        assert _fwd(lib, B=1 << 20, H=1 << 10, N=4096, f32=f32) == 1  # more than 2^31 elements
+        assert _fwd(lib, o=P1, f32=f32) == 1  # output aliases q
+        assert _fwd(lib, lse=P1 + 3 * BIG + 100, f32=f32) == 1  # lse inside o
+        assert _fwd(lib, N=4194305, mask=P9, f32=f32) == 2
+
+
+def _bwd(lib, ws=P9, ws_bytes=None, B=1, H=1, N=128, d=64, dq=P1 + 6 * BIG, dk=P1 + 7 * BIG, dv=P1 + 8 * BIG,
+         scale=0.125, f32=False):
+    fn = lib.fa_bwd_f32 if f32 else lib.fa_bwd
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_size(B, H, N, d)
+    ws = ws + 16 * BIG if ws else ws
+    return fn(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG, dq, dk, dv, B, H, N, d,
+              ctypes.c_float(scale), 0, None, ws, ws_bytes, None)
+
+
+def test_bwd_validation(lib):
+    for f32 in (False, True):
+        assert _bwd(lib, ws=None, f32=f32) == 3
+        assert _bwd(lib, ws_bytes=100, f32=f32) == 3
+        assert _bwd(lib, ws=P9 + 8, f32=f32) == 3  # misaligned
+        assert _bwd(lib, dq=None, f32=f32) == 1
+        assert _bwd(lib, dk=P1 + 6 * BIG, f32=f32) == 1  # dk aliases dq
+        assert _bwd(lib, dv=P1, f32=f32) == 1  # dv aliases q
+        assert _bwd(lib, d=32, f32=f32) == 2
+        assert _bwd(lib, scale=float("nan"), f32=f32) == 1
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(fa, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        fa.load()
+
+
+def test_alignment_validation(lib):
+    assert _fwd(lib, q=P1 + 2) == 1
+    assert _fwd(lib, lse=P1 + 4 * BIG + 2) == 1
+    assert _bwd(lib, dq=P1 + 6 * BIG + 8) == 1

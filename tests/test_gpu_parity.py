@@ -1,0 +1,220 @@
+"""Parity of the HIP kernels (through the C ABI) with the fp64 oracle.
+
+Small shapes are compared element by element over every output; they span
+several tiles, ragged tails (N not a multiple of the 64/128-row tiles),
+causal and block masks (including rows with no allowed key), negative and
+zero scales.  The full-size workloads run in the launch configuration the
+benchmark times and are compared on seeded sampled rows (forward) or whole
+sampled heads (backward), which the oracle computes independently.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.gpu_cases import TOL_BF16, TOL_F32, check, say, to_device, to_host64
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import exact_io_aware_59_amd as fa  # noqa: E402
+
+
+def _mask_for(kind, N, seed):
+    nb = (N + 127) // 128
+    if kind is None:
+        return None
+    if kind == "rand":
+        return W.random_blockmask(nb, seed, p=0.6, keep_diag=True)
+    if kind == "rand_empty_rows":
+        m = W.random_blockmask(nb, seed, p=0.5)
+        m[-1, :] = 0  # the last block row attends nothing
+        return m
+    if kind == "band":
+        return W.make_blockmask(nb, seed, band=2, density=1 / 8)
+    raise ValueError(kind)
+
+
+def _dev_mask(m):
+    return None if m is None else torch.from_numpy(np.ascontiguousarray(m)).to("cuda:0")
+
+
+FWD_BF16 = [
+    # B, H, N, d, causal, mask, scale (None = 1/sqrt(d))
+    (1, 1, 1, 64, False, None, None),
+    (1, 2, 17, 64, True, None, None),
+    (2, 1, 128, 128, False, None, None),
+    (1, 2, 200, 128, True, None, None),
+    (1, 1, 333, 64, False, None, None),
+    (2, 2, 256, 64, True, None, None),
+    (1, 1, 1000, 128, True, None, None),
+    (1, 1, 777, 128, False, None, None),
+    (1, 1, 300, 128, False, "rand", None),
+    (1, 2, 384, 64, True, "rand", None),
+    (1, 1, 260, 128, False, "rand_empty_rows", None),
+    (1, 1, 520, 64, True, "rand_empty_rows", None),
+    (1, 1, 200, 128, True, None, -0.09),
+    (1, 1, 150, 64, False, None, 0.0),
+    (1, 1, 640, 64, False, "band", None),
+]
+
+
+@pytest.mark.parametrize("case", FWD_BF16, ids=lambda c: "B{}H{}N{}d{}{}{}{}".format(
+    *c[:4], "c" if c[4] else "", "-" + c[5] if c[5] else "", "" if c[6] is None else f"-s{c[6]}"))
+def test_fwd_bf16_small(case):
+    B, H, N, d, causal, mkind, scale = case
+    scale = float(np.float32(1 / math.sqrt(d) if scale is None else scale))
+    say(f"[fwd bf16] B={B} H={H} N={N} d={d} causal={causal} mask={mkind} scale={scale}")
+    x = W.make_inputs(B, H, N, d, "bf16", seed=11)
+    m = _mask_for(mkind, N, 5)
+    q, k, v = (to_device(x[n], "bf16") for n in "qkv")
+    o, lse = fa.forward(q, k, v, scale, causal, _dev_mask(m))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(x["q"].values, x["k"].values, x["v"].values, scale, causal, m)
+    check("O", to_host64(o), o_ref, TOL_BF16["o"])
+    check("lse", to_host64(lse), lse_ref, TOL_BF16["lse"])
+
+
+BWD_BF16 = [
+    (1, 1, 64, 64, False, None, None),
+    (1, 2, 200, 128, True, None, None),
+    (2, 1, 333, 64, False, None, None),
+    (1, 1, 300, 128, False, "rand", None),
+    (1, 1, 384, 128, True, "rand", None),
+    (1, 1, 260, 64, False, "rand_empty_rows", None),
+    (1, 1, 256, 128, True, None, -0.1),
+    (1, 1, 129, 128, False, None, None),
+]
+
+
+@pytest.mark.parametrize("case", BWD_BF16, ids=lambda c: "B{}H{}N{}d{}{}{}{}".format(
+    *c[:4], "c" if c[4] else "", "-" + c[5] if c[5] else "", "" if c[6] is None else f"-s{c[6]}"))
+def test_bwd_bf16_small(case):
+    B, H, N, d, causal, mkind, scale = case
+    scale = float(np.float32(1 / math.sqrt(d) if scale is None else scale))
+    say(f"[bwd bf16] B={B} H={H} N={N} d={d} causal={causal} mask={mkind} scale={scale}")
+    x = W.make_inputs(B, H, N, d, "bf16", seed=21, with_do=True)
+    m = _mask_for(mkind, N, 6)
+    q, k, v, do = (to_device(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    dm = _dev_mask(m)
+    o, lse = fa.forward(q, k, v, scale, causal, dm)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, scale, causal, dm)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attn_bwd(x["q"].values, x["k"].values, x["v"].values, x["do"].values, scale, causal, m)
+    check("dQ", to_host64(dq), rq, TOL_BF16["dq"])
+    check("dK", to_host64(dk), rk, TOL_BF16["dk"])
+    check("dV", to_host64(dv), rv, TOL_BF16["dv"])
+
+
+F32_CASES = [
+    (1, 1, 128, 64, False, None, None),  # the tiny fp32 workload
+    (1, 2, 77, 128, True, None, None),
+    (2, 1, 300, 64, False, "rand", None),
+    (1, 1, 260, 128, True, "rand_empty_rows", None),
+    (1, 1, 100, 64, False, None, -0.3),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "B{}H{}N{}d{}{}{}{}".format(
+    *c[:4], "c" if c[4] else "", "-" + c[5] if c[5] else "", "" if c[6] is None else f"-s{c[6]}"))
+def test_f32_fwd_bwd(case):
+    B, H, N, d, causal, mkind, scale = case
+    scale = float(np.float32(1 / math.sqrt(d) if scale is None else scale))
+    say(f"[f32] B={B} H={H} N={N} d={d} causal={causal} mask={mkind} scale={scale}")
+    x = W.make_inputs(B, H, N, d, "f32", seed=31, with_do=True)
+    m = _mask_for(mkind, N, 7)
+    q, k, v, do = (to_device(x[n], "f32") for n in ("q", "k", "v", "do"))
+    dm = _dev_mask(m)
+    o, lse = fa.forward(q, k, v, scale, causal, dm)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, scale, causal, dm)
+    torch.cuda.synchronize()
+    rq, rk, rv, ro, rl, _ = oracle.attn_bwd(x["q"].values, x["k"].values, x["v"].values, x["do"].values,
+                                            scale, causal, m, return_fwd=True)
+    check("O", to_host64(o), ro, TOL_F32["o"])
+    check("lse", to_host64(lse), rl, TOL_F32["lse"])
+    check("dQ", to_host64(dq), rq, TOL_F32["dq"])
+    check("dK", to_host64(dk), rk, TOL_F32["dk"])
+    check("dV", to_host64(dv), rv, TOL_F32["dv"])
+
+
+def test_fwd_deterministic():
+    say("[fwd determinism] B=1 H=4 N=1024 d=128 causal")
+    x = W.make_inputs(1, 4, 1024, 128, "bf16", seed=41)
+    q, k, v = (to_device(x[n], "bf16") for n in "qkv")
+    o1, l1 = fa.forward(q, k, v, None, True)
+    o2, l2 = fa.forward(q, k, v, None, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_empty_rows_exact():
+    """Rows whose block-mask row is all zero: O = 0 exactly and lse = -inf."""
+    say("[empty rows] N=384 d=64")
+    N = 384
+    x = W.make_inputs(1, 1, N, 64, "bf16", seed=51, with_do=True)
+    m = np.ones((3, 3), dtype=np.uint8)
+    m[1, :] = 0
+    q, k, v, do = (to_device(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, None, False, _dev_mask(m))
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, None, False, _dev_mask(m))
+    torch.cuda.synchronize()
+    assert torch.all(o[0, 0, 128:256] == 0)
+    assert torch.all(torch.isneginf(lse[0, 0, 128:256]))
+    assert torch.all(dq[0, 0, 128:256] == 0)
+    assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads (benchmark launch configuration), sampled comparison
+# ----------------------------------------------------------------------------
+
+FULL_FWD = ["bf16_fwd_b4h16n2048d64", "bf16_causal_fwd_b1h8n8192d128", "bf16_blocksparse_fwd_b1h8n65536d64",
+            "bf16_causal_fwdbwd_b2h16n4096d128"]
+
+
+@pytest.mark.parametrize("name", FULL_FWD)
+def test_full_size_fwd_sampled_rows(name):
+    w = W.WORKLOADS[name]
+    say(f"[full fwd] {name}")
+    x = W.workload_inputs(w, seed=0)
+    m = W.workload_mask(w, seed=0)
+    q, k, v = (to_device(x[n], "bf16") for n in "qkv")
+    o, lse = fa.forward(q, k, v, w.scale, w.causal, _dev_mask(m))
+    torch.cuda.synchronize()
+    rows = W.sample_rows(w.B * w.H, w.N, 512, seed=W.SEED_ROWS)
+    o_ref, l_ref = oracle.attn_fwd_rows(x["q"].values, x["k"].values, x["v"].values, w.scale, rows, w.causal, m)
+    of = o.reshape(w.B * w.H, w.N, w.d)
+    lf = lse.reshape(w.B * w.H, w.N)
+    idx0 = torch.from_numpy(rows[:, 0]).to("cuda:0")
+    idx1 = torch.from_numpy(rows[:, 1]).to("cuda:0")
+    check("O rows", to_host64(of[idx0, idx1]), o_ref, TOL_BF16["o"], f"max|O| = {np.abs(o_ref).max():.3f}")
+    check("lse rows", to_host64(lf[idx0, idx1]), l_ref, TOL_BF16["lse"])
+    # properties at every row: finite, |O| bounded by max |V| (convex combination)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    assert float(o.abs().max()) <= float(v.abs().max()) * (1 + 2 ** -7)
+
+
+def test_full_size_bwd_sampled_heads():
+    w = W.WORKLOADS["bf16_causal_fwdbwd_b2h16n4096d128"]
+    say(f"[full bwd] {w.name}")
+    x = W.workload_inputs(w, seed=0)
+    q, k, v, do = (to_device(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, w.scale, w.causal)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, w.scale, w.causal)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    for b, h in ((0, 0), (1, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = oracle.attn_bwd(x["q"].values[sl], x["k"].values[sl], x["v"].values[sl],
+                                     x["do"].values[sl], w.scale, w.causal)
+        say(f"  head b={b} h={h}: max|dV| = {np.abs(rv).max():.3f}")
+        check("dQ", to_host64(dq[b:b + 1, h:h + 1]), rq, TOL_BF16["dq"])
+        check("dK", to_host64(dk[b:b + 1, h:h + 1]), rk, TOL_BF16["dk"])
+        check("dV", to_host64(dv[b:b + 1, h:h + 1]), rv, TOL_BF16["dv"])
