@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark: exact attention forward + recompute backward on one MI355X.
+
+One step is the whole hot path over one batch of synthetic inputs:
+fa_fwd (fused forward, writes O and lse) followed by the backward's three
+stages fa_bwd_prep, fa_bwd_main and fa_bwd_dq (exactly what fa_bwd enqueues).
+Workload: B=2, H=16, N=4096, d=128, bf16, causal, iid N(0,1) inputs (seed 0).
+
+Prints one JSON line.  `value` is the whole step's throughput in TFLOP/s with
+the FLOP convention 4*B*H*N^2*d for the forward (halved for causal) and 2.5x
+that for the backward; inputs are resident in HBM before timing starts.
+HIP events on the launch stream time every kernel call of every timed step;
+`roofline` reports the backward's main kernel (the dominant one) against the
+bf16 dense matrix-core peak.  `cpu_baseline` times the fp64 oracle on a
+bounded sample of the same workload (a few heads).
+
+Options: --steps K --warmup W (timed / untimed steps), --gpus N (only 1 is
+supported: this build runs on a single GPU), --workload NAME (another
+workload of workloads.WORKLOADS, forward only unless it has a backward),
+--no-cpu-baseline, --copy-calib (run a plain device copy first, for the
+profiler's traffic calibration).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as W  # noqa: E402
+from workloads import accounting as A  # noqa: E402
+
+METRIC = "attention fwd/bwd TFLOP/s (4·B·H·N²·d, causal halved) and % of MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 bf16 FLOP/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "bf16_causal_fwdbwd_b2h16n4096d128"
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, x, mask_np, heads: int) -> dict:
+    """Time the fp64 oracle as it stands on a bounded sample of the workload.
+
+    Sample: forward (and backward) of the first `heads` heads of batch 0 when
+    a head's N x N matrices fit comfortably (N <= 8192); otherwise 512 seeded
+    sampled rows of the forward.
+    """
+    import oracle
+    sl = (slice(0, 1), slice(0, heads))
+    if w.N <= 8192:
+        t0 = time.perf_counter()
+        oracle.attn_fwd(x["q"].values[sl], x["k"].values[sl], x["v"].values[sl], w.scale, w.causal, mask_np)
+        if w.backward:
+            oracle.attn_bwd(x["q"].values[sl], x["k"].values[sl], x["v"].values[sl], x["do"].values[sl],
+                            w.scale, w.causal, mask_np)
+        dt = time.perf_counter() - t0
+        fl = A.fwd_flops(1, heads, w.N, w.d, w.causal, mask_np)
+        if w.backward:
+            fl += A.bwd_flops(1, heads, w.N, w.d, w.causal, mask_np)
+        what = (f"{'forward+backward' if w.backward else 'forward'} of heads (b=0, h=0..{heads - 1}) of "
+                f"{w.B * w.H}")
+    else:
+        rows = W.sample_rows(w.B * w.H, w.N, 512, seed=W.SEED_ROWS)
+        t0 = time.perf_counter()
+        oracle.attn_fwd_rows(x["q"].values, x["k"].values, x["v"].values, w.scale, rows, w.causal, mask_np)
+        dt = time.perf_counter() - t0
+        fl = A.fwd_flops(1, 1, w.N, w.d, w.causal, mask_np) * len(rows) / w.N
+        what = f"forward of 512 sampled rows of {w.B * w.H * w.N}"
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{what} (N={w.N}, d={w.d}, {'causal' if w.causal else 'non-causal'}), fp64, {dt:.2f} s",
+        "seconds": round(dt, 3),
+        "host_cpu": host_cpu_model(),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--copy-calib", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on a single GPU; --gpus must be 1 "
+              "(no multi-GPU path is implemented)", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_io_aware_59_amd as fa
+
+    w = W.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        print("bench.py: only bf16 workloads are benchmarked", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    x = W.workload_inputs(w, seed=0)
+    mask_np = W.workload_mask(w, seed=0)
+
+    def to_dev(t):
+        return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = (to_dev(x[n]) for n in "qkv")
+    do = to_dev(x["do"]) if w.backward else None
+    mask = torch.from_numpy(mask_np).to(dev) if mask_np is not None else None
+    B, H, N, d = w.B, w.H, w.N, w.d
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if w.backward:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = fa.workspace(B, H, N, d, dev)
+
+    if args.copy_calib:
+        # a plain copy of known size, for scaling the profiler's byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    n_ev = 5 if w.backward else 2
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, mask, stream)
+        if evs is not None:
+            evs[1].record(stream)
+        if w.backward:
+            fa.fa_bwd_prep(o, do, ws, stream)
+            if evs is not None:
+                evs[2].record(stream)
+            fa.fa_bwd_main(q, k, v, do, lse, dk, dv, w.scale, w.causal, mask, ws, stream)
+            if evs is not None:
+                evs[3].record(stream)
+            fa.fa_bwd_dq(dq, w.scale, ws, stream)
+            if evs is not None:
+                evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_fwd = [e[0].elapsed_time(e[1]) for e in events]
+    res = {"fwd_ms": statistics.median(t_fwd)}
+    if w.backward:
+        t_prep = [e[1].elapsed_time(e[2]) for e in events]
+        t_main = [e[2].elapsed_time(e[3]) for e in events]
+        t_dq = [e[3].elapsed_time(e[4]) for e in events]
+        res.update(bwd_prep_ms=statistics.median(t_prep), bwd_main_ms=statistics.median(t_main),
+                   bwd_dq_ms=statistics.median(t_dq))
+
+    flops = A.workload_flops(w, mask_np)
+    bytes_ = A.workload_bytes(w, mask_np)
+    total_flops = flops["fwd"] + flops.get("bwd", 0.0)
+    ms_per_step = wall / args.steps * 1e3
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    fwd_tflops = flops["fwd"] / (res["fwd_ms"] * 1e-3) / 1e12
+    extra = {
+        "fwd_ms": round(res["fwd_ms"], 4),
+        "fwd_tflops": round(fwd_tflops, 1),
+        "fwd_pct_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+    }
+    if w.backward:
+        bwd_ms = res["bwd_prep_ms"] + res["bwd_main_ms"] + res["bwd_dq_ms"]
+        bwd_tflops = flops["bwd"] / (bwd_ms * 1e-3) / 1e12
+        extra.update({
+            "bwd_ms": round(bwd_ms, 4),
+            "bwd_tflops": round(bwd_tflops, 1),
+            "bwd_pct_peak": round(100 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
+            "bwd_prep_ms": round(res["bwd_prep_ms"], 4),
+            "bwd_main_ms": round(res["bwd_main_ms"], 4),
+            "bwd_dq_ms": round(res["bwd_dq_ms"], 4),
+        })
+        dom_name, dom_ms, dom_flops = "bwd_bf16_kernel (fa_bwd_main)", res["bwd_main_ms"], flops["bwd"]
+    else:
+        dom_name, dom_ms, dom_flops = "fwd_bf16_kernel (fa_fwd)", res["fwd_ms"], flops["fwd"]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": None,
+        "kernel": dom_name,
+        "kernel_ms": round(dom_ms, 4),
+    }
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "B": B, "H": H, "N": N, "d": d,
+            "causal": w.causal,
+            "block_density": None if mask_np is None else float(mask_np.mean()),
+            "step": "fa_fwd + fa_bwd" if w.backward else "fa_fwd",
+            "step_flops": total_flops,
+            "algorithmic_bytes": sum(bytes_.values()),
+        },
+        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        **extra,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x, mask_np, min(args.cpu_heads, w.H))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -22,7 +22,8 @@ from typing import Optional, Tuple
 
 __all__ = [
     "FAError", "library_path", "load", "fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32",
-    "fa_bwd_workspace_size", "fa_status_string", "fa_version", "forward", "backward",
+    "fa_bwd_workspace_size", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq", "fa_status_string", "fa_version",
+    "forward", "backward", "workspace",
     "MASK_BLOCK",
 ]
 
@@ -55,7 +56,11 @@ def load():
     lib.fa_fwd_f32.argtypes = lib.fa_fwd.argtypes
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.fa_bwd_f32.argtypes = lib.fa_bwd.argtypes
-    for name in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_version"):
+    lib.fa_bwd_prep.argtypes = [vp, vp, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
+    lib.fa_bwd_dq.argtypes = [vp, i, i, i, i, f, vp, sz, vp]
+    for name in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq",
+                 "fa_version"):
         getattr(lib, name).restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
@@ -143,6 +148,30 @@ def fa_bwd_f32(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = Fal
     _check(load().fa_bwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                              _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                              _ptr(blockmask), _ptr(workspace), nbytes, _stream(stream)), "fa_bwd_f32")
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def fa_bwd_prep(o, do, workspace, stream=None):
+    B, H, N, d = _dims(o)
+    _check(load().fa_bwd_prep(_ptr(o), _ptr(do), B, H, N, d, _ptr(workspace), _nbytes(workspace),
+                              _stream(stream)), "fa_bwd_prep")
+
+
+def fa_bwd_main(q, k, v, do, lse, dk, dv, scale: float, causal: bool = False, blockmask=None, workspace=None,
+                stream=None):
+    B, H, N, d = _dims(q)
+    _check(load().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv), B, H, N, d,
+                              float(scale), int(bool(causal)), _ptr(blockmask), _ptr(workspace),
+                              _nbytes(workspace), _stream(stream)), "fa_bwd_main")
+
+
+def fa_bwd_dq(dq, scale: float, workspace, stream=None):
+    B, H, N, d = _dims(dq)
+    _check(load().fa_bwd_dq(_ptr(dq), B, H, N, d, float(scale), _ptr(workspace), _nbytes(workspace),
+                            _stream(stream)), "fa_bwd_dq")
 
 
 # ----------------------------------------------------------------------------

@@ -58,32 +58,50 @@ int fwd_common(const T* q, const T* k, const T* v, T* o, float* lse, int B, int 
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+enum Stage { kAll = 0, kPrep = 1, kMain = 2, kDq = 3 };
+
+// Validates and enqueues the backward (or one stage of it).  Tensors a stage
+// does not use may be NULL and are not checked.
 template <typename T>
 int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, const float* lse, T* dq, T* dk, T* dv,
                int B, int H, int N, int d, float scale, int causal, const uint8_t* mask, void* ws, size_t ws_bytes,
-               void* stream, bool bf16) {
-    if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) ||
-        !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3))
-        return FA_ERR_INVALID_ARG;
+               void* stream, bool bf16, Stage stage) {
+    const bool use_qkv = stage == kAll || stage == kMain;
+    const bool use_o = stage == kAll || stage == kPrep;
+    const bool use_do = stage != kDq;
+    const bool use_dq = stage == kAll || stage == kDq;
+    const bool use_dkdv = stage == kAll || stage == kMain;
+    if (use_qkv && (!q || !k || !v || !lse)) return FA_ERR_INVALID_ARG;
+    if (use_o && !o) return FA_ERR_INVALID_ARG;
+    if (use_do && !dO) return FA_ERR_INVALID_ARG;
+    if (use_dq && !dq) return FA_ERR_INVALID_ARG;
+    if (use_dkdv && (!dk || !dv)) return FA_ERR_INVALID_ARG;
+    const void* all[] = {q, k, v, o, dO, dq, dk, dv};
+    for (const void* p : all)
+        if (p && !aligned16(p)) return FA_ERR_INVALID_ARG;
+    if (lse && ((uintptr_t)lse & 3)) return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     int st = check_sizes(B, H, N, d, scale, mask);
     if (st != FA_OK) return st;
-    const size_t tb = (size_t)B * H * N * d * sizeof(T);
+    const size_t tb = (size_t)B * H * N * d * sizeof(T), lb = (size_t)B * H * N * sizeof(float);
     const void* ins[] = {q, k, v, o, dO};
     void* outs[] = {dq, dk, dv};
     for (void* x : outs) {
+        if (!x) continue;
         for (const void* y : ins)
-            if (overlap(x, tb, y, tb)) return FA_ERR_INVALID_ARG;
-        if (overlap(x, tb, lse, (size_t)B * H * N * sizeof(float))) return FA_ERR_INVALID_ARG;
+            if (y && overlap(x, tb, y, tb)) return FA_ERR_INVALID_ARG;
+        if (lse && overlap(x, tb, lse, lb)) return FA_ERR_INVALID_ARG;
     }
-    if (overlap(dq, tb, dk, tb) || overlap(dq, tb, dv, tb) || overlap(dk, tb, dv, tb)) return FA_ERR_INVALID_ARG;
+    for (int i = 0; i < 3; i++)
+        for (int j = i + 1; j < 3; j++)
+            if (outs[i] && outs[j] && overlap(outs[i], tb, outs[j], tb)) return FA_ERR_INVALID_ARG;
     const size_t need = fa_bwd_workspace_size(B, H, N, d);
     if (!ws || ws_bytes < need || ((uintptr_t)ws % kAlign) != 0) return FA_ERR_WORKSPACE;
     for (void* x : outs)
-        if (overlap(x, tb, ws, need)) return FA_ERR_INVALID_ARG;
+        if (x && overlap(x, tb, ws, need)) return FA_ERR_INVALID_ARG;
     for (const void* y : ins)
-        if (overlap(ws, need, y, tb)) return FA_ERR_INVALID_ARG;
+        if (y && overlap(ws, need, y, tb)) return FA_ERR_INVALID_ARG;
+    if (lse && overlap(ws, need, lse, lb)) return FA_ERR_INVALID_ARG;
     fa::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
     a.dq = dq; a.dk = dk; a.dv = dv;
@@ -95,7 +113,12 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
     a.ws_D = (float*)ws;
     a.ws_dq = (float*)((char*)ws + align_up((size_t)B * H * N * sizeof(float)));
     a.stream = (hipStream_t)stream;
-    hipError_t e = bf16 ? fa::launch_bwd_bf16(a) : fa::launch_bwd_f32(a);
+    hipError_t e;
+    if (!bf16) e = fa::launch_bwd_f32(a);
+    else if (stage == kPrep) e = fa::launch_bwd_prep_bf16(a);
+    else if (stage == kMain) e = fa::launch_bwd_main_bf16(a);
+    else if (stage == kDq) e = fa::launch_bwd_dq_bf16(a);
+    else e = fa::launch_bwd_bf16(a);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -125,14 +148,35 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* workspace, size_t workspace_bytes, void* stream) {
     return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
                                 (const uint16_t*)dO, lse, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, B, H, N, d,
-                                scale, causal, blockmask, workspace, workspace_bytes, stream, true);
+                                scale, causal, blockmask, workspace, workspace_bytes, stream, true, kAll);
+}
+
+int fa_bwd_prep(const void* o, const void* dO, int B, int H, int N, int d, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    return bwd_common<uint16_t>(nullptr, nullptr, nullptr, (const uint16_t*)o, (const uint16_t*)dO, nullptr,
+                                nullptr, nullptr, nullptr, B, H, N, d, 1.0f, 0, nullptr, workspace, workspace_bytes,
+                                stream, true, kPrep);
+}
+
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, nullptr,
+                                (const uint16_t*)dO, lse, nullptr, (uint16_t*)dk, (uint16_t*)dv, B, H, N, d, scale,
+                                causal, blockmask, workspace, workspace_bytes, stream, true, kMain);
+}
+
+int fa_bwd_dq(void* dq, int B, int H, int N, int d, float scale, void* workspace, size_t workspace_bytes,
+              void* stream) {
+    return bwd_common<uint16_t>(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, (uint16_t*)dq, nullptr,
+                                nullptr, B, H, N, d, scale, 0, nullptr, workspace, workspace_bytes, stream, true, kDq);
 }
 
 int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dO, const float* lse,
                float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
                const uint8_t* blockmask, void* workspace, size_t workspace_bytes, void* stream) {
     return bwd_common<float>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, blockmask, workspace,
-                             workspace_bytes, stream, false);
+                             workspace_bytes, stream, false, kAll);
 }
 
 const char* fa_status_string(int status) {

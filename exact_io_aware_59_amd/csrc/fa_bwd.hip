@@ -363,27 +363,44 @@ hipError_t launch_main(const BwdArgs& a) {
 }
 
 template <int D>
-hipError_t launch_all(const BwdArgs& a) {
+hipError_t launch_prep(const BwdArgs& a) {
     const long rows = (long)a.BH * a.N;
     const long nthr = rows * (D / 8);
     hipLaunchKernelGGL(rowdot_kernel<D>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, a.stream,
                        (const bf16*)a.o, (const bf16*)a.dO, a.ws_D, a.ws_dq, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_main_all(const BwdArgs& a) {
     const bool m = a.mask != nullptr;
-    if (a.causal) e = m ? launch_main<D, true, true>(a) : launch_main<D, true, false>(a);
-    else e = m ? launch_main<D, false, true>(a) : launch_main<D, false, false>(a);
-    if (e != hipSuccess) return e;
-    const long n8 = rows * D / 8;
+    if (a.causal) return m ? launch_main<D, true, true>(a) : launch_main<D, true, false>(a);
+    return m ? launch_main<D, false, true>(a) : launch_main<D, false, false>(a);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep_bf16(const BwdArgs& a) {
+    return a.d == 128 ? launch_prep<128>(a) : launch_prep<64>(a);
+}
+
+hipError_t launch_bwd_main_bf16(const BwdArgs& a) {
+    return a.d == 128 ? launch_main_all<128>(a) : launch_main_all<64>(a);
+}
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
+    const long n8 = (long)a.BH * a.N * a.d / 8;
     hipLaunchKernelGGL(dq_out_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, a.stream, a.ws_dq,
                        (bf16*)a.dq, a.scale, n8);
     return hipGetLastError();
 }
 
-}  // namespace
-
 hipError_t launch_bwd_bf16(const BwdArgs& a) {
-    return a.d == 128 ? launch_all<128>(a) : launch_all<64>(a);
+    hipError_t e = launch_bwd_prep_bf16(a);
+    if (e != hipSuccess) return e;
+    e = launch_bwd_main_bf16(a);
+    if (e != hipSuccess) return e;
+    return launch_bwd_dq_bf16(a);
 }
 
 }  // namespace fa

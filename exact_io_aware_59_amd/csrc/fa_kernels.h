@@ -46,7 +46,10 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
-hipError_t launch_bwd_bf16(const BwdArgs& a);
+hipError_t launch_bwd_bf16(const BwdArgs& a);  // the three stages below, in order
+hipError_t launch_bwd_prep_bf16(const BwdArgs& a);
+hipError_t launch_bwd_main_bf16(const BwdArgs& a);
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_f32(const BwdArgs& a);
 

@@ -104,6 +104,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int causal, const uint8_t* blockmask, void* workspace, size_t workspace_bytes,
            void* stream);
 
+/*
+ * The three stages fa_bwd enqueues, for callers that want to schedule or time
+ * them separately.  fa_bwd(...) is exactly fa_bwd_prep, fa_bwd_main and
+ * fa_bwd_dq on the same stream with the same workspace.
+ *   fa_bwd_prep: D_i = sum_c dO_ic O_ic into the workspace; clears the fp32 dQ
+ *                accumulator.  Reads o, dO.
+ *   fa_bwd_main: recomputes S and P per tile from q, k and lse; writes dk, dv
+ *                (bf16) and adds scale-free dQ contributions into the
+ *                accumulator.  Needs the workspace as left by fa_bwd_prep.
+ *   fa_bwd_dq:   dq = scale * accumulator, rounded to bf16.
+ * Validation and error codes as for fa_bwd.
+ */
+int fa_bwd_prep(const void* o, const void* dO, int B, int H, int N, int d, void* workspace,
+                size_t workspace_bytes, void* stream);
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                const uint8_t* blockmask, void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_dq(void* dq, int B, int H, int N, int d, float scale, void* workspace,
+              size_t workspace_bytes, void* stream);
+
 /* Backward, float32 tensors; same semantics as fa_bwd (deterministic). */
 int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dO,
                const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,

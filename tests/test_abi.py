@@ -111,3 +111,17 @@ def test_alignment_validation(lib):
     assert _fwd(lib, q=P1 + 2) == 1
     assert _fwd(lib, lse=P1 + 4 * BIG + 2) == 1
     assert _bwd(lib, dq=P1 + 6 * BIG + 8) == 1
+
+
+def test_stage_validation(lib):
+    ws = P9 + 16 * BIG
+    nbytes = lib.fa_bwd_workspace_size(1, 1, 128, 64)
+    assert lib.fa_bwd_prep(None, P2, 1, 1, 128, 64, ws, nbytes, None) == 1
+    assert lib.fa_bwd_prep(P1, P2, 1, 1, 128, 64, ws, nbytes - 1, None) == 3
+    assert lib.fa_bwd_prep(P1, P1 + BIG, 1, 1, 128, 96, ws, nbytes, None) == 2
+    assert lib.fa_bwd_dq(None, 1, 1, 128, 64, ctypes.c_float(0.1), ws, nbytes, None) == 1
+    assert lib.fa_bwd_dq(P1, 1, 1, 128, 64, ctypes.c_float(0.1), None, nbytes, None) == 3
+    assert lib.fa_bwd_main(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, None, P1 + 4 * BIG, P1 + 5 * BIG,
+                           1, 1, 128, 64, ctypes.c_float(0.1), 0, None, ws, nbytes, None) == 1
+    assert lib.fa_bwd_main(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 6 * BIG, P1 + 4 * BIG, P1 + 4 * BIG,
+                           1, 1, 128, 64, ctypes.c_float(0.1), 0, None, ws, nbytes, None) == 1  # dk aliases dv
