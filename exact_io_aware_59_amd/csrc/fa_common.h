@@ -109,6 +109,66 @@ __device__ __forceinline__ bf16x8 lds_read_tr_operand(const bf16* tile, int row0
     return r;
 }
 
+// ---------------------------------------------------------------------------
+// Buffer resources (gfx9 descriptor): loads past num_records bytes return 0
+// and stores past it are dropped, which handles ragged tails without branches.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// 16 bytes per lane from global straight into LDS: lane i writes lds_base + 16*i
+// (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, void* lds_base, uint32_t byte_off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, byte_off, 0,
+                                             0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Padded row-major tiles in LDS (row stride = D + pad elements).  A stride of
+// 16*odd bytes mod 256 makes 16 consecutive rows of a 16-byte column hit 16
+// distinct bank groups (operand reads with ds_read_b128); a stride of 64 mod
+// 256 bytes makes 4 consecutive rows of 64 bytes disjoint (transposing reads
+// by half a wave).  Every operand address is then a base plus an immediate.
+// ---------------------------------------------------------------------------
+template <int D>
+struct PadK {  // tiles read with ds_read_b128 (16 rows x 16 B)
+    static constexpr int STRIDE = D + 8;  // 272 B (d=128) or 144 B (d=64)
+};
+template <int D>
+struct PadV {  // tiles read with ds_read_tr16_b64 (4 rows x 64 B per half-wave)
+    static constexpr int STRIDE = D + 32;  // 320 B (d=128) or 192 B (d=64)
+};
+
+// Transposing A-operand read from a padded row-major tile (see
+// lds_read_tr_operand): lane l obtains
+// tile[row0 + 8*(i/4) + 4*(l/32) + i%4][col0 + l%32], i = 0..7.
+// `lane_base` = tile + lane_tr_offset<STRIDE>(lane), computed once.
+template <int STRIDE>
+__device__ __forceinline__ int lane_tr_offset(int lane) {
+    const int s = lane & 15, j = s >> 2, q = s & 3, g = (lane >> 4) & 1, h = lane >> 5;
+    return (4 * h + j) * STRIDE + 16 * g + 4 * q;
+}
+template <int STRIDE>
+__device__ __forceinline__ bf16x8 lds_tr_operand_pad(const bf16* lane_base, int row0, int col0) {
+    const bf16x4 lo = lds_read_tr4(lane_base, row0 * STRIDE + col0);
+    const bf16x4 hi = lds_read_tr4(lane_base, (row0 + 8) * STRIDE + col0);
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgVmem = 0x020;
+
 // Workgroup id -> logical work item such that consecutive logical items land
 // on the same XCD (the hardware deals workgroups round-robin over the 8 XCDs),
 // so tiles of one (batch, head) share that XCD's L2.

@@ -1,29 +1,35 @@
 // Fused exact-attention forward for bf16 on gfx950.
 //
 // One workgroup (4 waves) owns 128 query rows of one (batch, head) and sweeps
-// the K/V tiles that its mask allows: the Q-outer loop order of
-// FlashAttention-2 with the grid spread over batch x heads x query blocks
-// ("FlashAttention 深度解析" section 四; "FlashAttention原理概览" section 3.1).
-// Per K/V tile every wave computes S^T = K Q^T for its 32 queries on the
-// matrix cores, folds the tile into a running row max and row sum (online
-// softmax, "FlashAttention 深度解析" section 二), and accumulates
-// O^T += V^T P^T, again on the matrix cores.  S and P live only in registers;
-// K and V tiles go through LDS with the next tile's global loads in flight
-// while the current one is computed ("FlashAttention原理概览" section 3.3).
-// O is divided by the row sum once, after the last tile (section 四).
+// the K/V tiles its mask allows: the Q-outer loop order of FlashAttention-2
+// with the grid spread over batch x heads x query blocks ("FlashAttention
+// 深度解析" section 四; "FlashAttention原理概览" section 3.1).  Per K/V tile
+// every wave computes S^T = K Q^T for its 32 queries on the matrix cores,
+// folds the tile into a running row max and row sum (online softmax,
+// "FlashAttention 深度解析" section 二) and accumulates O^T += V^T P^T, again
+// on the matrix cores.  S and P live only in registers; O is divided by the
+// row sum once, after the last tile (section 四).
 //
-// Layout choices for CDNA4:
+// Layout and scheduling choices for CDNA4:
 //  * S is computed transposed (keys x queries) so each lane owns one query:
 //    the row max and row sum are in-lane reductions plus one half-wave swap.
-//  * The S^T accumulator is converted in place to the B operand of the
-//    O^T = V^T P^T product; V is read transposed straight from its row-major
-//    LDS tile with ds_read_tr16_b64, matching the accumulator's key order.
-//  * The softmax runs in the log2 domain: p = 2^(s*c - m*c) with
-//    c = |scale|*log2(e) applied by one FMA; a negative scale is handled by
-//    negating Q (exact in bf16).  The running max is only moved when it grows
-//    by more than 8 (in log2 units), which keeps p <= 256 and skips most O
-//    rescales; the result is the same exact quantity since O and l always
-//    share one reference point.
+//  * The S^T accumulator, rounded to bf16 in place, is the B operand of
+//    O^T = V^T P^T; V is read transposed straight from its row-major LDS tile
+//    with ds_read_tr16_b64, in the accumulator's key order.
+//  * K and V tiles travel HBM -> LDS with buffer_load ... lds (no register
+//    staging); the XOR swizzle of the LDS tile is applied by choosing each
+//    lane's source address.  Rows past N read as zero (buffer range check).
+//  * K runs one tile ahead of V: while the exponentials of tile j are being
+//    computed on the vector ALUs, the matrix cores already compute S for tile
+//    j+1; the P V products of tile j then overlap the row max of tile j+1
+//    ("FlashAttention原理概览" section 3.3: overlap compute with data movement).
+//  * Softmax in the log2 domain: p = 2^(s*c - m*c), c = |scale|*log2(e), one
+//    FMA per score; a negative scale negates Q (exact in bf16).  The reference
+//    max only moves when the running max grows by more than 8 (log2 units), so
+//    p <= 256 and O is rarely rescaled; O and l share one reference point, so
+//    the result is the same exact quantity.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -38,28 +44,102 @@ constexpr float kRescaleThreshold = 8.0f;
 
 template <int D>
 struct FwdCfg {
-    static constexpr int BC = 8192 / D;       // keys per K/V tile: 64 (d=128) or 128 (d=64)
-    static constexpr int NKB = BC / 32;       // 32-key blocks per tile
-    static constexpr int NKK = D / 16;        // k-steps of the S product
-    static constexpr int NDM = D / 32;        // 32-dim blocks of O
-    static constexpr int TILE = BC * D;       // elements of one K (or V) tile
-    static constexpr int CHUNKS = TILE / 8;   // 16-byte chunks per tile
-    static constexpr int LD_PER_THREAD = CHUNKS / kThreads;
-    static_assert(LD_PER_THREAD * kThreads == CHUNKS, "tile must split evenly over the threads");
+    static constexpr int BC = 64;            // keys per K/V tile
+    static constexpr int NKB = BC / 32;      // 32-key blocks per tile
+    static constexpr int NKK = D / 16;       // k-steps of the S product
+    static constexpr int NDM = D / 32;       // 32-dim blocks of O
+    static constexpr int NT = BC / 16;       // k-steps of the PV product
+    static constexpr int KS = PadK<D>::STRIDE;
+    static constexpr int VS = PadV<D>::STRIDE;
+    static constexpr int KTILE = BC * KS;    // elements of a padded K tile
+    static constexpr int VTILE = BC * VS;
+    static constexpr int KSEGS = KTILE / 512;  // 1 KB segments (one wave-wide 16 B/lane copy each)
+    static constexpr int VSEGS = VTILE / 512;
+    static_assert(KSEGS * 512 == KTILE && VSEGS * 512 == VTILE, "tiles must be whole 1 KB segments");
     static_assert(kMaskBlock % BC == 0, "a mask block must hold whole tiles");
 };
 
 // Which K/V tiles a query block visits.
 struct TileList {
-    int n;          // number of tiles
-    int tpb;        // tiles per mask block (mask mode)
+    int n;                  // number of tiles
+    int tpb;                // tiles per mask block (mask mode)
     int bc;
-    const uint16_t* cols;  // mask mode: allowed mask columns (LDS)
+    const uint16_t* cols;   // mask mode: allowed mask columns (LDS)
     __device__ __forceinline__ int kv0(int it) const {
         if (cols == nullptr) return it * bc;
         return cols[it / tpb] * kMaskBlock + (it % tpb) * bc;
     }
 };
+
+// Issue the HBM -> LDS copy of BC rows (kv0 ..) of a [N][D] tensor into a
+// padded tile of row stride STRIDE.  The tile is cut into 1 KB segments,
+// dealt round-robin to the waves; a lane whose 16 bytes fall in row padding
+// re-reads the row's first chunk (in range, never used).
+template <int D, int STRIDE, int SEGS>
+__device__ __forceinline__ void load_tile(rsrc_t r, bf16* tile, int kv0, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < (SEGS + kWaves - 1) / kWaves; i++) {
+        const int s = i * kWaves + wave;
+        if (s < SEGS) {
+            const int el = s * 512 + lane * 8;
+            const int row = el / STRIDE;
+            int col = el - row * STRIDE;
+            col = col < D ? col : 0;
+            buf_load16_lds(r, tile + s * 512, ((uint32_t)(kv0 + row) * D + col) * 2);
+        }
+    }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Scores of keys past the causal diagonal or past N become -inf.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[FwdCfg<D>::NKB], int kv0, int my_q, int N, int h) {
+    using C = FwdCfg<D>;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; kb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+            const bool dead = (CAUSAL && key > my_q) || key >= N;
+            s[kb][r] = dead ? -INFINITY : s[kb][r];
+        }
+}
+
+template <int D>
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[FwdCfg<D>::NKB]) {
+    using C = FwdCfg<D>;
+    float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; kb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) m[r & 3] = fmaxf(m[r & 3], s[kb][r]);
+    return xhalf_max(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])));
+}
+
+// S^T of one tile: s[kb] += K[32kb + l32][..] . Q[my_q][..]; `kl` is this lane's row base.
+template <int D>
+__device__ __forceinline__ void tile_scores(const bf16* kl, const bf16x8 (&qf)[D / 16], f32x16 (&s)[FwdCfg<D>::NKB]) {
+    using C = FwdCfg<D>;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; kb++) s[kb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; kk++)
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; kb++)
+            s[kb] = mfma32(lds_read8(kl, 32 * kb * C::KS + 16 * kk), qf[kk], s[kb]);
+}
+
+// O^T += V^T P^T for one tile; `vl` is this lane's transposing-read base.
+template <int D>
+__device__ __forceinline__ void tile_pv(const bf16* vl, const bf16x8 (&pb)[FwdCfg<D>::NT], f32x16 (&o)[D / 32]) {
+    using C = FwdCfg<D>;
+#pragma unroll
+    for (int t = 0; t < C::NT; t++)
+#pragma unroll
+        for (int dm = 0; dm < C::NDM; dm++)
+            o[dm] = mfma32(lds_tr_operand_pad<C::VS>(vl, 16 * t, 32 * dm), pb[t], o[dm]);
+}
 
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
@@ -67,13 +147,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     bf16* __restrict__ O, float* __restrict__ LSE, int N, float c, uint32_t qsign,
     const uint8_t* __restrict__ mask, int nb, int nqb, int n_items) {
     using C = FwdCfg<D>;
-    __shared__ __attribute__((aligned(16))) bf16 kbuf[2][C::TILE];
-    __shared__ __attribute__((aligned(16))) bf16 vbuf[2][C::TILE];
+    // four separate arrays (not one 2-D array) so that alias analysis can tell
+    // the tile being read from the tile the DMA is filling
+    __shared__ __attribute__((aligned(1024))) bf16 kbuf0[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) bf16 kbuf1[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) bf16 vbuf0[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) bf16 vbuf1[C::VTILE];
     __shared__ int wave_cnt[kWaves];
     extern __shared__ uint16_t mask_cols[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
     const int h = lane >> 5, l32 = lane & 31;
+    const int k_lane = l32 * C::KS + 8 * h;            // this lane's K operand offset in a tile
+    const int v_lane = lane_tr_offset<C::VS>(lane);    // this lane's transposing-read offset
 
     // work item -> (bh, up to two query blocks); causal pairs block p with nqb-1-p
     const int item = xcd_remap(blockIdx.x, n_items);
@@ -92,9 +179,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         nblk = 1;
     }
     const size_t head_off = (size_t)bh * N * D;
-    const bf16* Qh = Q + head_off;
-    const bf16* Kh = K + head_off;
-    const bf16* Vh = V + head_off;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const rsrc_t rq = make_rsrc(Q + head_off, head_bytes);
+    const rsrc_t rk = make_rsrc(K + head_off, head_bytes);
+    const rsrc_t rv = make_rsrc(V + head_off, head_bytes);
+    const rsrc_t ro = make_rsrc(O + head_off, head_bytes);
+    const rsrc_t rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
 
     for (int bi = 0; bi < nblk; bi++) {
         const int qb = qblk[bi];
@@ -120,96 +210,59 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
         // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
         bf16x8 qf[C::NKK];
-        {
-            const bool ok = my_q < N;
-            const bf16* src = Qh + (size_t)(ok ? my_q : 0) * D + 8 * h;
 #pragma unroll
-            for (int kk = 0; kk < C::NKK; kk++) {
-                u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(src + 16 * kk) : u32x4{0, 0, 0, 0};
-                raw ^= qsign;
-                qf[kk] = __builtin_bit_cast(bf16x8, raw);
-            }
+        for (int kk = 0; kk < C::NKK; kk++) {
+            u32x4 raw = buf_load16(rq, (uint32_t)(my_q * D + 16 * kk + 8 * h) * 2);
+            raw ^= qsign;
+            qf[kk] = __builtin_bit_cast(bf16x8, raw);
         }
 
         f32x16 oacc[C::NDM];
 #pragma unroll
         for (int dm = 0; dm < C::NDM; dm++) oacc[dm] = f32x16{};
-        float m_ref = -INFINITY;  // running max of raw scores (reference point)
+        float m_ref = -INFINITY;  // reference max of raw scores (moves lazily)
         float l_part = 0.f;       // this lane's half of the running sum
 
-        // ---- staging of K/V tiles: global -> registers -> swizzled LDS ----
-        u32x4 kst[C::LD_PER_THREAD], vst[C::LD_PER_THREAD];
-        auto gload = [&](int kv0) {
-#pragma unroll
-            for (int i = 0; i < C::LD_PER_THREAD; i++) {
-                const int idx = tid + kThreads * i;
-                const int row = idx / (D / 8), ch = idx % (D / 8);
-                const bool ok = kv0 + row < N;
-                const size_t off = (size_t)(ok ? kv0 + row : 0) * D + ch * 8;
-                kst[i] = ok ? *reinterpret_cast<const u32x4*>(Kh + off) : u32x4{0, 0, 0, 0};
-                vst[i] = ok ? *reinterpret_cast<const u32x4*>(Vh + off) : u32x4{0, 0, 0, 0};
-            }
-        };
-        auto lstore = [&](int buf) {
-#pragma unroll
-            for (int i = 0; i < C::LD_PER_THREAD; i++) {
-                const int idx = tid + kThreads * i;
-                const int row = idx / (D / 8), ch = idx % (D / 8);
-                const int off = swz<D>(row, ch * 8);
-                *reinterpret_cast<u32x4*>(&kbuf[buf][off]) = kst[i];
-                *reinterpret_cast<u32x4*>(&vbuf[buf][off]) = vst[i];
-            }
-        };
+        auto needs_mask = [&](int kv0) { return (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N); };
 
+        // ---- prologue: K0, V0, K1 in flight; S(0) and its max ----
+        f32x16 sa[C::NKB], sb[C::NKB];
+        float mx_cur = -INFINITY;
         if (tl.n > 0) {
-            gload(tl.kv0(0));
-            lstore(0);
+            load_tile<D, C::KS, C::KSEGS>(rk, kbuf0, tl.kv0(0), wave, lane);
+            load_tile<D, C::VS, C::VSEGS>(rv, vbuf0, tl.kv0(0), wave, lane);
+            if (tl.n > 1) load_tile<D, C::KS, C::KSEGS>(rk, kbuf1, tl.kv0(1), wave, lane);
+            wait_vmem();
         }
         __syncthreads();
+        if (tl.n > 0) {
+            const int kv0 = tl.kv0(0);
+            tile_scores<D>(kbuf0 + k_lane, qf, sa);
+            if (needs_mask(kv0)) mask_scores<D, CAUSAL>(sa, kv0, my_q, N, h);
+            mx_cur = tile_max<D>(sa);
+        }
+        __syncthreads();  // every wave is done with kbuf0 before K2 overwrites it
 
-        for (int it = 0; it < tl.n; it++) {
-            const int buf = it & 1;
-            const int kv0 = tl.kv0(it);
-            if (it + 1 < tl.n) gload(tl.kv0(it + 1));
+        // One pipelined step: tile `it` (scores in sc, max mx_cur) is exponentiated
+        // and multiplied into O while the scores of tile it+1 land in sn.
+        // P = parity of `it`: tile it lives in kbuf<P>/vbuf<P>, tile it+1 in the other pair.
+        auto step = [&](auto parity, int it, f32x16 (&sc)[C::NKB], f32x16 (&sn)[C::NKB]) {
+            constexpr int P = decltype(parity)::value;
+            bf16* k_this = P ? kbuf1 : kbuf0;   // K(it), then K(it+2)
+            bf16* k_next = P ? kbuf0 : kbuf1;   // K(it+1)
+            bf16* v_this = P ? vbuf1 : vbuf0;   // V(it)
+            bf16* v_next = P ? vbuf0 : vbuf1;   // V(it+1)
+            const bool has_next = it + 1 < tl.n;
+            const int kv1 = has_next ? tl.kv0(it + 1) : 0;
+            // HBM -> LDS: K of tile it+2 and V of tile it+1 (their buffers were last read before the barrier)
+            if (it + 2 < tl.n) load_tile<D, C::KS, C::KSEGS>(rk, k_this, tl.kv0(it + 2), wave, lane);
+            if (has_next) load_tile<D, C::VS, C::VSEGS>(rv, v_next, kv1, wave, lane);
 
-            // Does this wave see any key of the tile?  Does it need element masks?
-            const bool wave_skip = CAUSAL && kv0 > qw + kQPerWave - 1;
-            const bool need_mask = (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N);
-            if (!wave_skip) {
-                const bf16* kt = kbuf[buf];
-                const bf16* vt = vbuf[buf];
-                // ---- S^T = K Q^T (keys x queries), fp32 accumulate ----
-                f32x16 s[C::NKB];
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; kb++) s[kb] = f32x16{};
-#pragma unroll
-                for (int kk = 0; kk < C::NKK; kk++) {
-#pragma unroll
-                    for (int kb = 0; kb < C::NKB; kb++) {
-                        const bf16x8 a = lds_read8(kt, swz<D>(32 * kb + l32, 16 * kk + 8 * h));
-                        s[kb] = mfma32(a, qf[kk], s[kb]);
-                    }
-                }
-                // ---- masks: causal (key > query) and keys past N ----
-                if (need_mask) {
-#pragma unroll
-                    for (int kb = 0; kb < C::NKB; kb++)
-#pragma unroll
-                        for (int r = 0; r < 16; r++) {
-                            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                            const bool dead = (CAUSAL && key > my_q) || key >= N;
-                            s[kb][r] = dead ? -INFINITY : s[kb][r];
-                        }
-                }
-                // ---- online softmax: tile max, lazy rescale, exponentials ----
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; kb++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[kb][r]);
-                mx = xhalf_max(mx);
-                const float m_new = fmaxf(m_ref, mx);
-                const bool bump = m_new != -INFINITY && (m_ref == -INFINITY || (m_new - m_ref) * c > kRescaleThreshold);
+            // ---- reference-max update for tile it (rare O rescale) ----
+            {
+                const float m_new = fmaxf(m_ref, mx_cur);
+                const bool bump = m_new != -INFINITY &&
+                                  (m_ref == -INFINITY || (m_new - m_ref) * c > kRescaleThreshold);
                 if (__builtin_expect(__ballot(bump) != 0, 0)) {
                     const float alpha = bump ? (m_ref == -INFINITY ? 0.f : exp2f_hw((m_ref - m_new) * c)) : 1.f;
                     if (bump) m_ref = m_new;
@@ -217,53 +270,71 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
                     for (int dm = 0; dm < C::NDM; dm++) oacc[dm] *= alpha;
                 }
-                const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
-                float lsum = 0.f;
+            }
+            const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
+
+            // ---- phase A: S(it+1) on the matrix cores, 2^(c s - c m) of tile it on the VALU ----
+            // (a tile past the end computes S on stale LDS data; its result is never used)
+            bf16x8 pb[C::NT];
+            {
+                const bf16* kl = k_next + k_lane;
 #pragma unroll
-                for (int kb = 0; kb < C::NKB; kb++)
+                for (int kb = 0; kb < C::NKB; kb++) sn[kb] = f32x16{};
+                float ls[4] = {0.f, 0.f, 0.f, 0.f};   // independent partial sums (short dependency chains)
+                constexpr int NM = C::NKK * C::NKB;   // MFMAs in this phase
+                constexpr int EPM = 16 * C::NKB / NM; // exponentials per MFMA (d=128: 2, d=64: 4)
 #pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        float p = exp2f_hw(__builtin_fmaf(s[kb][r], c, -mc));
-                        if (need_mask) p = (s[kb][r] == -INFINITY) ? 0.f : p;
-                        s[kb][r] = p;
-                        lsum += p;
+                for (int i = 0; i < NM; i++) {
+                    const int kk = i / C::NKB, kb = i % C::NKB;
+                    sn[kb] = mfma32(lds_read8(kl, 32 * kb * C::KS + 16 * kk), qf[kk], sn[kb]);
+#pragma unroll
+                    for (int e = 0; e < EPM; e++) {
+                        const int idx = i * EPM + e;           // 0 .. 16*NKB-1
+                        const int skb = idx / 16, r = idx % 16;
+                        const float p = exp2f_hw(__builtin_fmaf(sc[skb][r], c, -mc));
+                        sc[skb][r] = p;
+                        ls[idx & 3] += p;
                     }
-                l_part += lsum;
-                // ---- O^T += V^T P^T ----
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; kb++) {
-#pragma unroll
-                    for (int half = 0; half < 2; half++) {
-                        const bf16x8 pb = half ? pack8<8>(s[kb]) : pack8<0>(s[kb]);
-                        const int row0 = 32 * kb + 16 * half;
-#pragma unroll
-                        for (int dm = 0; dm < C::NDM; dm++) {
-                            const bf16x8 a = lds_read_tr_operand<D>(vt, row0, 32 * dm, lane);
-                            oacc[dm] = mfma32(a, pb, oacc[dm]);
-                        }
+                    if ((i * EPM + EPM) % 8 == 0) {
+                        const int t = (i * EPM + EPM) / 8 - 1;   // 8 probabilities complete
+                        pb[t] = (t & 1) ? pack8<8>(sc[t >> 1]) : pack8<0>(sc[t >> 1]);
                     }
                 }
+                l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
             }
-            if (it + 1 < tl.n) lstore(buf ^ 1);
+            // ---- phase B: O^T += V^T P^T for tile it; mask and max of tile it+1 ----
+            tile_pv<D>(v_this + v_lane, pb, oacc);
+            if (has_next) {
+                if (needs_mask(kv1)) mask_scores<D, CAUSAL>(sn, kv1, my_q, N, h);
+                mx_cur = tile_max<D>(sn);
+            }
+            wait_vmem();
             __syncthreads();
-        }
+        };
 
-        // ---- epilogue: one division per row, bf16 output, lse ----
+        int it = 0;
+        for (; it + 1 < tl.n; it += 2) {
+            step(std::integral_constant<int, 0>{}, it, sa, sb);
+            step(std::integral_constant<int, 1>{}, it + 1, sb, sa);
+        }
+        if (it < tl.n) step(std::integral_constant<int, 0>{}, it, sa, sb);
+
+        // ---- epilogue: one division per row, bf16 output, lse (buffer stores drop rows >= N) ----
         const float l = xhalf_sum(l_part);
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        if (my_q < N) {
-            bf16* dst = O + head_off + (size_t)my_q * D;
 #pragma unroll
-            for (int dm = 0; dm < C::NDM; dm++)
+        for (int dm = 0; dm < C::NDM; dm++)
 #pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    bf16x4 v4;
+            for (int g = 0; g < 4; g++) {
+                bf16x4 v4;
 #pragma unroll
-                    for (int e = 0; e < 4; e++) v4[e] = (bf16)(oacc[dm][4 * g + e] * inv);
-                    *reinterpret_cast<bf16x4*>(dst + 32 * dm + 8 * g + 4 * h) = v4;
-                }
-            if (h == 0)
-                LSE[(size_t)bh * N + my_q] = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
+                for (int e = 0; e < 4; e++) v4[e] = (bf16)(oacc[dm][4 * g + e] * inv);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), ro,
+                                                      (uint32_t)(my_q * D + 32 * dm + 8 * g + 4 * h) * 2, 0, 0);
+            }
+        if (h == 0) {
+            const float lse = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, (uint32_t)my_q * 4, 0, 0);
         }
     }
 }
@@ -279,9 +350,12 @@ hipError_t launch(const FwdArgs& a) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
+    // c = 0 (scale 0) would turn -inf * 0 into NaN; any c below 1e-30 gives the
+    // same fp32 probabilities (2^(s*c) == 1 for every finite score s).
+    const float c = a.c < 1e-30f ? 1e-30f : a.c;
     hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads), dyn, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.N,
-                       a.c, a.qsign, a.mask, a.nb, nqb, n_items);
+                       c, a.qsign, a.mask, a.nb, nqb, n_items);
     return hipGetLastError();
 }
 
