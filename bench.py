@@ -156,10 +156,10 @@ def main() -> int:
         if evs is not None:
             evs[1].record(stream)
         if w.backward:
-            fa.fa_bwd_prep(o, do, ws, stream)
+            fa.fa_bwd_prep(o, do, lse, ws, stream)
             if evs is not None:
                 evs[2].record(stream)
-            fa.fa_bwd_main(q, k, v, do, lse, dk, dv, w.scale, w.causal, mask, ws, stream)
+            fa.fa_bwd_main(q, k, v, do, dk, dv, w.scale, w.causal, mask, ws, stream)
             if evs is not None:
                 evs[3].record(stream)
             fa.fa_bwd_dq(dq, w.scale, ws, stream)

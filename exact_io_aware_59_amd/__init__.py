@@ -56,8 +56,8 @@ def load():
     lib.fa_fwd_f32.argtypes = lib.fa_fwd.argtypes
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.fa_bwd_f32.argtypes = lib.fa_bwd.argtypes
-    lib.fa_bwd_prep.argtypes = [vp, vp, i, i, i, i, vp, sz, vp]
-    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
+    lib.fa_bwd_prep.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.fa_bwd_dq.argtypes = [vp, i, i, i, i, f, vp, sz, vp]
     for name in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq",
                  "fa_version"):
@@ -154,16 +154,16 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size() if t is not None else 0
 
 
-def fa_bwd_prep(o, do, workspace, stream=None):
+def fa_bwd_prep(o, do, lse, workspace, stream=None):
     B, H, N, d = _dims(o)
-    _check(load().fa_bwd_prep(_ptr(o), _ptr(do), B, H, N, d, _ptr(workspace), _nbytes(workspace),
+    _check(load().fa_bwd_prep(_ptr(o), _ptr(do), _ptr(lse), B, H, N, d, _ptr(workspace), _nbytes(workspace),
                               _stream(stream)), "fa_bwd_prep")
 
 
-def fa_bwd_main(q, k, v, do, lse, dk, dv, scale: float, causal: bool = False, blockmask=None, workspace=None,
+def fa_bwd_main(q, k, v, do, dk, dv, scale: float, causal: bool = False, blockmask=None, workspace=None,
                 stream=None):
     B, H, N, d = _dims(q)
-    _check(load().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv), B, H, N, d,
+    _check(load().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv), B, H, N, d,
                               float(scale), int(bool(causal)), _ptr(blockmask), _ptr(workspace),
                               _nbytes(workspace), _stream(stream)), "fa_bwd_main")
 

@@ -10,6 +10,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxMaskN = 4194304;
+constexpr int kMaxMaskNBwd = 524288;  // the backward keeps its block-row list in LDS beside its tiles
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -68,10 +69,12 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
                void* stream, bool bf16, Stage stage) {
     const bool use_qkv = stage == kAll || stage == kMain;
     const bool use_o = stage == kAll || stage == kPrep;
+    const bool use_lse = stage != kDq;
     const bool use_do = stage != kDq;
     const bool use_dq = stage == kAll || stage == kDq;
     const bool use_dkdv = stage == kAll || stage == kMain;
-    if (use_qkv && (!q || !k || !v || !lse)) return FA_ERR_INVALID_ARG;
+    if (use_qkv && (!q || !k || !v)) return FA_ERR_INVALID_ARG;
+    if (use_lse && !lse) return FA_ERR_INVALID_ARG;
     if (use_o && !o) return FA_ERR_INVALID_ARG;
     if (use_do && !dO) return FA_ERR_INVALID_ARG;
     if (use_dq && !dq) return FA_ERR_INVALID_ARG;
@@ -83,6 +86,7 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     int st = check_sizes(B, H, N, d, scale, mask);
     if (st != FA_OK) return st;
+    if (mask && N > kMaxMaskNBwd) return FA_ERR_UNSUPPORTED;
     const size_t tb = (size_t)B * H * N * d * sizeof(T), lb = (size_t)B * H * N * sizeof(float);
     const void* ins[] = {q, k, v, o, dO};
     void* outs[] = {dq, dk, dv};
@@ -110,8 +114,10 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
     a.causal = causal;
     a.mask = mask;
     a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+    const size_t vec_bytes = align_up((size_t)B * H * N * sizeof(float));
     a.ws_D = (float*)ws;
-    a.ws_dq = (float*)((char*)ws + align_up((size_t)B * H * N * sizeof(float)));
+    a.ws_lse2 = (float*)((char*)ws + vec_bytes);
+    a.ws_dq = (float*)((char*)ws + 2 * vec_bytes);
     a.stream = (hipStream_t)stream;
     hipError_t e;
     if (!bf16) e = fa::launch_bwd_f32(a);
@@ -140,7 +146,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
     if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
     const size_t rows = (size_t)B * H * N;
-    return align_up(rows * sizeof(float)) + align_up(rows * (size_t)d * sizeof(float));
+    return 2 * align_up(rows * sizeof(float)) + align_up(rows * (size_t)d * sizeof(float));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
@@ -151,18 +157,18 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                                 scale, causal, blockmask, workspace, workspace_bytes, stream, true, kAll);
 }
 
-int fa_bwd_prep(const void* o, const void* dO, int B, int H, int N, int d, void* workspace, size_t workspace_bytes,
-                void* stream) {
-    return bwd_common<uint16_t>(nullptr, nullptr, nullptr, (const uint16_t*)o, (const uint16_t*)dO, nullptr,
+int fa_bwd_prep(const void* o, const void* dO, const float* lse, int B, int H, int N, int d, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    return bwd_common<uint16_t>(nullptr, nullptr, nullptr, (const uint16_t*)o, (const uint16_t*)dO, lse,
                                 nullptr, nullptr, nullptr, B, H, N, d, 1.0f, 0, nullptr, workspace, workspace_bytes,
                                 stream, true, kPrep);
 }
 
-int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dk, void* dv,
-                int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask, void* workspace,
-                size_t workspace_bytes, void* stream) {
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv, int B, int H, int N,
+                int d, float scale, int causal, const uint8_t* blockmask, void* workspace, size_t workspace_bytes,
+                void* stream) {
     return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, nullptr,
-                                (const uint16_t*)dO, lse, nullptr, (uint16_t*)dk, (uint16_t*)dv, B, H, N, d, scale,
+                                (const uint16_t*)dO, nullptr, nullptr, (uint16_t*)dk, (uint16_t*)dv, B, H, N, d, scale,
                                 causal, blockmask, workspace, workspace_bytes, stream, true, kMain);
 }
 

@@ -169,6 +169,33 @@ __device__ __forceinline__ bf16x8 lds_tr_operand_pad(const bf16* lane_base, int 
 // Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgVmem = 0x020;
 
+// The same HBM -> LDS copy issued as an opaque instruction: the compiler does
+// not track it, so it inserts no wait for it before unrelated LDS reads.  The
+// caller must wait (s_waitcnt vmcnt(0)) and synchronize the workgroup before
+// reading what it wrote.  `srd` is a gfx9 buffer descriptor, `lds_addr` the
+// wave-uniform LDS byte address of lane 0's 16 bytes.
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int32x4_t make_srd(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    return int32x4_t{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)bytes, kRsrcFlags};
+}
+
+__device__ __forceinline__ void dma16_untracked(int32x4_t srd, uint32_t lds_addr, uint32_t byte_off) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds_addr), "v"(byte_off), "s"(srd)
+        : "memory", "m0");
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr_of(const T* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
+}
+
 // Workgroup id -> logical work item such that consecutive logical items land
 // on the same XCD (the hardware deals workgroups round-robin over the 8 XCDs),
 // so tiles of one (batch, head) share that XCD's L2.

@@ -41,7 +41,8 @@
  *           synchronized.  Kernel faults surface at the caller's next sync.
  * Limits    B, H, N >= 1; d in {64, 128} (the pages allow any multiple of 16 up
  *           to 256; other values return FA_ERR_UNSUPPORTED); B*H*N*d < 2^31;
- *           scale finite; with a blockmask, N <= 4194304.
+ *           scale finite; with a blockmask, N <= 4194304 (forward) and
+ *           N <= 524288 (backward).
  * Errors    arguments are validated before anything is enqueued; on any
  *           error nothing is enqueued and the outputs are untouched.
  *           FA_ERR_HIP reports a failed kernel launch (hipGetLastError).
@@ -82,9 +83,10 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                int N, int d, float scale, int causal, const uint8_t* blockmask, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd and fa_bwd_f32 need: an fp32 row vector
- * D_i = sum_c dO_ic O_ic per (b, h, i) and an fp32 dQ accumulator
- * [B][H][N][d], each 256-byte aligned.  Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_bwd and fa_bwd_f32 need: two fp32 row vectors
+ * per (b, h, i) -- D_i = sum_c dO_ic O_ic and lse_i in log2 units -- and an
+ * fp32 dQ accumulator [B][H][N][d], each 256-byte aligned.  Returns 0 for
+ * invalid sizes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -108,19 +110,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * The three stages fa_bwd enqueues, for callers that want to schedule or time
  * them separately.  fa_bwd(...) is exactly fa_bwd_prep, fa_bwd_main and
  * fa_bwd_dq on the same stream with the same workspace.
- *   fa_bwd_prep: D_i = sum_c dO_ic O_ic into the workspace; clears the fp32 dQ
- *                accumulator.  Reads o, dO.
- *   fa_bwd_main: recomputes S and P per tile from q, k and lse; writes dk, dv
- *                (bf16) and adds scale-free dQ contributions into the
- *                accumulator.  Needs the workspace as left by fa_bwd_prep.
+ *   fa_bwd_prep: D_i = sum_c dO_ic O_ic and lse_i * log2(e) into the
+ *                workspace; clears the fp32 dQ accumulator.  Reads o, dO, lse.
+ *   fa_bwd_main: recomputes S and P per tile from q, k and the workspace's
+ *                lse; writes dk, dv (bf16) and adds scale-free dQ
+ *                contributions into the accumulator.  Needs the workspace as
+ *                left by fa_bwd_prep.
  *   fa_bwd_dq:   dq = scale * accumulator, rounded to bf16.
  * Validation and error codes as for fa_bwd.
  */
-int fa_bwd_prep(const void* o, const void* dO, int B, int H, int N, int d, void* workspace,
-                size_t workspace_bytes, void* stream);
-int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-                const uint8_t* blockmask, void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_prep(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
+                void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+                void* workspace, size_t workspace_bytes, void* stream);
 int fa_bwd_dq(void* dq, int B, int H, int N, int d, float scale, void* workspace,
               size_t workspace_bytes, void* stream);
 

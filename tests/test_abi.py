@@ -49,8 +49,8 @@ def test_version_and_status(lib):
 def test_workspace_size(lib):
     ws = fa.fa_bwd_workspace_size(2, 16, 4096, 128)
     rows = 2 * 16 * 4096
-    assert ws == rows * 4 + rows * 128 * 4  # both parts already 256-byte multiples
-    assert fa.fa_bwd_workspace_size(1, 1, 3, 64) == 256 + 768
+    assert ws == 2 * rows * 4 + rows * 128 * 4  # all parts already 256-byte multiples
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 64) == 2 * 256 + 768
     assert fa.fa_bwd_workspace_size(0, 1, 1, 64) == 0
 
 
@@ -116,12 +116,13 @@ def test_alignment_validation(lib):
 def test_stage_validation(lib):
     ws = P9 + 16 * BIG
     nbytes = lib.fa_bwd_workspace_size(1, 1, 128, 64)
-    assert lib.fa_bwd_prep(None, P2, 1, 1, 128, 64, ws, nbytes, None) == 1
-    assert lib.fa_bwd_prep(P1, P2, 1, 1, 128, 64, ws, nbytes - 1, None) == 3
-    assert lib.fa_bwd_prep(P1, P1 + BIG, 1, 1, 128, 96, ws, nbytes, None) == 2
+    assert lib.fa_bwd_prep(None, P2, P3, 1, 1, 128, 64, ws, nbytes, None) == 1
+    assert lib.fa_bwd_prep(P1, P1 + BIG, None, 1, 1, 128, 64, ws, nbytes, None) == 1
+    assert lib.fa_bwd_prep(P1, P1 + BIG, P1 + 2 * BIG, 1, 1, 128, 64, ws, nbytes - 1, None) == 3
+    assert lib.fa_bwd_prep(P1, P1 + BIG, P1 + 2 * BIG, 1, 1, 128, 96, ws, nbytes, None) == 2
     assert lib.fa_bwd_dq(None, 1, 1, 128, 64, ctypes.c_float(0.1), ws, nbytes, None) == 1
     assert lib.fa_bwd_dq(P1, 1, 1, 128, 64, ctypes.c_float(0.1), None, nbytes, None) == 3
-    assert lib.fa_bwd_main(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, None, P1 + 4 * BIG, P1 + 5 * BIG,
+    assert lib.fa_bwd_main(P1, P1 + BIG, None, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG,
                            1, 1, 128, 64, ctypes.c_float(0.1), 0, None, ws, nbytes, None) == 1
-    assert lib.fa_bwd_main(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 6 * BIG, P1 + 4 * BIG, P1 + 4 * BIG,
+    assert lib.fa_bwd_main(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 4 * BIG,
                            1, 1, 128, 64, ctypes.c_float(0.1), 0, None, ws, nbytes, None) == 1  # dk aliases dv
