@@ -162,7 +162,7 @@ def main() -> int:
             fa.fa_bwd_main(q, k, v, do, dk, dv, w.scale, w.causal, mask, ws, stream)
             if evs is not None:
                 evs[3].record(stream)
-            fa.fa_bwd_dq(dq, w.scale, ws, stream)
+            fa.fa_bwd_dq(q, k, v, do, dq, w.scale, w.causal, mask, ws, stream)
             if evs is not None:
                 evs[4].record(stream)
 

@@ -58,7 +58,7 @@ def load():
     lib.fa_bwd_f32.argtypes = lib.fa_bwd.argtypes
     lib.fa_bwd_prep.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
-    lib.fa_bwd_dq.argtypes = [vp, i, i, i, i, f, vp, sz, vp]
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
     for name in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq",
                  "fa_version"):
         getattr(lib, name).restype = i
@@ -168,9 +168,10 @@ def fa_bwd_main(q, k, v, do, dk, dv, scale: float, causal: bool = False, blockma
                               _nbytes(workspace), _stream(stream)), "fa_bwd_main")
 
 
-def fa_bwd_dq(dq, scale: float, workspace, stream=None):
-    B, H, N, d = _dims(dq)
-    _check(load().fa_bwd_dq(_ptr(dq), B, H, N, d, float(scale), _ptr(workspace), _nbytes(workspace),
+def fa_bwd_dq(q, k, v, do, dq, scale: float, causal: bool = False, blockmask=None, workspace=None, stream=None):
+    B, H, N, d = _dims(q)
+    _check(load().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), B, H, N, d, float(scale),
+                            int(bool(causal)), _ptr(blockmask), _ptr(workspace), _nbytes(workspace),
                             _stream(stream)), "fa_bwd_dq")
 
 

@@ -67,10 +67,10 @@ template <typename T>
 int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, const float* lse, T* dq, T* dk, T* dv,
                int B, int H, int N, int d, float scale, int causal, const uint8_t* mask, void* ws, size_t ws_bytes,
                void* stream, bool bf16, Stage stage) {
-    const bool use_qkv = stage == kAll || stage == kMain;
+    const bool use_qkv = stage != kPrep;
     const bool use_o = stage == kAll || stage == kPrep;
-    const bool use_lse = stage != kDq;
-    const bool use_do = stage != kDq;
+    const bool use_lse = stage == kAll || stage == kPrep;
+    const bool use_do = true;
     const bool use_dq = stage == kAll || stage == kDq;
     const bool use_dkdv = stage == kAll || stage == kMain;
     if (use_qkv && (!q || !k || !v)) return FA_ERR_INVALID_ARG;
@@ -117,7 +117,6 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
     const size_t vec_bytes = align_up((size_t)B * H * N * sizeof(float));
     a.ws_D = (float*)ws;
     a.ws_lse2 = (float*)((char*)ws + vec_bytes);
-    a.ws_dq = (float*)((char*)ws + 2 * vec_bytes);
     a.stream = (hipStream_t)stream;
     hipError_t e;
     if (!bf16) e = fa::launch_bwd_f32(a);
@@ -146,7 +145,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
     if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
     const size_t rows = (size_t)B * H * N;
-    return 2 * align_up(rows * sizeof(float)) + align_up(rows * (size_t)d * sizeof(float));
+    return 2 * align_up(rows * sizeof(float));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
@@ -172,10 +171,12 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, voi
                                 causal, blockmask, workspace, workspace_bytes, stream, true, kMain);
 }
 
-int fa_bwd_dq(void* dq, int B, int H, int N, int d, float scale, void* workspace, size_t workspace_bytes,
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void* dq, int B, int H, int N, int d,
+              float scale, int causal, const uint8_t* blockmask, void* workspace, size_t workspace_bytes,
               void* stream) {
-    return bwd_common<uint16_t>(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, (uint16_t*)dq, nullptr,
-                                nullptr, B, H, N, d, scale, 0, nullptr, workspace, workspace_bytes, stream, true, kDq);
+    return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, nullptr,
+                                (const uint16_t*)dO, nullptr, (uint16_t*)dq, nullptr, nullptr, B, H, N, d, scale,
+                                causal, blockmask, workspace, workspace_bytes, stream, true, kDq);
 }
 
 int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dO, const float* lse,

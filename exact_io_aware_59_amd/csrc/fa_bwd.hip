@@ -9,13 +9,17 @@
 // -- the five matrix products of "FlashAttention 深度解析" section 四.
 //
 // Three launches on one stream:
-//   1. rowdot:  D_i = rowsum(dO o O) in fp32, and clear the fp32 dQ accumulator;
-//   2. main:    one workgroup per (batch, head, block of 128 keys); its K and V
-//               rows stay in registers, dK and dV accumulate in registers; it
-//               sweeps the query tiles its mask allows (the K/V-outer order of
-//               the IO-Awareness page section 2.3) and adds each tile's dQ
-//               contribution into the fp32 accumulator with atomic adds;
-//   3. dq_out:  dQ = scale * accumulator, rounded to bf16.
+//   1. rowdot:  D_i = rowsum(dO o O) and lse_i * log2(e), fp32;
+//   2. main:    one workgroup per (batch, head, block of 128 keys); dK and dV
+//               accumulate in registers while it sweeps the query tiles its mask
+//               allows (the K/V-outer order of the IO-Awareness page section 2.3);
+//   3. dq:      one workgroup per (batch, head, block of 128 queries) sweeping
+//               the key tiles (Q-outer), recomputing S and dP and accumulating
+//               dQ = dS K in registers.
+// Splitting dQ off costs two extra tile products (S and dP are recomputed) but
+// replaces fp32 atomic accumulation of dQ, which measured slower than the
+// extra matrix work on this part; every output is deterministic ("FlashAttention
+// 深度解析" section 五 notes the deterministic backward as a trade-off).
 #include <type_traits>
 
 #include "fa_common.h"
@@ -30,13 +34,12 @@ constexpr int kBck = 128;  // keys per workgroup (32 per wave) = one mask block 
 constexpr int kBrq = 64;   // queries per step
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O); lse in log2 units; clear the dQ accumulator.
+// 1. D = rowsum(dO * O); lse in log2 units.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void rowdot_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
                                                      const float* __restrict__ LSE, float* __restrict__ Dv,
-                                                     float* __restrict__ lse2, float* __restrict__ dq_acc,
-                                                     long rows) {
+                                                     float* __restrict__ lse2, long rows) {
     constexpr int CPR = D / 8;  // 16-byte chunks per row
     const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const long row = gid / CPR;
@@ -48,9 +51,6 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const bf16* __restrict__ O,
         const bf16x8 x = __builtin_bit_cast(bf16x8, a), y = __builtin_bit_cast(bf16x8, b);
 #pragma unroll
         for (int i = 0; i < 8; i++) acc = __builtin_fmaf((float)x[i], (float)y[i], acc);
-        f32x4* z = reinterpret_cast<f32x4*>(dq_acc + row * D + ch * 8);
-        z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // reduce over the CPR lanes of the row (CPR divides 64, rows never straddle waves)
 #pragma unroll
@@ -61,24 +61,6 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const bf16* __restrict__ O,
         const float l = LSE[row];
         lse2[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
     }
-}
-
-// ---------------------------------------------------------------------------
-// 3. dQ = scale * accumulator -> bf16.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void dq_out_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
-                                                     float scale, long n8) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n8) return;
-    const f32x4 a = reinterpret_cast<const f32x4*>(acc)[2 * i];
-    const f32x4 b = reinterpret_cast<const f32x4*>(acc)[2 * i + 1];
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        r[e] = (bf16)(a[e] * scale);
-        r[4 + e] = (bf16)(b[e] * scale);
-    }
-    reinterpret_cast<bf16x8*>(dq)[i] = r;
 }
 
 // ---------------------------------------------------------------------------
@@ -94,7 +76,6 @@ struct BwdCfg {
     static constexpr int QSEGS = QTILE / 512;   // 1 KB DMA segments
     static constexpr int KTILE = kBck * QS;     // the workgroup's K rows
     static constexpr int KSEGS = KTILE / 512;
-    static constexpr int DSS = kBck + 8;        // dS tile: 64 rows (queries) x 128 keys, padded
     static_assert(QSEGS * 512 == QTILE && KSEGS * 512 == KTILE, "tiles must be whole 1 KB segments");
 };
 
@@ -119,24 +100,16 @@ __device__ __forceinline__ void dma_rows(int32x4_t srd, const bf16* tile, int r0
     }
 }
 
-// Position of key k (within the workgroup's 128) in a dS row: swaps the middle
-// two groups of four in every 16 keys, so that one 16-byte read returns keys in
-// the order a transposing read of the K tile produces (lds_tr_operand_pad).
-__device__ __forceinline__ int ds_pos(int k) {
-    return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
-}
-
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
-    float* __restrict__ dq_acc, bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float c,
-    float scale, const uint8_t* __restrict__ mask, int nb, int nkb, int BH) {
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float c, float scale,
+    const uint8_t* __restrict__ mask, int nb, int nkb, int BH) {
     using C = BwdCfg<D>;
     __shared__ __attribute__((aligned(1024))) bf16 qbuf[2][C::QTILE];
     __shared__ __attribute__((aligned(1024))) bf16 obuf[2][C::QTILE];
     __shared__ __attribute__((aligned(1024))) bf16 ktile[C::KTILE];
-    __shared__ __attribute__((aligned(16))) bf16 dsb[kBrq * C::DSS];
     __shared__ __attribute__((aligned(16))) float lvec[2][kBrq];
     __shared__ __attribute__((aligned(16))) float dvec[2][kBrq];
     __shared__ int wave_cnt[kWaves];
@@ -158,9 +131,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     const int32x4_t sdo = make_srd(dO + head_off, head_bytes);
     const int32x4_t sl = make_srd(LSE2 + (size_t)bh * N, (uint32_t)N * 4);
     const int32x4_t sdv = make_srd(Dv + (size_t)bh * N, (uint32_t)N * 4);
-    const rsrc_t racc = make_rsrc(dq_acc + head_off, (uint32_t)N * D * 4);
 
-    // ---- K rows of the block to LDS (S operand and dQ operand); this wave's V rows to registers ----
+    // ---- K rows of the block to LDS (S operand); this wave's V rows to registers ----
     dma_rows<D, C::KSEGS>(make_srd(K + head_off, head_bytes), ktile, k0, wave, lane);
     bf16x8 vf[C::NKK];
     {
@@ -169,12 +141,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
 #pragma unroll
         for (int kk = 0; kk < C::NKK; kk++) vf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off + 32 * kk));
     }
-    // dQ work split: d=128 -> wave owns dims 32w..32w+31 of both 32-query halves;
-    //                d=64  -> wave owns dim block w&1 of query half w>>1.
-    constexpr int DQ_QB = (D == 128) ? 2 : 1;
-    const int dq_db = (D == 128) ? wave : (wave & 1);
-    const int dq_qb0 = (D == 128) ? 0 : (wave >> 1);
-
     // ---- the query tiles to visit ----
     int nsteps, n_masked;
     int q_first = 0;
@@ -211,8 +177,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
 
     const int q_lane = l32 * C::QS + 8 * h;                 // b128 operand offset in a Q/dO/K tile
     const int tr_lane = lane_tr_offset<C::QS>(lane);        // transposing-read offset in a Q/dO/K tile
-    const int ds_lane = l32 * C::DSS + 8 * h;               // b128 operand offset in the dS tile
-    const int kcol = ds_pos(32 * wave + l32);               // this lane's key column in the dS tile
     const bf16* kf_base = ktile + 32 * wave * C::QS + q_lane;
 
     // One step over 64 queries.  MASKED adds the element mask (diagonal tiles, keys past N).
@@ -226,7 +190,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
         const int q0 = step_q0(st);
         if (st + 1 < nsteps) issue_loads(step_q0(st + 1), buf ^ 1);
 
-        bf16x8 dsp[4];  // dS of the four 16-query k-steps, bf16
 #pragma unroll
         for (int qb = 0; qb < 2; qb++) {
             // ---- S = Q K^T and dP = dO V^T for 32 queries (queries x keys) ----
@@ -259,42 +222,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
             for (int half = 0; half < 2; half++) {
                 const int t = 2 * qb + half;
                 const bf16x8 pb = half ? pack8<8>(s) : pack8<0>(s);
-                dsp[t] = half ? pack8<8>(dp) : pack8<0>(dp);
+                const bf16x8 sb = half ? pack8<8>(dp) : pack8<0>(dp);
 #pragma unroll
                 for (int dm = 0; dm < C::NDM; dm++) {
                     dvacc[dm] = mfma32(lds_tr_operand_pad<C::QS>(ot + tr_lane, 16 * t, 32 * dm), pb, dvacc[dm]);
-                    dkacc[dm] = mfma32(lds_tr_operand_pad<C::QS>(qt + tr_lane, 16 * t, 32 * dm), dsp[t], dkacc[dm]);
+                    dkacc[dm] = mfma32(lds_tr_operand_pad<C::QS>(qt + tr_lane, 16 * t, 32 * dm), sb, dkacc[dm]);
                 }
             }
         }
-        // ---- dS tile to LDS ([query][key], key-permuted), once every wave is done with the previous one ----
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < 4; t++)
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int row = 16 * t + 8 * (i >> 2) + 4 * h + (i & 3);
-                dsb[row * C::DSS + kcol] = dsp[t][i];
-            }
         wait_vmem();  // this wave's copies for the next step have landed
         __syncthreads();
-
-        // ---- dQ (queries x dims) += dS K over the 128 keys; fp32 atomics (rows >= N dropped) ----
-#pragma unroll
-        for (int qq = 0; qq < DQ_QB; qq++) {
-            const int qb = dq_qb0 + qq;
-            f32x16 acc = f32x16{};
-#pragma unroll
-            for (int t = 0; t < kBck / 16; t++)
-                acc = mfma32(lds_read8(dsb + ds_lane, 32 * qb * C::DSS + 16 * t),
-                             lds_tr_operand_pad<C::QS>(ktile + tr_lane, 16 * t, 32 * dq_db), acc);
-            const int dim = 32 * dq_db + l32;
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int qi = q0 + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
-                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], racc, (uint32_t)(qi * D + dim) * 4, 0, 0);
-            }
-        }
     };
 
     int st = 0;
@@ -320,6 +257,213 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
         }
 }
 
+// ---------------------------------------------------------------------------
+// 3. dQ kernel (query-outer): recompute S and dP per key tile, dQ += dS K.
+// One workgroup (4 waves x 32 queries) per 128-query block, like the forward:
+// the lane owns one query, so lse and D are per-lane scalars.  Deterministic.
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqCfg {
+    static constexpr int BC = 64;               // keys per tile
+    static constexpr int NKK = D / 16;
+    static constexpr int NDM = D / 32;
+    static constexpr int KS = D + 40;           // K tile: 16-row b128 reads and 4-row transposing reads
+    static constexpr int VS = PadK<D>::STRIDE;  // V tile: 16-row b128 reads only
+    static constexpr int KTILE = BC * KS;
+    static constexpr int VTILE = BC * VS;
+    static constexpr int KSEGS = KTILE / 512;
+    static constexpr int VSEGS = VTILE / 512;
+    static_assert(KSEGS * 512 == KTILE && VSEGS * 512 == VTILE, "tiles must be whole 1 KB segments");
+};
+constexpr int kDqBr = 128;  // queries per workgroup
+
+template <int D, int STRIDE, int SEGS>
+__device__ __forceinline__ void dq_load_tile(rsrc_t r, bf16* tile, int kv0, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < (SEGS + kWaves - 1) / kWaves; i++) {
+        const int s = i * kWaves + wave;
+        if (s < SEGS) {
+            const int el = s * 512 + lane * 8;
+            const int row = el / STRIDE;
+            int col = el - row * STRIDE;
+            col = col < D ? col : 0;
+            buf_load16_lds(r, tile + s * 512, ((uint32_t)(kv0 + row) * D + col) * 2);
+        }
+    }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
+    bf16* __restrict__ dQ, int N, float c, float scale, const uint8_t* __restrict__ mask, int nb, int nqb,
+    int n_items) {
+    using C = DqCfg<D>;
+    __shared__ __attribute__((aligned(1024))) bf16 kbuf0[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) bf16 kbuf1[C::KTILE];
+    __shared__ __attribute__((aligned(1024))) bf16 vbuf0[C::VTILE];
+    __shared__ __attribute__((aligned(1024))) bf16 vbuf1[C::VTILE];
+    __shared__ int wave_cnt[kWaves];
+    extern __shared__ uint16_t mask_cols[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int k_lane = l32 * C::KS + 8 * h;           // K rows as the A operand of S^T
+    const int v_lane = l32 * C::VS + 8 * h;           // V rows as the A operand of dP^T
+    const int kt_lane = lane_tr_offset<C::KS>(lane);  // K^T via transposing reads (A operand of dQ^T)
+
+    const int item = xcd_remap(blockIdx.x, n_items);
+    int bh, qblk[2], nblk;
+    if (CAUSAL) {
+        const int npair = (nqb + 1) / 2;
+        bh = item / npair;
+        const int p = item % npair;
+        qblk[0] = nqb - 1 - p;
+        qblk[1] = p;
+        nblk = (qblk[1] == qblk[0]) ? 1 : 2;
+    } else {
+        bh = item / nqb;
+        qblk[0] = item % nqb;
+        qblk[1] = -1;
+        nblk = 1;
+    }
+    const size_t head_off = (size_t)bh * N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const rsrc_t rq = make_rsrc(Q + head_off, head_bytes);
+    const rsrc_t rdo = make_rsrc(dO + head_off, head_bytes);
+    const rsrc_t rk = make_rsrc(K + head_off, head_bytes);
+    const rsrc_t rv = make_rsrc(V + head_off, head_bytes);
+    const rsrc_t rdq = make_rsrc(dQ + head_off, head_bytes);
+    const rsrc_t rl = make_rsrc(LSE2 + (size_t)bh * N, (uint32_t)N * 4);
+    const rsrc_t rd = make_rsrc(Dv + (size_t)bh * N, (uint32_t)N * 4);
+
+    for (int bi = 0; bi < nblk; bi++) {
+        const int qb = qblk[bi];
+        const int q0 = qb * kDqBr;
+        const int qw = q0 + wave * 32;
+        const int my_q = qw + l32;
+
+        int ntiles;
+        const uint16_t* cols = nullptr;
+        const int q_end = min(N, q0 + kDqBr);
+        if (MASK) {
+            const int max_col = CAUSAL ? (q_end - 1) / kMaskBlock : nb - 1;
+            const int cnt = build_block_list<kWaves>(mask + (size_t)qb * nb, 1, 0, max_col, mask_cols, wave_cnt);
+            cols = mask_cols;
+            ntiles = cnt * (kMaskBlock / C::BC);
+        } else {
+            ntiles = ((CAUSAL ? q_end : N) + C::BC - 1) / C::BC;
+        }
+        auto kv0_of = [&](int it) -> int {
+            if (MASK) return cols[it / (kMaskBlock / C::BC)] * kMaskBlock + (it % (kMaskBlock / C::BC)) * C::BC;
+            return it * C::BC;
+        };
+
+        // this lane's query: Q and dO fragments (B operands, k = head dim, n = query), lse2 and D
+        bf16x8 qf[C::NKK], of[C::NKK];
+        {
+            const uint32_t off = (uint32_t)(my_q * D + 8 * h) * 2;
+#pragma unroll
+            for (int kk = 0; kk < C::NKK; kk++) {
+                qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, off + 32 * kk));
+                of[kk] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off + 32 * kk));
+            }
+        }
+        const float l2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)my_q * 4, 0, 0));
+        const float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)my_q * 4, 0, 0));
+        const float ml2 = (my_q < N) ? -l2 : -INFINITY;  // rows past N get P = 0
+
+        f32x16 acc[C::NDM];
+#pragma unroll
+        for (int dm = 0; dm < C::NDM; dm++) acc[dm] = f32x16{};
+
+        if (ntiles > 0) {
+            dq_load_tile<D, C::KS, C::KSEGS>(rk, kbuf0, kv0_of(0), wave, lane);
+            dq_load_tile<D, C::VS, C::VSEGS>(rv, vbuf0, kv0_of(0), wave, lane);
+        }
+        wait_vmem();
+        __syncthreads();
+
+        auto step = [&](auto parity, int it) {
+            constexpr int P = decltype(parity)::value;
+            const bf16* kt = P ? kbuf1 : kbuf0;
+            const bf16* vt = P ? vbuf1 : vbuf0;
+            const int kv0 = kv0_of(it);
+            if (it + 1 < ntiles) {
+                dq_load_tile<D, C::KS, C::KSEGS>(rk, P ? kbuf0 : kbuf1, kv0_of(it + 1), wave, lane);
+                dq_load_tile<D, C::VS, C::VSEGS>(rv, P ? vbuf0 : vbuf1, kv0_of(it + 1), wave, lane);
+            }
+            const bool need_mask = (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N);
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+                // S^T and dP^T for 32 keys (keys x queries)
+                f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < C::NKK; kk++) {
+                    s = mfma32(lds_read8(kt + k_lane, 32 * kb * C::KS + 16 * kk), qf[kk], s);
+                    dp = mfma32(lds_read8(vt + v_lane, 32 * kb * C::VS + 16 * kk), of[kk], dp);
+                }
+                // P = 2^(c s - lse2), dS = P (dP - D)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    float p = exp2f_hw(__builtin_fmaf(s[r], c, ml2));
+                    if (need_mask) {
+                        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        p = ((CAUSAL && key > my_q) || key >= N) ? 0.f : p;
+                    }
+                    dp[r] = p * (dp[r] - dd);
+                }
+                // dQ^T += K^T dS^T
+#pragma unroll
+                for (int half = 0; half < 2; half++) {
+                    const bf16x8 sb = half ? pack8<8>(dp) : pack8<0>(dp);
+#pragma unroll
+                    for (int dm = 0; dm < C::NDM; dm++)
+                        acc[dm] = mfma32(lds_tr_operand_pad<C::KS>(kt + kt_lane, 32 * kb + 16 * half, 32 * dm), sb, acc[dm]);
+                }
+            }
+            wait_vmem();
+            __syncthreads();
+        };
+        int it = 0;
+        for (; it + 1 < ntiles; it += 2) {
+            step(std::integral_constant<int, 0>{}, it);
+            step(std::integral_constant<int, 1>{}, it + 1);
+        }
+        if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
+
+        // dQ = scale * acc -> bf16 (rows >= N dropped)
+#pragma unroll
+        for (int dm = 0; dm < C::NDM; dm++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                bf16x4 v4;
+#pragma unroll
+                for (int e = 0; e < 4; e++) v4[e] = (bf16)(acc[dm][4 * g + e] * scale);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), rdq,
+                                                      (uint32_t)(my_q * D + 32 * dm + 8 * g + 4 * h) * 2, 0, 0);
+            }
+    }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+hipError_t launch_dq(const BwdArgs& a) {
+    const int nqb = (a.N + kDqBr - 1) / kDqBr;
+    const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
+    const int n_items = a.BH * per_head;
+    const size_t dyn = MASK ? (size_t)a.nb * sizeof(uint16_t) : 0;
+    auto kern = bwd_dq_kernel<D, CAUSAL, MASK>;
+    if (dyn > 0) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads), dyn, a.stream, (const bf16*)a.q, (const bf16*)a.k,
+                       (const bf16*)a.v, (const bf16*)a.dO, a.ws_lse2, a.ws_D, (bf16*)a.dq, a.N,
+                       a.scale * kLog2e, a.scale, a.mask, a.nb, nqb, n_items);
+    return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, bool MASK>
 hipError_t launch_main(const BwdArgs& a) {
     const int nkb = (a.N + kBck - 1) / kBck;
@@ -331,7 +475,7 @@ hipError_t launch_main(const BwdArgs& a) {
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads), dyn, a.stream, (const bf16*)a.q, (const bf16*)a.k,
-                       (const bf16*)a.v, (const bf16*)a.dO, a.ws_lse2, a.ws_D, a.ws_dq, (bf16*)a.dk, (bf16*)a.dv,
+                       (const bf16*)a.v, (const bf16*)a.dO, a.ws_lse2, a.ws_D, (bf16*)a.dk, (bf16*)a.dv,
                        a.N, a.scale * kLog2e, a.scale, a.mask, a.nb, nkb, a.BH);
     return hipGetLastError();
 }
@@ -341,7 +485,7 @@ hipError_t launch_prep(const BwdArgs& a) {
     const long rows = (long)a.BH * a.N;
     const long nthr = rows * (D / 8);
     hipLaunchKernelGGL(rowdot_kernel<D>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, a.stream,
-                       (const bf16*)a.o, (const bf16*)a.dO, a.lse, a.ws_D, a.ws_lse2, a.ws_dq, rows);
+                       (const bf16*)a.o, (const bf16*)a.dO, a.lse, a.ws_D, a.ws_lse2, rows);
     return hipGetLastError();
 }
 
@@ -363,10 +507,13 @@ hipError_t launch_bwd_main_bf16(const BwdArgs& a) {
 }
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
-    const long n8 = (long)a.BH * a.N * a.d / 8;
-    hipLaunchKernelGGL(dq_out_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, a.stream, a.ws_dq,
-                       (bf16*)a.dq, a.scale, n8);
-    return hipGetLastError();
+    const bool m = a.mask != nullptr;
+    if (a.d == 128) {
+        if (a.causal) return m ? launch_dq<128, true, true>(a) : launch_dq<128, true, false>(a);
+        return m ? launch_dq<128, false, true>(a) : launch_dq<128, false, false>(a);
+    }
+    if (a.causal) return m ? launch_dq<64, true, true>(a) : launch_dq<64, true, false>(a);
+    return m ? launch_dq<64, false, true>(a) : launch_dq<64, false, false>(a);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a) {

@@ -42,7 +42,6 @@ struct BwdArgs {
     int nb;
     float* ws_D;      // [BH*N] fp32: D_i = rowsum(dO o O)
     float* ws_lse2;   // [BH*N] fp32: lse in log2 units (+inf for rows without keys)
-    float* ws_dq;     // [BH*N*d] fp32 dQ accumulator
     hipStream_t stream;
 };
 

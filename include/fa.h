@@ -84,9 +84,9 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 
 /*
  * Bytes of device workspace fa_bwd and fa_bwd_f32 need: two fp32 row vectors
- * per (b, h, i) -- D_i = sum_c dO_ic O_ic and lse_i in log2 units -- and an
- * fp32 dQ accumulator [B][H][N][d], each 256-byte aligned.  Returns 0 for
- * invalid sizes.
+ * per (b, h, i) -- D_i = sum_c dO_ic O_ic and lse_i in log2 units -- each
+ * 256-byte aligned (O(N) memory, nothing O(N^2) and no O(N d) accumulator).
+ * Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -96,10 +96,10 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * Outputs: dq, dk, dv bf16 [B][H][N][d] (written, rounded to bf16).  The
  * scores and probabilities are recomputed from q, k and lse; nothing N x N is
  * stored.  workspace: device buffer of at least fa_bwd_workspace_size() bytes,
- * 256-byte aligned, contents ignored on entry and clobbered.  dQ is summed in
- * fp32 with atomic adds, so dq may differ between runs in the last bits;
- * dk and dv are deterministic.  scale, causal and blockmask must be the ones
- * the forward used.
+ * 256-byte aligned, contents ignored on entry and clobbered.  Every gradient is
+ * accumulated in fp32 registers by exactly one workgroup (no atomics), so the
+ * results are bitwise deterministic.  scale, causal and blockmask must be the
+ * ones the forward used.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
@@ -111,12 +111,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * them separately.  fa_bwd(...) is exactly fa_bwd_prep, fa_bwd_main and
  * fa_bwd_dq on the same stream with the same workspace.
  *   fa_bwd_prep: D_i = sum_c dO_ic O_ic and lse_i * log2(e) into the
- *                workspace; clears the fp32 dQ accumulator.  Reads o, dO, lse.
- *   fa_bwd_main: recomputes S and P per tile from q, k and the workspace's
- *                lse; writes dk, dv (bf16) and adds scale-free dQ
- *                contributions into the accumulator.  Needs the workspace as
- *                left by fa_bwd_prep.
- *   fa_bwd_dq:   dq = scale * accumulator, rounded to bf16.
+ *                workspace.  Reads o, dO, lse.
+ *   fa_bwd_main: key-outer pass: recomputes S, P, dP and dS per tile from q, k,
+ *                v, dO and the workspace; writes dk and dv (bf16).
+ *   fa_bwd_dq:   query-outer pass: recomputes S, P, dP and dS per tile; writes
+ *                dq (bf16).  Independent of fa_bwd_main (both need only the
+ *                workspace as left by fa_bwd_prep).
  * Validation and error codes as for fa_bwd.
  */
 int fa_bwd_prep(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
@@ -124,7 +124,8 @@ int fa_bwd_prep(const void* o, const void* dO, const float* lse, int B, int H, i
 int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
                 int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
                 void* workspace, size_t workspace_bytes, void* stream);
-int fa_bwd_dq(void* dq, int B, int H, int N, int d, float scale, void* workspace,
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void* dq, int B, int H,
+              int N, int d, float scale, int causal, const uint8_t* blockmask, void* workspace,
               size_t workspace_bytes, void* stream);
 
 /* Backward, float32 tensors; same semantics as fa_bwd (deterministic). */

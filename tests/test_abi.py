@@ -49,8 +49,8 @@ def test_version_and_status(lib):
 def test_workspace_size(lib):
     ws = fa.fa_bwd_workspace_size(2, 16, 4096, 128)
     rows = 2 * 16 * 4096
-    assert ws == 2 * rows * 4 + rows * 128 * 4  # all parts already 256-byte multiples
-    assert fa.fa_bwd_workspace_size(1, 1, 3, 64) == 2 * 256 + 768
+    assert ws == 2 * rows * 4  # both row vectors already 256-byte multiples
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 64) == 2 * 256
     assert fa.fa_bwd_workspace_size(0, 1, 1, 64) == 0
 
 
@@ -120,8 +120,12 @@ def test_stage_validation(lib):
     assert lib.fa_bwd_prep(P1, P1 + BIG, None, 1, 1, 128, 64, ws, nbytes, None) == 1
     assert lib.fa_bwd_prep(P1, P1 + BIG, P1 + 2 * BIG, 1, 1, 128, 64, ws, nbytes - 1, None) == 3
     assert lib.fa_bwd_prep(P1, P1 + BIG, P1 + 2 * BIG, 1, 1, 128, 96, ws, nbytes, None) == 2
-    assert lib.fa_bwd_dq(None, 1, 1, 128, 64, ctypes.c_float(0.1), ws, nbytes, None) == 1
-    assert lib.fa_bwd_dq(P1, 1, 1, 128, 64, ctypes.c_float(0.1), None, nbytes, None) == 3
+    assert lib.fa_bwd_dq(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, None, 1, 1, 128, 64, ctypes.c_float(0.1), 0,
+                         None, ws, nbytes, None) == 1
+    assert lib.fa_bwd_dq(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, 1, 1, 128, 64,
+                         ctypes.c_float(0.1), 0, None, None, nbytes, None) == 3
+    assert lib.fa_bwd_dq(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1, 1, 1, 128, 64,
+                         ctypes.c_float(0.1), 0, None, ws, nbytes, None) == 1  # dq aliases q
     assert lib.fa_bwd_main(P1, P1 + BIG, None, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG,
                            1, 1, 128, 64, ctypes.c_float(0.1), 0, None, ws, nbytes, None) == 1
     assert lib.fa_bwd_main(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 4 * BIG,

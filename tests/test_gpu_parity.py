@@ -154,6 +154,37 @@ def test_fwd_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_bwd_deterministic():
+    """dQ, dK and dV are each summed by exactly one workgroup: bitwise reproducible."""
+    say("[bwd determinism] B=1 H=4 N=1024 d=128 causal")
+    x = W.make_inputs(1, 4, 1024, 128, "bf16", seed=43, with_do=True)
+    q, k, v, do = (to_device(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, None, True)
+    g1 = fa.backward(q, k, v, o, do, lse, None, True)
+    g2 = fa.backward(q, k, v, o, do, lse, None, True)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_bwd_stages_equal_monolithic():
+    """fa_bwd_prep + fa_bwd_main + fa_bwd_dq reproduce fa_bwd exactly."""
+    say("[bwd stages] B=2 H=2 N=640 d=64 causal")
+    B, H, N, d = 2, 2, 640, 64
+    x = W.make_inputs(B, H, N, d, "bf16", seed=44, with_do=True)
+    q, k, v, do = (to_device(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    s = 0.125
+    o, lse = fa.forward(q, k, v, s, True)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, s, True)
+    ws = fa.workspace(B, H, N, d, q.device)
+    dq2, dk2, dv2 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa.fa_bwd_prep(o, do, lse, ws)
+    fa.fa_bwd_main(q, k, v, do, dk2, dv2, s, True, None, ws)
+    fa.fa_bwd_dq(q, k, v, do, dq2, s, True, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
 def test_empty_rows_exact():
     """Rows whose block-mask row is all zero: O = 0 exactly and lse = -inf."""
     say("[empty rows] N=384 d=64")
