@@ -3,15 +3,16 @@
 
 One step is the whole hot path over one batch of synthetic inputs:
 fa_fwd (fused forward, writes O and lse) followed by the backward's three
-stages fa_bwd_prep, fa_bwd_main and fa_bwd_dq (exactly what fa_bwd enqueues).
+stages fa_bwd_prep, fa_bwd_main (key-outer: dK, dV) and fa_bwd_dq
+(query-outer: dQ) -- exactly what fa_bwd enqueues.
 Workload: B=2, H=16, N=4096, d=128, bf16, causal, iid N(0,1) inputs (seed 0).
 
 Prints one JSON line.  `value` is the whole step's throughput in TFLOP/s with
 the FLOP convention 4*B*H*N^2*d for the forward (halved for causal) and 2.5x
 that for the backward; inputs are resident in HBM before timing starts.
 HIP events on the launch stream time every kernel call of every timed step;
-`roofline` reports the backward's main kernel (the dominant one) against the
-bf16 dense matrix-core peak.  `cpu_baseline` times the fp64 oracle on a
+`roofline` reports the backward's key-outer kernel (the dominant one: four of
+the five products) against the bf16 dense matrix-core peak.  `cpu_baseline` times the fp64 oracle on a
 bounded sample of the same workload (a few heads).
 
 Options: --steps K --warmup W (timed / untimed steps), --gpus N (only 1 is
@@ -210,7 +211,8 @@ def main() -> int:
             "bwd_main_ms": round(res["bwd_main_ms"], 4),
             "bwd_dq_ms": round(res["bwd_dq_ms"], 4),
         })
-        dom_name, dom_ms, dom_flops = "bwd_bf16_kernel (fa_bwd_main)", res["bwd_main_ms"], flops["bwd"]
+        # fa_bwd_main computes four of the backward's five products (S, dP, dV, dK): 4/5 of its FLOPs
+        dom_name, dom_ms, dom_flops = "bwd_bf16_kernel (fa_bwd_main)", res["bwd_main_ms"], flops["bwd"] * 4 / 5
     else:
         dom_name, dom_ms, dom_flops = "fwd_bf16_kernel (fa_fwd)", res["fwd_ms"], flops["fwd"]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
