@@ -81,22 +81,40 @@ struct BwdCfg {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// HBM -> LDS copy of `rows` rows (r0 ..) of a [N][D] tensor into a padded tile
-// (row stride QS); untracked, see dma16_untracked.
+// HBM -> LDS copy of rows r0 .. of a [N][D] tensor into a padded tile (row
+// stride QS); untracked, see dma16_untracked.  The tile is cut into 1 KB
+// segments dealt round-robin to the waves; `lane_off[i]` is this lane's byte
+// offset of segment i relative to row r0 (precomputed once, dma_lane_offsets).
 template <int D, int SEGS>
-__device__ __forceinline__ void dma_rows(int32x4_t srd, const bf16* tile, int r0, int wave, int lane) {
+struct DmaPlan {
+    static constexpr int PER_WAVE = (SEGS + kWaves - 1) / kWaves;
+    uint32_t lane_off[PER_WAVE];
+};
+
+template <int D, int SEGS>
+__device__ __forceinline__ DmaPlan<D, SEGS> dma_plan(int wave, int lane) {
     using C = BwdCfg<D>;
-    const uint32_t base = lds_addr_of(tile);
+    DmaPlan<D, SEGS> p;
 #pragma unroll
-    for (int i = 0; i < (SEGS + kWaves - 1) / kWaves; i++) {
+    for (int i = 0; i < DmaPlan<D, SEGS>::PER_WAVE; i++) {
+        const int el = (i * kWaves + wave) * 512 + lane * 8;
+        const int row = el / C::QS;
+        int col = el - row * C::QS;
+        col = col < D ? col : 0;  // padding slot: harmless re-read of the row's first chunk
+        p.lane_off[i] = (uint32_t)(row * D + col) * 2;
+    }
+    return p;
+}
+
+template <int D, int SEGS>
+__device__ __forceinline__ void dma_rows(int32x4_t srd, const bf16* tile, int r0, const DmaPlan<D, SEGS>& p,
+                                         int wave) {
+    const uint32_t base = lds_addr_of(tile);
+    const uint32_t row_bytes = (uint32_t)r0 * D * 2;
+#pragma unroll
+    for (int i = 0; i < DmaPlan<D, SEGS>::PER_WAVE; i++) {
         const int s = i * kWaves + wave;
-        if (s < SEGS) {
-            const int el = s * 512 + lane * 8;
-            const int row = el / C::QS;
-            int col = el - row * C::QS;
-            col = col < D ? col : 0;  // padding slot: harmless re-read of the row's first chunk
-            dma16_untracked(srd, base + s * 1024, ((uint32_t)(r0 + row) * D + col) * 2);
-        }
+        if (s < SEGS) dma16_untracked(srd, base + s * 1024, row_bytes + p.lane_off[i]);
     }
 }
 
@@ -133,7 +151,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     const int32x4_t sdv = make_srd(Dv + (size_t)bh * N, (uint32_t)N * 4);
 
     // ---- K rows of the block to LDS (S operand); this wave's V rows to registers ----
-    dma_rows<D, C::KSEGS>(make_srd(K + head_off, head_bytes), ktile, k0, wave, lane);
+    dma_rows<D, C::KSEGS>(make_srd(K + head_off, head_bytes), ktile, k0, dma_plan<D, C::KSEGS>(wave, lane), wave);
     bf16x8 vf[C::NKK];
     {
         const rsrc_t rv = make_rsrc(V + head_off, head_bytes);
@@ -164,9 +182,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
 #pragma unroll
     for (int dm = 0; dm < C::NDM; dm++) dvacc[dm] = dkacc[dm] = f32x16{};
 
+    const DmaPlan<D, C::QSEGS> qplan = dma_plan<D, C::QSEGS>(wave, lane);
     auto issue_loads = [&](int q0, int buf) {
-        dma_rows<D, C::QSEGS>(sq, qbuf[buf], q0, wave, lane);
-        dma_rows<D, C::QSEGS>(sdo, obuf[buf], q0, wave, lane);
+        dma_rows<D, C::QSEGS>(sq, qbuf[buf], q0, qplan, wave);
+        dma_rows<D, C::QSEGS>(sdo, obuf[buf], q0, qplan, wave);
         if (wave == 0 && lane < 16) dma16_untracked(sl, lds_addr_of(lvec[buf]), (uint32_t)(q0 + 4 * lane) * 4);
         if (wave == 1 && lane < 16) dma16_untracked(sdv, lds_addr_of(dvec[buf]), (uint32_t)(q0 + 4 * lane) * 4);
     };
@@ -190,16 +209,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
         const int q0 = step_q0(st);
         if (st + 1 < nsteps) issue_loads(step_q0(st + 1), buf ^ 1);
 
-#pragma unroll
-        for (int qb = 0; qb < 2; qb++) {
-            // ---- S = Q K^T and dP = dO V^T for 32 queries (queries x keys) ----
-            f32x16 s = f32x16{}, dp = f32x16{};
+        // Two 32-query halves, software-pipelined: the matrix cores compute
+        // S/dP of half 1 while the vector ALUs turn half 0 into P/dS, and the
+        // dV/dK products of half 0 run while half 1's P/dS are computed.
+        f32x16 s[2], dp[2];
+        auto scores = [&](int qb) {
+            s[qb] = f32x16{};
+            dp[qb] = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < C::NKK; kk++) {
-                s = mfma32(lds_read8(qt + q_lane, 32 * qb * C::QS + 16 * kk), lds_read8(kf_base, 16 * kk), s);
-                dp = mfma32(lds_read8(ot + q_lane, 32 * qb * C::QS + 16 * kk), vf[kk], dp);
+                s[qb] = mfma32(lds_read8(qt + q_lane, 32 * qb * C::QS + 16 * kk), lds_read8(kf_base, 16 * kk), s[qb]);
+                dp[qb] = mfma32(lds_read8(ot + q_lane, 32 * qb * C::QS + 16 * kk), vf[kk], dp[qb]);
             }
-            // ---- P = 2^(c s - lse2), dS = P (dP - D) ----
+        };
+        bf16x8 pb[2][2], sb[2][2];
+        auto probs = [&](int qb) {  // P = 2^(c s - lse2), dS = P (dP - D), packed to bf16
 #pragma unroll
             for (int a = 0; a < 4; a++) {
                 const int rbase = 32 * qb + 8 * a + 4 * h;
@@ -208,28 +232,49 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
 #pragma unroll
                 for (int b = 0; b < 4; b++) {
                     const int r = 4 * a + b;
-                    float p = exp2f_hw(__builtin_fmaf(s[r], c, -l4[b]));
+                    float p = exp2f_hw(__builtin_fmaf(s[qb][r], c, -l4[b]));
                     if (MASKED) {
                         const int qi = q0 + rbase + b;
                         p = ((CAUSAL && my_key > qi) || my_key >= N) ? 0.f : p;
                     }
-                    s[r] = p;
-                    dp[r] = p * (dp[r] - d4[b]);
+                    s[qb][r] = p;
+                    dp[qb][r] = p * (dp[qb][r] - d4[b]);
                 }
             }
-            // ---- dV^T += dO^T P, dK^T += Q^T dS (dims x keys) ----
+            pb[qb][0] = pack8<0>(s[qb]);
+            pb[qb][1] = pack8<8>(s[qb]);
+            sb[qb][0] = pack8<0>(dp[qb]);
+            sb[qb][1] = pack8<8>(dp[qb]);
+        };
+        auto grads = [&](int qb) {  // dV^T += dO^T P, dK^T += Q^T dS (dims x keys)
 #pragma unroll
             for (int half = 0; half < 2; half++) {
                 const int t = 2 * qb + half;
-                const bf16x8 pb = half ? pack8<8>(s) : pack8<0>(s);
-                const bf16x8 sb = half ? pack8<8>(dp) : pack8<0>(dp);
 #pragma unroll
                 for (int dm = 0; dm < C::NDM; dm++) {
-                    dvacc[dm] = mfma32(lds_tr_operand_pad<C::QS>(ot + tr_lane, 16 * t, 32 * dm), pb, dvacc[dm]);
-                    dkacc[dm] = mfma32(lds_tr_operand_pad<C::QS>(qt + tr_lane, 16 * t, 32 * dm), sb, dkacc[dm]);
+                    dvacc[dm] = mfma32(lds_tr_operand_pad<C::QS>(ot + tr_lane, 16 * t, 32 * dm), pb[qb][half], dvacc[dm]);
+                    dkacc[dm] = mfma32(lds_tr_operand_pad<C::QS>(qt + tr_lane, 16 * t, 32 * dm), sb[qb][half], dkacc[dm]);
                 }
             }
+        };
+        scores(0);
+        scores(1);
+        probs(0);
+#pragma unroll
+        for (int i = 0; i < 2 * C::NKK; i++) {
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
         }
+        grads(0);
+        probs(1);
+#pragma unroll
+        for (int i = 0; i < 4 * C::NDM; i++) {
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
+        }
+        grads(1);
         wait_vmem();  // this wave's copies for the next step have landed
         __syncthreads();
     };
@@ -395,34 +440,45 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                 dq_load_tile<D, C::VS, C::VSEGS>(rv, P ? vbuf0 : vbuf1, kv0_of(it + 1), wave, lane);
             }
             const bool need_mask = (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N);
-#pragma unroll
-            for (int kb = 0; kb < 2; kb++) {
-                // S^T and dP^T for 32 keys (keys x queries)
-                f32x16 s = f32x16{}, dp = f32x16{};
+            // two 32-key halves, software-pipelined as in the key-outer kernel
+            f32x16 s[2], dp[2];
+            auto scores = [&](int kb) {  // S^T and dP^T for 32 keys (keys x queries)
+                s[kb] = f32x16{};
+                dp[kb] = f32x16{};
 #pragma unroll
                 for (int kk = 0; kk < C::NKK; kk++) {
-                    s = mfma32(lds_read8(kt + k_lane, 32 * kb * C::KS + 16 * kk), qf[kk], s);
-                    dp = mfma32(lds_read8(vt + v_lane, 32 * kb * C::VS + 16 * kk), of[kk], dp);
+                    s[kb] = mfma32(lds_read8(kt + k_lane, 32 * kb * C::KS + 16 * kk), qf[kk], s[kb]);
+                    dp[kb] = mfma32(lds_read8(vt + v_lane, 32 * kb * C::VS + 16 * kk), of[kk], dp[kb]);
                 }
-                // P = 2^(c s - lse2), dS = P (dP - D)
+            };
+            bf16x8 sb[2][2];
+            auto probs = [&](int kb) {  // P = 2^(c s - lse2), dS = P (dP - D)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    float p = exp2f_hw(__builtin_fmaf(s[r], c, ml2));
+                    float p = exp2f_hw(__builtin_fmaf(s[kb][r], c, ml2));
                     if (need_mask) {
                         const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
                         p = ((CAUSAL && key > my_q) || key >= N) ? 0.f : p;
                     }
-                    dp[r] = p * (dp[r] - dd);
+                    dp[kb][r] = p * (dp[kb][r] - dd);
                 }
-                // dQ^T += K^T dS^T
+                sb[kb][0] = pack8<0>(dp[kb]);
+                sb[kb][1] = pack8<8>(dp[kb]);
+            };
+            auto grads = [&](int kb) {  // dQ^T += K^T dS^T
 #pragma unroll
-                for (int half = 0; half < 2; half++) {
-                    const bf16x8 sb = half ? pack8<8>(dp) : pack8<0>(dp);
+                for (int half = 0; half < 2; half++)
 #pragma unroll
                     for (int dm = 0; dm < C::NDM; dm++)
-                        acc[dm] = mfma32(lds_tr_operand_pad<C::KS>(kt + kt_lane, 32 * kb + 16 * half, 32 * dm), sb, acc[dm]);
-                }
-            }
+                        acc[dm] = mfma32(lds_tr_operand_pad<C::KS>(kt + kt_lane, 32 * kb + 16 * half, 32 * dm),
+                                         sb[kb][half], acc[dm]);
+            };
+            scores(0);
+            scores(1);
+            probs(0);
+            grads(0);
+            probs(1);
+            grads(1);
             wait_vmem();
             __syncthreads();
         };
