@@ -70,53 +70,43 @@ template <int D>
 struct BwdCfg {
     static constexpr int NKK = D / 16;          // k-steps over the head dimension
     static constexpr int NDM = D / 32;          // 32-dim blocks
-    static constexpr int QS = D + 40;           // Q / dO / K tile row stride: 16-row b128 reads conflict-free,
-                                                // 4-row transposing reads at most 2-way
-    static constexpr int QTILE = kBrq * QS;     // elements of one Q (or dO) tile
+    static constexpr int RB = 2 * D;            // bytes per tile row (no padding: rows are swizzled)
+    static constexpr int QTILE = kBrq * D;      // elements of one Q (or dO) tile
     static constexpr int QSEGS = QTILE / 512;   // 1 KB DMA segments
-    static constexpr int KTILE = kBck * QS;     // the workgroup's K rows
-    static constexpr int KSEGS = KTILE / 512;
-    static_assert(QSEGS * 512 == QTILE && KSEGS * 512 == KTILE, "tiles must be whole 1 KB segments");
+    static constexpr int SEG_PER_WAVE = QSEGS / kWaves;
+    static_assert(SEG_PER_WAVE * kWaves * 512 == QTILE, "a tile must split into whole segments per wave");
+    // copies one wave issues per tile: its Q and dO segments, then one 256-byte
+    // row of lse2 (waves 0, 2) or D (waves 1, 3)
+    static constexpr int NDMA = 2 * SEG_PER_WAVE + 1;
+    // matrix products of one 32-query half step, in issue order:
+    //   NA = S and dP of the NEXT half (alternating), then NC for dV, NC for dK
+    static constexpr int NA = 2 * NKK;
+    static constexpr int NC = 2 * NDM;
+    static constexpr int NSLOT = NA + 2 * NC;
+    static constexpr int PD = 2;  // slots between an LDS operand read and its product
 };
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// HBM -> LDS copy of rows r0 .. of a [N][D] tensor into a padded tile (row
-// stride QS); untracked, see dma16_untracked.  The tile is cut into 1 KB
-// segments dealt round-robin to the waves; `lane_off[i]` is this lane's byte
-// offset of segment i relative to row r0 (precomputed once, dma_lane_offsets).
-template <int D, int SEGS>
-struct DmaPlan {
-    static constexpr int PER_WAVE = (SEGS + kWaves - 1) / kWaves;
-    uint32_t lane_off[PER_WAVE];
-};
-
-template <int D, int SEGS>
-__device__ __forceinline__ DmaPlan<D, SEGS> dma_plan(int wave, int lane) {
-    using C = BwdCfg<D>;
-    DmaPlan<D, SEGS> p;
-#pragma unroll
-    for (int i = 0; i < DmaPlan<D, SEGS>::PER_WAVE; i++) {
-        const int el = (i * kWaves + wave) * 512 + lane * 8;
-        const int row = el / C::QS;
-        int col = el - row * C::QS;
-        col = col < D ? col : 0;  // padding slot: harmless re-read of the row's first chunk
-        p.lane_off[i] = (uint32_t)(row * D + col) * 2;
-    }
-    return p;
+__device__ __forceinline__ bf16x8 lds_read8_b(const void* base, uint32_t byte_off) {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+__device__ __forceinline__ bf16x8 lds_tr_pair_b(const void* base, uint32_t lo_off, uint32_t hi_off) {
+    const bf16* b = reinterpret_cast<const bf16*>(base);
+    const bf16x4 lo = lds_read_tr4(b, lo_off / 2);
+    const bf16x4 hi = lds_read_tr4(b, hi_off / 2);
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
 }
 
-template <int D, int SEGS>
-__device__ __forceinline__ void dma_rows(int32x4_t srd, const bf16* tile, int r0, const DmaPlan<D, SEGS>& p,
-                                         int wave) {
-    const uint32_t base = lds_addr_of(tile);
-    const uint32_t row_bytes = (uint32_t)r0 * D * 2;
-#pragma unroll
-    for (int i = 0; i < DmaPlan<D, SEGS>::PER_WAVE; i++) {
-        const int s = i * kWaves + wave;
-        if (s < SEGS) dma16_untracked(srd, base + s * 1024, row_bytes + p.lane_off[i]);
-    }
-}
+// S and R chains (zero start / accumulate).  The builtin lets the compiler
+// see the matrix instructions and insert the hazard waits they need.
+__device__ __forceinline__ void mfma32_zero(f32x16& d, bf16x8 a, bf16x8 b) { d = mfma32(a, b, f32x16{}); }
+__device__ __forceinline__ void mfma32_acc(f32x16& d, bf16x8 a, bf16x8 b) { d = mfma32(a, b, d); }
+
+// Items [first(j), first(j+1)) of E items spread evenly over S slots.
+template <int E, int S>
+constexpr int slot_first(int j) { return (j * E + S - 1) / S; }
 
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
@@ -125,11 +115,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float c, float scale,
     const uint8_t* __restrict__ mask, int nb, int nkb, int BH) {
     using C = BwdCfg<D>;
-    __shared__ __attribute__((aligned(1024))) bf16 qbuf[2][C::QTILE];
-    __shared__ __attribute__((aligned(1024))) bf16 obuf[2][C::QTILE];
-    __shared__ __attribute__((aligned(1024))) bf16 ktile[C::KTILE];
-    __shared__ __attribute__((aligned(16))) float lvec[2][kBrq];
-    __shared__ __attribute__((aligned(16))) float dvec[2][kBrq];
+    // three-deep ring of query tiles (Q then dO): tile t+2 streams in while t and
+    // t+1 are read.  Rows are unpadded; 16-byte chunk c of row r sits at chunk
+    // position c ^ swz_sigma(r), which keeps both the 16-row operand reads and
+    // the 4-row transposing reads free of bank conflicts.
+    __shared__ __attribute__((aligned(1024))) bf16 ring[3][2][C::QTILE];
+    __shared__ __attribute__((aligned(256))) float lvec[3][kBrq];
+    __shared__ __attribute__((aligned(256))) float dvec[3][kBrq];
     __shared__ int wave_cnt[kWaves];
     extern __shared__ uint16_t rows_list[];
 
@@ -147,17 +139,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     const uint32_t head_bytes = (uint32_t)N * D * 2;
     const int32x4_t sq = make_srd(Q + head_off, head_bytes);
     const int32x4_t sdo = make_srd(dO + head_off, head_bytes);
-    const int32x4_t sl = make_srd(LSE2 + (size_t)bh * N, (uint32_t)N * 4);
-    const int32x4_t sdv = make_srd(Dv + (size_t)bh * N, (uint32_t)N * 4);
+    // waves 0 and 2 copy lse2 rows, waves 1 and 3 the D rows (the second copy is
+    // a duplicate of identical bytes, which keeps the issue free of branches)
+    const int32x4_t svec = (wave & 1) ? make_srd(Dv + (size_t)bh * N, (uint32_t)N * 4)
+                                      : make_srd(LSE2 + (size_t)bh * N, (uint32_t)N * 4);
+    const uint32_t vec_lds0 = (wave & 1) ? lds_addr_of(&dvec[0][0]) : lds_addr_of(&lvec[0][0]);
 
-    // ---- K rows of the block to LDS (S operand); this wave's V rows to registers ----
-    dma_rows<D, C::KSEGS>(make_srd(K + head_off, head_bytes), ktile, k0, dma_plan<D, C::KSEGS>(wave, lane), wave);
-    bf16x8 vf[C::NKK];
+    // ---- this wave's K and V rows as MFMA B operands (k = head dim, n = key) ----
+    bf16x8 kf[C::NKK], vneg[C::NKK];
     {
+        const rsrc_t rk = make_rsrc(K + head_off, head_bytes);
         const rsrc_t rv = make_rsrc(V + head_off, head_bytes);
         const uint32_t off = (uint32_t)(my_key * D + 8 * h) * 2;
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; kk++) vf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off + 32 * kk));
+        for (int kk = 0; kk < C::NKK; kk++) {
+            kf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, off + 32 * kk));
+            // -V (exact: a sign flip), so the R chain yields D - dP
+            vneg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off + 32 * kk) ^ 0x80008000u);
+        }
     }
     // ---- the query tiles to visit ----
     int nsteps, n_masked;
@@ -173,117 +172,239 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
         nsteps = (N - q_first + kBrq - 1) / kBrq;
         n_masked = key_tail ? nsteps : (CAUSAL ? min(nsteps, kBck / kBrq) : 0);
     }
+    // first query of step st; steps past the end map to row N, whose copies
+    // fall outside the buffers and fetch nothing
     auto step_q0 = [&](int st) -> int {
+        if (st >= nsteps) return N;
         if (MASK) return rows_list[st / (kMaskBlock / kBrq)] * kMaskBlock + (st % (kMaskBlock / kBrq)) * kBrq;
         return q_first + st * kBrq;
     };
+
+    // Per-lane byte offsets of this wave's DMA segments relative to the tile's
+    // first row.  Segments are dealt round-robin to the waves; lane i of a
+    // segment fills LDS chunk position i, i.e. logical chunk i ^ sigma(row).
+    uint32_t seg_off[C::SEG_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < C::SEG_PER_WAVE; i++) {
+        constexpr int CPR = D / 8;  // chunks per row
+        const int seg = i * kWaves + wave;
+        const int row = seg * (512 / D) + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz_sigma<D>(row & 15);
+        seg_off[i] = (uint32_t)(row * D + 8 * chunk) * 2;
+    }
+    // copy k (0 .. NDMA-1) of the tile starting at query q0 into ring slot `buf`
+    auto dma_op = [&](auto kc, int q0, int buf) {
+        constexpr int k = decltype(kc)::value;
+        const uint32_t rb = (uint32_t)q0 * D * 2;
+        if constexpr (k < 2 * C::SEG_PER_WAVE) {
+            constexpr int i = k % C::SEG_PER_WAVE;
+            constexpr int tensor = k / C::SEG_PER_WAVE;
+            const uint32_t dst = lds_addr_of(ring[buf][tensor]) + (i * kWaves + wave) * 1024;
+            dma16_untracked(tensor == 0 ? sq : sdo, dst, rb + seg_off[i]);
+        } else {
+            dma4_untracked(svec, vec_lds0 + buf * (kBrq * 4), (uint32_t)(q0 + lane) * 4);
+        }
+    };
+    auto dma_tile = [&](int q0, int buf) { static_for<C::NDMA>([&](auto k) { dma_op(k, q0, buf); }); };
 
     f32x16 dvacc[C::NDM], dkacc[C::NDM];
 #pragma unroll
     for (int dm = 0; dm < C::NDM; dm++) dvacc[dm] = dkacc[dm] = f32x16{};
 
-    const DmaPlan<D, C::QSEGS> qplan = dma_plan<D, C::QSEGS>(wave, lane);
-    auto issue_loads = [&](int q0, int buf) {
-        dma_rows<D, C::QSEGS>(sq, qbuf[buf], q0, qplan, wave);
-        dma_rows<D, C::QSEGS>(sdo, obuf[buf], q0, qplan, wave);
-        if (wave == 0 && lane < 16) dma16_untracked(sl, lds_addr_of(lvec[buf]), (uint32_t)(q0 + 4 * lane) * 4);
-        if (wave == 1 && lane < 16) dma16_untracked(sdv, lds_addr_of(dvec[buf]), (uint32_t)(q0 + 4 * lane) * 4);
+    // Operand byte offsets inside a swizzled tile (loop invariant, per lane):
+    //   a_off[kk]: row l32, logical chunk 2kk + h (B128 read of the S / dP A operand);
+    //   tr_lo/hi[dm]: rows 4h + j and 4h + j + 8, columns 32dm + 16g + 4q (the two
+    //   transposing reads of a dV / dK A operand, see lds_tr_operand_pad).
+    uint32_t a_off[C::NKK], tr_lo[C::NDM], tr_hi[C::NDM];
+    {
+        const int sig = swz_sigma<D>(l32 & 15);
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; kk++) a_off[kk] = l32 * C::RB + (((2 * kk + h) ^ sig) << 4);
+        const int sl = lane & 15, j = sl >> 2, q = sl & 3, g = (lane >> 4) & 1;
+        const int r = 4 * h + j;
+        const int slo = swz_sigma<D>(r), shi = swz_sigma<D>(r + 8);
+#pragma unroll
+        for (int dm = 0; dm < C::NDM; dm++) {
+            const int cc = 4 * dm + 2 * g + (q >> 1);
+            tr_lo[dm] = r * C::RB + ((cc ^ slo) << 4) + (q & 1) * 8;
+            tr_hi[dm] = (r + 8) * C::RB + ((cc ^ shi) << 4) + (q & 1) * 8;
+        }
+    }
+
+    // One 32-query half step g, as a fixed schedule of NSLOT matrix products.
+    // Slot j issues the LDS operand read of slot j + PD, its own product and the
+    // vector work assigned to it; a scheduling fence closes every slot, so the
+    // products stay evenly interleaved with the vector work and the copies.
+    //   products: S of half g+1 (NKK, chain from zero), then R = D - dP of half
+    //             g+1 (NKK, chain from that half's D rows; V is held negated),
+    //             then dV += dO^T P (NC) and dK += Q^T dS' (NC) of half g;
+    //   vector:   during the S / R products dS' = P R of half g (= -dS, the
+    //             sign is restored in the dK epilogue); during the dV / dK
+    //             products P = 2^(c s - lse2) of half g+1, whose S is ready.
+    struct HalfRegs {
+        f32x16 s;   // S, then P (fp32) in place
+        f32x16 r;   // R = D - dP, then dS' in place
+        u32x4 pb[2];  // P as bf16 pairs, B operands of dV
+    };
+    HalfRegs X, Y;
+    u32x4 sb[2];      // dS' as bf16 pairs, B operands of dK
+    // `ta` / `tc`: ring slots of the A-phase and C-phase tiles, `ha` / `hc` the
+    // 32-query halves inside them; lv_next / dv_next the lse2 / D rows and qn
+    // the first query of half g+1.
+    // `carry`: the first PD operands of a step's first half step, read at the
+    // end of the previous step (its tile was published by that step's
+    // barrier), so that half step does not start on an LDS round trip.  The
+    // second half step follows the barrier and reads its own.
+    bf16x8 carry[C::PD];
+    auto half_step = [&](auto masked, auto with_dma, HalfRegs& cur, HalfRegs& nxt,
+                         const bf16 (*ta)[C::QTILE], int ha, const bf16 (*tc)[C::QTILE], int hc,
+                         const bf16 (*tn)[C::QTILE], int hn,
+                         const float* lv_next, const float* dv_next, int qn, int dma_q0, int dma_buf) {
+        constexpr bool MASKED = decltype(masked)::value;
+        constexpr bool DMA = decltype(with_dma)::value;
+        bf16x8 opnd[C::NSLOT];
+        f32x4 lvn[4], dvn[4];
+        auto read_operand = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr (j < C::NA) {
+                opnd[j] = lds_read8_b(ta[j < C::NKK ? 0 : 1], a_off[j % C::NKK] + ha * 32 * C::RB);
+            } else if constexpr (j < C::NA + C::NC) {
+                constexpr int cc = j - C::NA;
+                const uint32_t rows = (hc * 32 + 16 * (cc / C::NDM)) * C::RB;
+                opnd[j] = lds_tr_pair_b(tc[1], tr_lo[cc % C::NDM] + rows, tr_hi[cc % C::NDM] + rows);
+            } else {
+                constexpr int cc = j - C::NA - C::NC;
+                const uint32_t rows = (hc * 32 + 16 * (cc / C::NDM)) * C::RB;
+                opnd[j] = lds_tr_pair_b(tc[0], tr_lo[cc % C::NDM] + rows, tr_hi[cc % C::NDM] + rows);
+            }
+        };
+        // P of half g+1, element r (row 8(r/4) + 4h + r%4 of the half)
+        auto probs = [&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            float p = exp2f_hw(__builtin_fmaf(nxt.s[r], c, -lvn[r / 4][r % 4]));
+            if constexpr (MASKED) {
+                const int qi = qn + 8 * (r / 4) + 4 * h + (r % 4);
+                p = ((CAUSAL && my_key > qi) || my_key >= N) ? 0.f : p;
+            }
+            nxt.s[r] = p;
+            if constexpr (r % 2 == 1) nxt.pb[r / 8][(r % 8) / 2] = cvt_pk_bf16(nxt.s[r - 1], p);
+        };
+        // the half step with the copies is the one after the barrier
+        if constexpr (DMA) static_for<C::PD>([&](auto jc) { read_operand(jc); });
+        else static_for<C::PD>([&](auto jc) { opnd[decltype(jc)::value] = carry[decltype(jc)::value]; });
+        static_for<C::NSLOT>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr (j + C::PD < C::NSLOT) read_operand(std::integral_constant<int, j + C::PD>{});
+            else if constexpr (DMA)
+                carry[j + C::PD - C::NSLOT] = lds_read8_b(tn[0], a_off[j + C::PD - C::NSLOT] + hn * 32 * C::RB);
+            if constexpr (j < C::NA) {
+                // ---- S / R of half g+1; dS' of half g; lse2 / D rows of half g+1 ----
+                if constexpr (j == 0) {
+                    mfma32_zero(nxt.s, opnd[j], kf[0]);
+                } else if constexpr (j < C::NKK) {
+                    mfma32_acc(nxt.s, opnd[j], kf[j]);
+                } else if constexpr (j == C::NKK) {
+                    nxt.r = f32x16{dvn[0][0], dvn[0][1], dvn[0][2], dvn[0][3], dvn[1][0], dvn[1][1], dvn[1][2],
+                                   dvn[1][3], dvn[2][0], dvn[2][1], dvn[2][2], dvn[2][3], dvn[3][0], dvn[3][1],
+                                   dvn[3][2], dvn[3][3]};
+                    mfma32_acc(nxt.r, opnd[j], vneg[0]);
+                } else {
+                    mfma32_acc(nxt.r, opnd[j], vneg[j - C::NKK]);
+                }
+                if constexpr (j < 4) dvn[j] = *reinterpret_cast<const f32x4*>(dv_next + 8 * j + 4 * h);
+                else if constexpr (j < 8) lvn[j - 4] = *reinterpret_cast<const f32x4*>(lv_next + 8 * (j - 4) + 4 * h);
+                static_for<slot_first<16, C::NA>(j + 1) - slot_first<16, C::NA>(j)>([&](auto ic) {
+                    constexpr int r = slot_first<16, C::NA>(j) + decltype(ic)::value;
+                    const float ds = cur.s[r] * cur.r[r];
+                    cur.r[r] = ds;
+                    if constexpr (r % 2 == 1) sb[r / 8][(r % 8) / 2] = cvt_pk_bf16(cur.r[r - 1], ds);
+                });
+            } else {
+                constexpr int cc = j - C::NA;  // 0 .. 2 NC - 1
+                if constexpr (cc < C::NC) {
+                    // ---- dV += dO^T P of half g ----
+                    dvacc[cc % C::NDM] =
+                        mfma32(opnd[j], __builtin_bit_cast(bf16x8, cur.pb[cc / C::NDM]), dvacc[cc % C::NDM]);
+                } else {
+                    // ---- dK' += Q^T dS' of half g ----
+                    constexpr int ck = cc - C::NC;
+                    dkacc[ck % C::NDM] =
+                        mfma32(opnd[j], __builtin_bit_cast(bf16x8, sb[ck / C::NDM]), dkacc[ck % C::NDM]);
+                }
+                // ---- P of half g+1 ----
+                static_for<slot_first<16, 2 * C::NC>(cc + 1) - slot_first<16, 2 * C::NC>(cc)>([&](auto ic) {
+                    probs(std::integral_constant<int, slot_first<16, 2 * C::NC>(cc) + decltype(ic)::value>{});
+                });
+            }
+            if constexpr (DMA) {
+                static_for<slot_first<C::NDMA, C::NSLOT>(j + 1) - slot_first<C::NDMA, C::NSLOT>(j)>([&](auto kc) {
+                    dma_op(std::integral_constant<int, slot_first<C::NDMA, C::NSLOT>(j) + decltype(kc)::value>{},
+                           dma_q0, dma_buf);
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
     };
 
-    if (nsteps > 0) issue_loads(step_q0(0), 0);
+    // ---- prologue: tile 0 resident, tile 1 in flight; S, R and P of tile 0's first half ----
+    dma_tile(step_q0(0), 0);
     wait_vmem();
     __syncthreads();
+    dma_tile(step_q0(1), 1);
+    {
+        f32x4 l4[4], d4[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            l4[e] = *reinterpret_cast<const f32x4*>(&lvec[0][8 * e + 4 * h]);
+            d4[e] = *reinterpret_cast<const f32x4*>(&dvec[0][8 * e + 4 * h]);
+        }
+        mfma32_zero(X.s, lds_read8_b(ring[0][0], a_off[0]), kf[0]);
+#pragma unroll
+        for (int kk = 1; kk < C::NKK; kk++) mfma32_acc(X.s, lds_read8_b(ring[0][0], a_off[kk]), kf[kk]);
+        X.r = f32x16{d4[0][0], d4[0][1], d4[0][2], d4[0][3], d4[1][0], d4[1][1], d4[1][2], d4[1][3],
+                     d4[2][0], d4[2][1], d4[2][2], d4[2][3], d4[3][0], d4[3][1], d4[3][2], d4[3][3]};
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; kk++) mfma32_acc(X.r, lds_read8_b(ring[0][1], a_off[kk]), vneg[kk]);
+        const int q0 = step_q0(0);
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            float p = exp2f_hw(__builtin_fmaf(X.s[r], c, -l4[r / 4][r % 4]));
+            const int qi = q0 + 8 * (r / 4) + 4 * h + (r % 4);
+            p = ((CAUSAL && my_key > qi) || my_key >= N) ? 0.f : p;
+            X.s[r] = p;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) X.pb[i / 4][i % 4] = cvt_pk_bf16(X.s[2 * i], X.s[2 * i + 1]);
+#pragma unroll
+        for (int j = 0; j < C::PD; j++) carry[j] = lds_read8_b(ring[0][0], a_off[j] + 32 * C::RB);
+    }
 
-    const int q_lane = l32 * C::QS + 8 * h;                 // b128 operand offset in a Q/dO/K tile
-    const int tr_lane = lane_tr_offset<C::QS>(lane);        // transposing-read offset in a Q/dO/K tile
-    const bf16* kf_base = ktile + 32 * wave * C::QS + q_lane;
-
-    // One step over 64 queries.  MASKED adds the element mask (diagonal tiles, keys past N).
+    // Step st uses ring slot st % 3.  Its first half step computes S / R of
+    // its own second half; its second half step, after the barrier that
+    // publishes tile st+1, computes S / R / P of tile st+1's first half and
+    // streams tile st+2 into the slot that tile st-1 occupied (every wave
+    // finished it before that barrier).  Past the last tile the next-half work
+    // runs on stale LDS contents and is discarded.
+    int cur = 0;
     auto step = [&](auto masked, int st) {
-        constexpr bool MASKED = decltype(masked)::value;
-        const int buf = st & 1;
-        const bf16* qt = qbuf[buf];
-        const bf16* ot = obuf[buf];
-        const float* lv = lvec[buf];
-        const float* dvv = dvec[buf];
+        const int nxt = cur == 2 ? 0 : cur + 1;
+        const int nn = nxt == 2 ? 0 : nxt + 1;
         const int q0 = step_q0(st);
-        if (st + 1 < nsteps) issue_loads(step_q0(st + 1), buf ^ 1);
-
-        // Two 32-query halves, software-pipelined: the matrix cores compute
-        // S/dP of half 1 while the vector ALUs turn half 0 into P/dS, and the
-        // dV/dK products of half 0 run while half 1's P/dS are computed.
-        f32x16 s[2], dp[2];
-        auto scores = [&](int qb) {
-            s[qb] = f32x16{};
-            dp[qb] = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < C::NKK; kk++) {
-                s[qb] = mfma32(lds_read8(qt + q_lane, 32 * qb * C::QS + 16 * kk), lds_read8(kf_base, 16 * kk), s[qb]);
-                dp[qb] = mfma32(lds_read8(ot + q_lane, 32 * qb * C::QS + 16 * kk), vf[kk], dp[qb]);
-            }
-        };
-        bf16x8 pb[2][2], sb[2][2];
-        auto probs = [&](int qb) {  // P = 2^(c s - lse2), dS = P (dP - D), packed to bf16
-#pragma unroll
-            for (int a = 0; a < 4; a++) {
-                const int rbase = 32 * qb + 8 * a + 4 * h;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lv + rbase);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dvv + rbase);
-#pragma unroll
-                for (int b = 0; b < 4; b++) {
-                    const int r = 4 * a + b;
-                    float p = exp2f_hw(__builtin_fmaf(s[qb][r], c, -l4[b]));
-                    if (MASKED) {
-                        const int qi = q0 + rbase + b;
-                        p = ((CAUSAL && my_key > qi) || my_key >= N) ? 0.f : p;
-                    }
-                    s[qb][r] = p;
-                    dp[qb][r] = p * (dp[qb][r] - d4[b]);
-                }
-            }
-            pb[qb][0] = pack8<0>(s[qb]);
-            pb[qb][1] = pack8<8>(s[qb]);
-            sb[qb][0] = pack8<0>(dp[qb]);
-            sb[qb][1] = pack8<8>(dp[qb]);
-        };
-        auto grads = [&](int qb) {  // dV^T += dO^T P, dK^T += Q^T dS (dims x keys)
-#pragma unroll
-            for (int half = 0; half < 2; half++) {
-                const int t = 2 * qb + half;
-#pragma unroll
-                for (int dm = 0; dm < C::NDM; dm++) {
-                    dvacc[dm] = mfma32(lds_tr_operand_pad<C::QS>(ot + tr_lane, 16 * t, 32 * dm), pb[qb][half], dvacc[dm]);
-                    dkacc[dm] = mfma32(lds_tr_operand_pad<C::QS>(qt + tr_lane, 16 * t, 32 * dm), sb[qb][half], dkacc[dm]);
-                }
-            }
-        };
-        scores(0);
-        scores(1);
-        probs(0);
-#pragma unroll
-        for (int i = 0; i < 2 * C::NKK; i++) {
-            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
-        }
-        grads(0);
-        probs(1);
-#pragma unroll
-        for (int i = 0; i < 4 * C::NDM; i++) {
-            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
-        }
-        grads(1);
-        wait_vmem();  // this wave's copies for the next step have landed
+        half_step(masked, std::false_type{}, X, Y, ring[cur], 1, ring[cur], 0, ring[nxt], 0, &lvec[cur][32],
+                  &dvec[cur][32], q0 + 32, 0, 0);
+        wait_vmem();  // this wave's copies of tile st+1 have landed
         __syncthreads();
+        half_step(masked, std::true_type{}, Y, X, ring[nxt], 0, ring[cur], 1, ring[nxt], 1, &lvec[nxt][0],
+                  &dvec[nxt][0], step_q0(st + 1), step_q0(st + 2), nn);
+        cur = nxt;
     };
 
     int st = 0;
     for (; st < n_masked; st++) step(std::true_type{}, st);
     for (; st < nsteps; st++) step(std::false_type{}, st);
+    wait_vmem();  // copies past the last tile fetch nothing, but must retire before exit
 
-    // ---- epilogue: dK = scale * acc, dV = acc, bf16 (rows >= N dropped) ----
+    // ---- epilogue: dK = -scale * acc, dV = acc, bf16 (rows >= N dropped) ----
     const rsrc_t rdk = make_rsrc(dK + head_off, head_bytes);
     const rsrc_t rdv = make_rsrc(dV + head_off, head_bytes);
 #pragma unroll
@@ -293,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
             bf16x4 a, b;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                a[e] = (bf16)(dkacc[dm][4 * g + e] * scale);
+                a[e] = (bf16)(dkacc[dm][4 * g + e] * -scale);  // the accumulator holds -dK / scale
                 b[e] = (bf16)dvacc[dm][4 * g + e];
             }
             const uint32_t off = (uint32_t)(my_key * D + 32 * dm + 8 * g + 4 * h) * 2;

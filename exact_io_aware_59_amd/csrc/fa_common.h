@@ -16,6 +16,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
 
 typedef __bf16 bf16;
@@ -48,6 +51,24 @@ __device__ __forceinline__ float xhalf_max(float x) {
 __device__ __forceinline__ float xhalf_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two floats to a packed pair of bf16 (RNE, one v_cvt_pk_bf16_f32); `lo` is
+// the element with the lower index.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Pack registers [base, base+8) of an accumulator into MFMA bf16 operands (RNE).
@@ -190,6 +211,26 @@ __device__ __forceinline__ void dma16_untracked(int32x4_t srd, uint32_t lds_addr
         : "s"(lds_addr), "v"(byte_off), "s"(srd)
         : "memory", "m0");
 }
+
+// Four bytes per lane: lane i writes lds_addr + 4*i (one 256-byte row of a
+// 64-entry fp32 vector per instruction).
+__device__ __forceinline__ void dma4_untracked(int32x4_t srd, uint32_t lds_addr, uint32_t byte_off) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %1, %2, 0 offen lds"
+        :
+        : "s"(lds_addr), "v"(byte_off), "s"(srd)
+        : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(0) through the builtin, so the compiler's wait tracking sees
+// it.  An inline-asm wait is invisible to that tracking: loads issued before it
+// (fragments kept in registers) would still count as outstanding, and the
+// compiler would add waits of its own at their first use -- inside a loop, where
+// the hardware counter also holds the next tile's untracked copies, such a wait
+// stalls until those copies land.  Encoding: vmcnt 0, expcnt 7, lgkmcnt 15.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <typename T>
 __device__ __forceinline__ uint32_t lds_addr_of(const T* p) {

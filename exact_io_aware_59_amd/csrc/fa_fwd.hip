@@ -90,7 +90,6 @@ __device__ __forceinline__ void load_tile(rsrc_t r, bf16* tile, int kv0, int wav
     }
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Scores of keys past the causal diagonal or past N become -inf.
 template <int D, bool CAUSAL>
