@@ -24,6 +24,7 @@ profiler's traffic calibration).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -55,6 +56,24 @@ def host_cpu_model() -> str:
     except OSError:
         pass
     return platform.processor() or "unknown"
+
+
+def measured_traffic(workload: str, kernel_api: str):
+    """HBM bytes per launch of `kernel_api` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or
+    None when that summary is for another workload or the kernel sources have
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        src = b"".join(open(os.path.join(ROOT, "exact_io_aware_59_amd", "csrc", n), "rb").read()
+                       for n in t["sources"])
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("workload") != workload or hashlib.sha256(src).hexdigest() != t.get("kernel_source_sha256"):
+        return None
+    return t["per_launch"].get(kernel_api)
 
 
 def cpu_baseline(w, x, mask_np, heads: int) -> dict:
@@ -213,8 +232,11 @@ def main() -> int:
         })
         # fa_bwd_main computes four of the backward's five products (S, dP, dV, dK): 4/5 of its FLOPs
         dom_name, dom_ms, dom_flops = "bwd_bf16_kernel (fa_bwd_main)", res["bwd_main_ms"], flops["bwd"] * 4 / 5
+        dom_api = "fa_bwd_main"
     else:
         dom_name, dom_ms, dom_flops = "fwd_bf16_kernel (fa_fwd)", res["fwd_ms"], flops["fwd"]
+        dom_api = "fa_fwd"
+    tr = measured_traffic(w.name, dom_api)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     roofline = {
         "bound": "mfma",
@@ -222,7 +244,9 @@ def main() -> int:
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
+        "traffic": None if tr is None else tr["traffic_bytes"],
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+        "traffic_vs_algorithmic": None if tr is None else round(tr["traffic_bytes"] / tr["algorithmic_bytes"], 3),
         "kernel": dom_name,
         "kernel_ms": round(dom_ms, 4),
     }
