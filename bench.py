@@ -58,6 +58,19 @@ def host_cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def kernel_source_digest(names) -> str:
+    """sha256 of the kernel sources with // comments and blank lines removed
+    (a comment edit does not change the counted kernels)."""
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_io_aware_59_amd", "csrc", n)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
 def measured_traffic(workload: str, kernel_api: str):
     """HBM bytes per launch of `kernel_api` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or
@@ -67,11 +80,10 @@ def measured_traffic(workload: str, kernel_api: str):
     try:
         with open(path) as f:
             t = json.load(f)
-        src = b"".join(open(os.path.join(ROOT, "exact_io_aware_59_amd", "csrc", n), "rb").read()
-                       for n in t["sources"])
+        src = kernel_source_digest(t["sources"])
     except (OSError, KeyError, ValueError):
         return None
-    if t.get("workload") != workload or hashlib.sha256(src).hexdigest() != t.get("kernel_source_sha256"):
+    if t.get("workload") != workload or src != t.get("kernel_source_sha256"):
         return None
     return t["per_launch"].get(kernel_api)
 

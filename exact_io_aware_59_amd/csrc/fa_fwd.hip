@@ -17,8 +17,9 @@
 //    O^T = V^T P^T; V is read transposed straight from its row-major LDS tile
 //    with ds_read_tr16_b64, in the accumulator's key order.
 //  * K and V tiles travel HBM -> LDS with buffer_load ... lds (no register
-//    staging); the XOR swizzle of the LDS tile is applied by choosing each
-//    lane's source address.  Rows past N read as zero (buffer range check).
+//    staging) into padded rows: K rows D+8 elements apart (16-row operand
+//    reads hit distinct banks), V rows D+32 apart (4-row transposing reads
+//    hit distinct banks).  Rows past N read as zero (buffer range check).
 //  * K runs one tile ahead of V: while the exponentials of tile j are being
 //    computed on the vector ALUs, the matrix cores already compute S for tile
 //    j+1; the P V products of tile j then overlap the row max of tile j+1
