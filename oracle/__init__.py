@@ -7,8 +7,11 @@ imports nothing from it.
 
 The arithmetic lives in ``ref_attn.c`` (plain C, OpenMP over rows, no BLAS);
 this file only compiles it with gcc and marshals numpy arrays.  All functions
-take and return float64 arrays of shape [B, H, N, d] (lse: [B, H, N]) and an
-optional uint8 block mask [nb, nb], nb = ceil(N / 128).
+take and return float64 arrays of shape [B, H, N, d] (lse: [B, H, N]), an
+optional uint8 block mask [nb, nb], nb = ceil(N / 128), and optionally a local
+window ``window=(wl, wr)`` (key j allowed for query i iff i - wl <= j <= i + wr,
+a negative bound = unbounded) and ALiBi slopes ``slopes`` [H] (the score gets
+-slope_h * |i - j|).
 
 Every function is pinned by tests/test_oracle.py against facts that do not
 come from this code: a brute-force evaluation with a different softmax
@@ -60,8 +63,17 @@ class _Lib:
                                             c_int, _u8p, c_int, _dp, _dp]
         lib.ref_attn_bwd.argtypes = [_dp, _dp, _dp, _dp, c_int, c_int, c_int, c_int, c_double,
                                      c_int, _u8p, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.ref_attn_fwd_ex.argtypes = [_dp, _dp, _dp, c_int, c_int, c_int, c_int, c_double, c_int,
+                                        _u8p, c_int, c_int, _dp, _dp, _dp]
+        lib.ref_attn_fwd_rows_ex.argtypes = [_dp, _dp, _dp, c_int, c_int, c_int, c_int, c_double,
+                                             c_int, _u8p, c_int, c_int, _dp, _i64p, c_int, _dp, _dp]
+        lib.ref_attn_fwd_online_ex.argtypes = [_dp, _dp, _dp, c_int, c_int, c_int, c_int, c_double,
+                                               c_int, _u8p, c_int, c_int, _dp, c_int, _dp, _dp]
+        lib.ref_attn_bwd_ex.argtypes = [_dp, _dp, _dp, _dp, c_int, c_int, c_int, c_int, c_double,
+                                        c_int, _u8p, c_int, c_int, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         for f in ("ref_attn_probs", "ref_attn_fwd", "ref_attn_fwd_rows", "ref_attn_fwd_online",
-                  "ref_attn_bwd"):
+                  "ref_attn_bwd", "ref_attn_fwd_ex", "ref_attn_fwd_rows_ex", "ref_attn_fwd_online_ex",
+                  "ref_attn_bwd_ex"):
             getattr(lib, f).restype = c_int
         self.lib = lib
 
@@ -105,25 +117,47 @@ def _shape(q):
     return q.shape
 
 
+def _window(window):
+    """(wl, wr) with -1 for an unbounded side."""
+    if window is None:
+        return -1, -1
+    wl, wr = window
+    wl = -1 if wl is None or wl < 0 else int(wl)
+    wr = -1 if wr is None or wr < 0 else int(wr)
+    return wl, wr
+
+
+def _slopes(slopes, H: int):
+    if slopes is None:
+        return None
+    a = np.ascontiguousarray(slopes, dtype=np.float64).reshape(-1)
+    if a.shape != (H,):
+        raise ValueError(f"slopes must have H={H} entries, got {a.shape}")
+    return a
+
+
 def _check(rc: int, what: str):
     if rc != 0:
         raise MemoryError(f"oracle {what} failed (allocation)")
 
 
-def attn_fwd(q, k, v, scale: float, causal: bool = False, mask=None) -> Tuple[np.ndarray, np.ndarray]:
+def attn_fwd(q, k, v, scale: float, causal: bool = False, mask=None, window=None,
+             slopes=None) -> Tuple[np.ndarray, np.ndarray]:
     """Exact attention forward: (O [B,H,N,d], lse [B,H,N]) from the definition."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = _shape(q)
     m = _mask(mask, N)
+    wl, wr = _window(window)
+    sl = _slopes(slopes, H)
     o = np.empty_like(q)
     lse = np.empty((B, H, N), dtype=np.float64)
-    rc = _load().ref_attn_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(causal),
-                              _ptr(m, _u8p), _ptr(o), _ptr(lse))
+    rc = _load().ref_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(causal),
+                                 _ptr(m, _u8p), wl, wr, _ptr(sl), _ptr(o), _ptr(lse))
     _check(rc, "fwd")
     return o, lse
 
 
-def attn_fwd_rows(q, k, v, scale: float, rows, causal: bool = False, mask=None):
+def attn_fwd_rows(q, k, v, scale: float, rows, causal: bool = False, mask=None, window=None, slopes=None):
     """Output rows only: rows is [R, 2] of (b*H + h, i).  Returns (O [R, d], lse [R])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = _shape(q)
@@ -133,23 +167,30 @@ def attn_fwd_rows(q, k, v, scale: float, rows, causal: bool = False, mask=None):
         raise ValueError("rows must be [R, 2]")
     if r.size and (r[:, 0].min() < 0 or r[:, 0].max() >= B * H or r[:, 1].min() < 0 or r[:, 1].max() >= N):
         raise ValueError("row index out of range")
+    wl, wr = _window(window)
+    sl = _slopes(slopes, H)
     o = np.empty((r.shape[0], d), dtype=np.float64)
     lse = np.empty((r.shape[0],), dtype=np.float64)
-    rc = _load().ref_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(causal),
-                                   _ptr(m, _u8p), _ptr(r, _i64p), r.shape[0], _ptr(o), _ptr(lse))
+    rc = _load().ref_attn_fwd_rows_ex(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(causal),
+                                      _ptr(m, _u8p), wl, wr, _ptr(sl), _ptr(r, _i64p), r.shape[0],
+                                      _ptr(o), _ptr(lse))
     _check(rc, "fwd_rows")
     return o, lse
 
 
-def attn_fwd_online(q, k, v, scale: float, chunk: int, causal: bool = False, mask=None):
+def attn_fwd_online(q, k, v, scale: float, chunk: int, causal: bool = False, mask=None, window=None,
+                    slopes=None):
     """Online-softmax forward scanning keys in chunks of ``chunk`` (same outputs as attn_fwd)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = _shape(q)
     m = _mask(mask, N)
+    wl, wr = _window(window)
+    sl = _slopes(slopes, H)
     o = np.empty_like(q)
     lse = np.empty((B, H, N), dtype=np.float64)
-    rc = _load().ref_attn_fwd_online(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale),
-                                     int(causal), _ptr(m, _u8p), int(chunk), _ptr(o), _ptr(lse))
+    rc = _load().ref_attn_fwd_online_ex(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale),
+                                        int(causal), _ptr(m, _u8p), wl, wr, _ptr(sl), int(chunk), _ptr(o),
+                                        _ptr(lse))
     _check(rc, "fwd_online")
     return o, lse
 
@@ -167,7 +208,8 @@ def attn_probs(q_head, k_head, scale: float, causal: bool = False, mask=None):
     return P, lse
 
 
-def attn_bwd(q, k, v, do, scale: float, causal: bool = False, mask=None, return_fwd: bool = False):
+def attn_bwd(q, k, v, do, scale: float, causal: bool = False, mask=None, return_fwd: bool = False,
+             window=None, slopes=None):
     """Gradients (dQ, dK, dV) of sum(dO * O) with O the exact attention output.
 
     With ``return_fwd`` also returns (O, lse, D) where D_i = sum_j P_ij dP_ij.
@@ -175,13 +217,15 @@ def attn_bwd(q, k, v, do, scale: float, causal: bool = False, mask=None, return_
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, N, d = _shape(q)
     m = _mask(mask, N)
+    wl, wr = _window(window)
+    sl = _slopes(slopes, H)
     dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
     o = np.empty_like(q) if return_fwd else None
     lse = np.empty((B, H, N)) if return_fwd else None
     D = np.empty((B, H, N)) if return_fwd else None
-    rc = _load().ref_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), B, H, N, d, float(scale),
-                              int(causal), _ptr(m, _u8p), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(o),
-                              _ptr(lse), _ptr(D))
+    rc = _load().ref_attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(do), B, H, N, d, float(scale),
+                                 int(causal), _ptr(m, _u8p), wl, wr, _ptr(sl), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(o), _ptr(lse), _ptr(D))
     _check(rc, "bwd")
     if return_fwd:
         return dq, dk, dv, o, lse, D

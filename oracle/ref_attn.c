@@ -20,8 +20,12 @@
  * shared by all (b, h); nonzero = block kept.
  *
  * Conventions (choices where the pages are silent):
- *   S_ij = scale * sum_k q_ik k_jk
+ *   S_ij = scale * sum_k q_ik k_jk - slope_h |i - j|   (slope_h = 0 without ALiBi)
  *   allowed(i, j) = (!causal || j <= i) && (mask == NULL || mask[i/128][j/128])
+ *                   && (wl < 0 || j >= i - wl) && (wr < 0 || j <= i + wr)
+ *   The window (wl, wr) and the per-head ALiBi slopes are the two further
+ *   built-in variants "FlashAttention 深度解析" section 五 names beside the
+ *   causal mask; the `_ex` entry points take them, the others use none.
  *   m_i = max over allowed j of S_ij;  Z_i = sum over allowed j of exp(S_ij - m_i)
  *   P_ij = exp(S_ij - m_i) / Z_i if allowed else 0
  *   O_i = sum_j P_ij v_j;  lse_i = m_i + log(Z_i)
@@ -55,15 +59,40 @@ int ref_num_threads(void) {
 #endif
 }
 
-static int ref_allowed(long i, long j, int causal, const uint8_t* mask, long nb) {
+/* Local-window bounds (negative = unbounded) and the ALiBi slope of the head. */
+typedef struct {
+    long wl, wr;
+    double slope;
+} ref_var;
+
+static const ref_var REF_PLAIN = {-1, -1, 0.0};
+
+static int ref_allowed(long i, long j, int causal, const uint8_t* mask, long nb, const ref_var* var) {
     if (causal && j > i) return 0;
     if (mask && !mask[(i / REF_MASK_BLOCK) * nb + (j / REF_MASK_BLOCK)]) return 0;
+    if (var->wl >= 0 && j < i - var->wl) return 0;
+    if (var->wr >= 0 && j > i + var->wr) return 0;
     return 1;
+}
+
+/* The ALiBi term of S_ij. */
+static double ref_bias(long i, long j, const ref_var* var) {
+    return var->slope == 0.0 ? 0.0 : -var->slope * (double)(i > j ? i - j : j - i);
+}
+
+/* Variant of head bh (slopes indexed by h = bh mod H). */
+static ref_var ref_var_of(long bh, int H, int wl, int wr, const double* slopes) {
+    ref_var v;
+    v.wl = wl;
+    v.wr = wr;
+    v.slope = slopes ? slopes[bh % H] : 0.0;
+    return v;
 }
 
 /* Scores, probabilities and lse of one head.  S and P are N*N doubles each. */
 static void ref_head_probs(const double* q, const double* k, long N, long d, double scale,
-                           int causal, const uint8_t* mask, double* S, double* P, double* lse) {
+                           int causal, const uint8_t* mask, const ref_var* var, double* S, double* P,
+                           double* lse) {
     long nb = (N + REF_MASK_BLOCK - 1) / REF_MASK_BLOCK;
 #pragma omp parallel for schedule(static)
     for (long i = 0; i < N; i++) {
@@ -71,13 +100,13 @@ static void ref_head_probs(const double* q, const double* k, long N, long d, dou
         for (long j = 0; j < N; j++) {
             double acc = 0.0;
             for (long c = 0; c < d; c++) acc += q[i * d + c] * k[j * d + c];
-            S[i * N + j] = scale * acc;
+            S[i * N + j] = scale * acc + ref_bias(i, j, var);
         }
         /* 2. stable softmax over the allowed keys */
         double m = -INFINITY;
         long count = 0;
         for (long j = 0; j < N; j++)
-            if (ref_allowed(i, j, causal, mask, nb)) {
+            if (ref_allowed(i, j, causal, mask, nb, var)) {
                 if (S[i * N + j] > m) m = S[i * N + j];
                 count++;
             }
@@ -88,9 +117,9 @@ static void ref_head_probs(const double* q, const double* k, long N, long d, dou
         }
         double z = 0.0;
         for (long j = 0; j < N; j++)
-            if (ref_allowed(i, j, causal, mask, nb)) z += exp(S[i * N + j] - m);
+            if (ref_allowed(i, j, causal, mask, nb, var)) z += exp(S[i * N + j] - m);
         for (long j = 0; j < N; j++)
-            P[i * N + j] = ref_allowed(i, j, causal, mask, nb) ? exp(S[i * N + j] - m) / z : 0.0;
+            P[i * N + j] = ref_allowed(i, j, causal, mask, nb, var) ? exp(S[i * N + j] - m) / z : 0.0;
         lse[i] = m + log(z);
     }
 }
@@ -113,19 +142,21 @@ int ref_attn_probs(const double* q, const double* k, int N, int d, double scale,
                    const uint8_t* mask, double* P, double* lse) {
     double* S = (double*)malloc(sizeof(double) * (size_t)N * N);
     if (!S) return 1;
-    ref_head_probs(q, k, N, d, scale, causal, mask, S, P, lse);
+    ref_head_probs(q, k, N, d, scale, causal, mask, &REF_PLAIN, S, P, lse);
     free(S);
     return 0;
 }
 
-int ref_attn_fwd(const double* q, const double* k, const double* v, int B, int H, int N, int d,
-                 double scale, int causal, const uint8_t* mask, double* o, double* lse) {
+int ref_attn_fwd_ex(const double* q, const double* k, const double* v, int B, int H, int N, int d,
+                    double scale, int causal, const uint8_t* mask, int wl, int wr, const double* slopes,
+                    double* o, double* lse) {
     size_t nn = (size_t)N * N, nd = (size_t)N * d;
     double* S = (double*)malloc(sizeof(double) * nn);
     double* P = (double*)malloc(sizeof(double) * nn);
     if (!S || !P) { free(S); free(P); return 1; }
     for (long bh = 0; bh < (long)B * H; bh++) {
-        ref_head_probs(q + bh * nd, k + bh * nd, N, d, scale, causal, mask, S, P, lse + bh * N);
+        const ref_var var = ref_var_of(bh, H, wl, wr, slopes);
+        ref_head_probs(q + bh * nd, k + bh * nd, N, d, scale, causal, mask, &var, S, P, lse + bh * N);
         ref_head_pv(P, v + bh * nd, N, d, o + bh * nd);
     }
     free(S);
@@ -133,17 +164,23 @@ int ref_attn_fwd(const double* q, const double* k, const double* v, int B, int H
     return 0;
 }
 
+int ref_attn_fwd(const double* q, const double* k, const double* v, int B, int H, int N, int d,
+                 double scale, int causal, const uint8_t* mask, double* o, double* lse) {
+    return ref_attn_fwd_ex(q, k, v, B, H, N, d, scale, causal, mask, -1, -1, NULL, o, lse);
+}
+
 /*
  * Selected rows only: rows[r] = {bh, i}.  Each row's scores, probabilities and
  * output follow the same definition; nothing is shared between rows.
  */
-int ref_attn_fwd_rows(const double* q, const double* k, const double* v, int B, int H, int N, int d,
-                      double scale, int causal, const uint8_t* mask, const int64_t* rows, int nrows,
-                      double* o_rows, double* lse_rows) {
+int ref_attn_fwd_rows_ex(const double* q, const double* k, const double* v, int B, int H, int N,
+                         int d, double scale, int causal, const uint8_t* mask, int wl, int wr,
+                         const double* slopes, const int64_t* rows, int nrows, double* o_rows,
+                         double* lse_rows) {
     size_t nd = (size_t)N * d;
     long nb = (N + REF_MASK_BLOCK - 1) / REF_MASK_BLOCK;
     int err = 0;
-    (void)B; (void)H;
+    (void)B;
 #pragma omp parallel
     {
         double* srow = (double*)malloc(sizeof(double) * (size_t)N);
@@ -155,18 +192,20 @@ int ref_attn_fwd_rows(const double* q, const double* k, const double* v, int B, 
 #pragma omp for schedule(dynamic, 1)
             for (int r = 0; r < nrows; r++) {
                 long bh = rows[2 * r], i = rows[2 * r + 1];
+                const ref_var vv = ref_var_of(bh, H, wl, wr, slopes);
+                const ref_var* var = &vv;
                 const double* qi = q + bh * nd + i * d;
                 const double* kh = k + bh * nd;
                 const double* vh = v + bh * nd;
                 for (long j = 0; j < N; j++) {
                     double acc = 0.0;
                     for (long c = 0; c < d; c++) acc += qi[c] * kh[j * d + c];
-                    srow[j] = scale * acc;
+                    srow[j] = scale * acc + ref_bias(i, j, var);
                 }
                 double m = -INFINITY;
                 long count = 0;
                 for (long j = 0; j < N; j++)
-                    if (ref_allowed(i, j, causal, mask, nb)) {
+                    if (ref_allowed(i, j, causal, mask, nb, var)) {
                         if (srow[j] > m) m = srow[j];
                         count++;
                     }
@@ -175,9 +214,9 @@ int ref_attn_fwd_rows(const double* q, const double* k, const double* v, int B, 
                 if (count == 0) { lse_rows[r] = -INFINITY; continue; }
                 double z = 0.0;
                 for (long j = 0; j < N; j++)
-                    if (ref_allowed(i, j, causal, mask, nb)) z += exp(srow[j] - m);
+                    if (ref_allowed(i, j, causal, mask, nb, var)) z += exp(srow[j] - m);
                 for (long j = 0; j < N; j++) {
-                    prow[j] = ref_allowed(i, j, causal, mask, nb) ? exp(srow[j] - m) / z : 0.0;
+                    prow[j] = ref_allowed(i, j, causal, mask, nb, var) ? exp(srow[j] - m) / z : 0.0;
                     if (prow[j] == 0.0) continue;
                     for (long c = 0; c < d; c++) orow[c] += prow[j] * vh[j * d + c];
                 }
@@ -190,15 +229,22 @@ int ref_attn_fwd_rows(const double* q, const double* k, const double* v, int B, 
     return err;
 }
 
+int ref_attn_fwd_rows(const double* q, const double* k, const double* v, int B, int H, int N, int d,
+                      double scale, int causal, const uint8_t* mask, const int64_t* rows, int nrows,
+                      double* o_rows, double* lse_rows) {
+    return ref_attn_fwd_rows_ex(q, k, v, B, H, N, d, scale, causal, mask, -1, -1, NULL, rows, nrows,
+                                o_rows, lse_rows);
+}
+
 /*
  * Online softmax ("FlashAttention 深度解析" section 二): scan the keys of each
  * row in chunks of `chunk`; keep the running max m, the running sum l and the
  * unnormalized output o; when the max grows, rescale l and o by exp(m - m_new);
  * divide once at the end.  Keys a mask removes are skipped.
  */
-int ref_attn_fwd_online(const double* q, const double* k, const double* v, int B, int H, int N,
-                        int d, double scale, int causal, const uint8_t* mask, int chunk,
-                        double* o, double* lse) {
+int ref_attn_fwd_online_ex(const double* q, const double* k, const double* v, int B, int H, int N,
+                           int d, double scale, int causal, const uint8_t* mask, int wl, int wr,
+                           const double* slopes, int chunk, double* o, double* lse) {
     if (chunk < 1) return 1;
     size_t nd = (size_t)N * d;
     long nb = (N + REF_MASK_BLOCK - 1) / REF_MASK_BLOCK;
@@ -207,6 +253,8 @@ int ref_attn_fwd_online(const double* q, const double* k, const double* v, int B
         const double* qh = q + bh * nd;
         const double* kh = k + bh * nd;
         const double* vh = v + bh * nd;
+        const ref_var vv = ref_var_of(bh, H, wl, wr, slopes);
+        const ref_var* var = &vv;
 #pragma omp parallel
         {
             double* sblk = (double*)malloc(sizeof(double) * (size_t)chunk);
@@ -227,8 +275,8 @@ int ref_attn_fwd_online(const double* q, const double* k, const double* v, int B
                     for (long j = j0; j < j1; j++) {
                         double acc = 0.0;
                         for (long c = 0; c < d; c++) acc += qh[i * d + c] * kh[j * d + c];
-                        sblk[j - j0] = scale * acc;
-                        if (ref_allowed(i, j, causal, mask, nb) && sblk[j - j0] > bmax) bmax = sblk[j - j0];
+                        sblk[j - j0] = scale * acc + ref_bias(i, j, var);
+                        if (ref_allowed(i, j, causal, mask, nb, var) && sblk[j - j0] > bmax) bmax = sblk[j - j0];
                     }
                     if (bmax == -INFINITY) continue; /* nothing allowed in this chunk */
                     double m_new = m > bmax ? m : bmax;
@@ -236,7 +284,7 @@ int ref_attn_fwd_online(const double* q, const double* k, const double* v, int B
                     l *= corr;
                     for (long c = 0; c < d; c++) oi[c] *= corr;
                     for (long j = j0; j < j1; j++) {
-                        if (!ref_allowed(i, j, causal, mask, nb)) continue;
+                        if (!ref_allowed(i, j, causal, mask, nb, var)) continue;
                         double p = exp(sblk[j - j0] - m_new);
                         l += p;
                         for (long c = 0; c < d; c++) oi[c] += p * vh[j * d + c];
@@ -256,13 +304,20 @@ int ref_attn_fwd_online(const double* q, const double* k, const double* v, int B
     return err;
 }
 
+int ref_attn_fwd_online(const double* q, const double* k, const double* v, int B, int H, int N,
+                        int d, double scale, int causal, const uint8_t* mask, int chunk,
+                        double* o, double* lse) {
+    return ref_attn_fwd_online_ex(q, k, v, B, H, N, d, scale, causal, mask, -1, -1, NULL, chunk, o, lse);
+}
+
 /*
  * Backward of the definition above for every (b, h).  Optionally returns the
  * forward's O and lse and the row terms D (pointers may be NULL).
  */
-int ref_attn_bwd(const double* q, const double* k, const double* v, const double* dO, int B, int H,
-                 int N, int d, double scale, int causal, const uint8_t* mask, double* dq, double* dk,
-                 double* dv, double* o_out, double* lse_out, double* D_out) {
+int ref_attn_bwd_ex(const double* q, const double* k, const double* v, const double* dO, int B, int H,
+                    int N, int d, double scale, int causal, const uint8_t* mask, int wl, int wr,
+                    const double* slopes, double* dq, double* dk, double* dv, double* o_out,
+                    double* lse_out, double* D_out) {
     size_t nn = (size_t)N * N, nd = (size_t)N * d;
     double* S = (double*)malloc(sizeof(double) * nn);
     double* P = (double*)malloc(sizeof(double) * nn);
@@ -279,7 +334,8 @@ int ref_attn_bwd(const double* q, const double* k, const double* v, const double
         const double* kh = k + bh * nd;
         const double* vh = v + bh * nd;
         const double* doh = dO + bh * nd;
-        ref_head_probs(qh, kh, N, d, scale, causal, mask, S, P, lse);
+        const ref_var var = ref_var_of(bh, H, wl, wr, slopes);
+        ref_head_probs(qh, kh, N, d, scale, causal, mask, &var, S, P, lse);
         if (o_out) ref_head_pv(P, vh, N, d, o_out + bh * nd);
         if (lse_out) memcpy(lse_out + bh * N, lse, sizeof(double) * (size_t)N);
         /* dP = dO V^T */
@@ -339,4 +395,11 @@ int ref_attn_bwd(const double* q, const double* k, const double* v, const double
     }
     free(S); free(P); free(dP); free(lse); free(D);
     return 0;
+}
+
+int ref_attn_bwd(const double* q, const double* k, const double* v, const double* dO, int B, int H,
+                 int N, int d, double scale, int causal, const uint8_t* mask, double* dq, double* dk,
+                 double* dv, double* o_out, double* lse_out, double* D_out) {
+    return ref_attn_bwd_ex(q, k, v, dO, B, H, N, d, scale, causal, mask, -1, -1, NULL, dq, dk, dv, o_out,
+                           lse_out, D_out);
 }

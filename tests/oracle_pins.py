@@ -30,27 +30,37 @@ def _rng(seed):
     return np.random.default_rng(seed)
 
 
-def _allowed(i, j, causal, mask):
+def _allowed(i, j, causal, mask, window=None):
     if causal and j > i:
         return False
     if mask is not None and not mask[i // MB, j // MB]:
         return False
+    if window is not None:
+        # local window: keys from i - left to i + right (None or < 0: unbounded)
+        left, right = window
+        if left is not None and left >= 0 and j < i - left:
+            return False
+        if right is not None and right >= 0 and j > i + right:
+            return False
     return True
 
 
-def brute_force_head(q, k, v, scale, causal=False, mask=None):
-    """Pure-Python scalar attention for one head with exp(s)/fsum(exp(s))."""
+def brute_force_head(q, k, v, scale, causal=False, mask=None, window=None, slope=0.0):
+    """Pure-Python scalar attention for one head with exp(s)/fsum(exp(s)).
+
+    ``slope``: ALiBi, the score of (i, j) gets -slope * |i - j| after scaling.
+    """
     N, d = q.shape
     o = [[0.0] * d for _ in range(N)]
     lse = [0.0] * N
     for i in range(N):
-        cols = [j for j in range(N) if _allowed(i, j, causal, mask)]
+        cols = [j for j in range(N) if _allowed(i, j, causal, mask, window)]
         if not cols:
             lse[i] = -math.inf
             continue
         e = []
         for j in cols:
-            s = scale * math.fsum(float(q[i, c]) * float(k[j, c]) for c in range(d))
+            s = scale * math.fsum(float(q[i, c]) * float(k[j, c]) for c in range(d)) - slope * abs(i - j)
             e.append(math.exp(s))
         z = math.fsum(e)
         for c in range(d):
@@ -306,6 +316,135 @@ def pin_backward_identities(orc):
         assert np.max(np.abs(dv.sum(axis=2) - do.sum(axis=2))) <= 1e-10
 
 
+# ----------------------------------------------------------------------------
+# Local window and ALiBi (the further built-in variants of "FlashAttention
+# 深度解析" section 五)
+# ----------------------------------------------------------------------------
+
+def pin_window_alibi_brute_force(orc):
+    """Window and ALiBi (alone and combined, with causal and a block mask) vs the brute force."""
+    g = _rng(21)
+    cases = [(9, 3, False, None, (2, 1), None), (9, 3, True, None, (3, -1), None),
+             (9, 3, False, None, None, (0.3, 1.1)), (12, 4, True, None, (4, -1), (0.7, 0.05)),
+             (10, 2, False, None, (0, 0), (0.5, 0.5)), (11, 3, False, None, (-1, 2), (1.5, 0.0)),
+             (140, 2, False, np.array([[1, 0], [1, 1]], dtype=np.uint8), (60, 5), (0.02, 0.2))]
+    for N, d, causal, m, window, slopes in cases:
+        q, k, v = (g.standard_normal((1, 2, N, d)) for _ in range(3))
+        o, lse = orc.attn_fwd(q, k, v, 0.7, causal, m, window=window, slopes=slopes)
+        for h in range(2):
+            sl = 0.0 if slopes is None else slopes[h]
+            ob, lb = brute_force_head(q[0, h], k[0, h], v[0, h], 0.7, causal, m, window, sl)
+            _close(o[0, h], ob, 1e-12, f"window/alibi O N={N} h={h}")
+            _close(lse[0, h], lb, 1e-12, f"window/alibi lse N={N} h={h}")
+
+
+def pin_window_special_cases(orc):
+    """Window (inf, 0) = causal; a window wider than N = no window; window (0, 0)
+    keeps only the diagonal: O_i = V_i and lse_i = scale q_i.k_i (ALiBi adds 0 there)."""
+    g = _rng(22)
+    N, d = 37, 5
+    q, k, v = (g.standard_normal((1, 2, N, d)) for _ in range(3))
+    o_c, l_c = orc.attn_fwd(q, k, v, 0.4, True)
+    o_w, l_w = orc.attn_fwd(q, k, v, 0.4, False, window=(-1, 0))
+    _close(o_w, o_c, 1e-15, "window (inf, 0) = causal")
+    _close(l_w, l_c, 1e-15, "window (inf, 0) = causal lse")
+    o_d, l_d = orc.attn_fwd(q, k, v, 0.4, False)
+    o_n, l_n = orc.attn_fwd(q, k, v, 0.4, False, window=(N, N + 3))
+    _close(o_n, o_d, 1e-15, "wide window = dense")
+    _close(l_n, l_d, 1e-15, "wide window = dense lse")
+    o_0, l_0 = orc.attn_fwd(q, k, v, 0.4, False, window=(0, 0), slopes=(0.9, 2.0))
+    _close(o_0, v, 1e-14, "window (0, 0): O = V")
+    _close(l_0, 0.4 * np.einsum("bhnd,bhnd->bhn", q, k), 1e-13, "window (0, 0): lse = s q.k")
+
+
+def pin_alibi_closed_form(orc):
+    """Scale 0 leaves only the bias: with two keys P_i = softmax(0, -m) in key order
+    of distance, O and lse in closed form; slope 0 equals no ALiBi."""
+    g = _rng(23)
+    d = 4
+    q, k, v = (g.standard_normal((1, 1, 2, d)) for _ in range(3))
+    m = 0.8
+    o, lse = orc.attn_fwd(q, k, v, 0.0, False, slopes=(m,))
+    e = math.exp(-m)
+    _close(o[0, 0, 0], (v[0, 0, 0] + e * v[0, 0, 1]) / (1 + e), 1e-14, "alibi row 0")
+    _close(o[0, 0, 1], (e * v[0, 0, 0] + v[0, 0, 1]) / (1 + e), 1e-14, "alibi row 1")
+    _close(lse[0, 0], [math.log1p(e)] * 2, 1e-14, "alibi lse")
+    q, k, v = (g.standard_normal((1, 3, 30, d)) for _ in range(3))
+    o1, l1 = orc.attn_fwd(q, k, v, 0.5, True, slopes=(0.0, 0.0, 0.0))
+    o2, l2 = orc.attn_fwd(q, k, v, 0.5, True)
+    _close(o1, o2, 1e-15, "slope 0 = no alibi")
+    _close(l1, l2, 1e-15, "slope 0 = no alibi lse")
+
+
+def pin_alibi_is_additive_bias(orc):
+    """ALiBi is exactly the additive bias -m_h |i - j|: a numpy softmax of the
+    biased, window-masked score matrix gives the same O and lse."""
+    g = _rng(24)
+    B, H, N, d = 1, 3, 150, 6
+    q, k, v = (g.standard_normal((B, H, N, d)) for _ in range(3))
+    slopes = np.array([0.01, 0.25, 1.0])
+    window = (40, 7)
+    o, lse = orc.attn_fwd(q, k, v, 0.35, False, window=window, slopes=slopes)
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    keep = (j >= i - window[0]) & (j <= i + window[1])
+    for h in range(H):
+        s = 0.35 * (q[0, h] @ k[0, h].T) - slopes[h] * np.abs(i - j)
+        s = np.where(keep, s, -np.inf)
+        mx = s.max(axis=1, keepdims=True)
+        e = np.exp(s - mx)
+        z = e.sum(axis=1, keepdims=True)
+        _close(o[0, h], (e / z) @ v[0, h], 1e-12, f"alibi bias O h={h}")
+        _close(lse[0, h], (mx + np.log(z))[:, 0], 1e-12, f"alibi bias lse h={h}")
+
+
+def pin_window_alibi_chunked_and_rows(orc):
+    """The online loop and the sampled-row entry point agree with the one-shot
+    forward under window + ALiBi."""
+    g = _rng(25)
+    B, H, N, d = 1, 2, 300, 4
+    q, k, v = (g.standard_normal((B, H, N, d)) for _ in range(3))
+    kw = dict(window=(70, 3), slopes=(0.05, 0.3))
+    o, lse = orc.attn_fwd(q, k, v, 0.5, True, **kw)
+    for chunk in (1, 13, 128):
+        oc, lc = orc.attn_fwd_online(q, k, v, 0.5, chunk, True, **kw)
+        _close(oc, o, 1e-12, f"online chunk={chunk}")
+        _close(lc, lse, 1e-12, f"online lse chunk={chunk}")
+    rows = np.array([[0, 0], [1, 5], [0, 150], [1, 299], [1, 71]], dtype=np.int64)
+    orr, lrr = orc.attn_fwd_rows(q, k, v, 0.5, rows, True, **kw)
+    for t, (bh, i) in enumerate(rows):
+        _close(orr[t], o[0, bh, i], 1e-14, "rows O")
+        _close(lrr[t], lse[0, bh, i], 1e-14, "rows lse")
+
+
+def pin_window_alibi_finite_differences(orc):
+    """dQ, dK, dV under window + ALiBi equal central differences of sum(dO * O)."""
+    g = _rng(26)
+    h = 1e-6
+    for N, d, causal, window, slopes in ((8, 3, False, (2, 1), (0.4,)), (11, 2, True, (3, -1), (1.2,))):
+        q, k, v, do = (g.standard_normal((1, 1, N, d)) for _ in range(4))
+        s = 0.6
+        kw = dict(window=window, slopes=slopes)
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, s, causal, None, **kw)
+
+        def loss(qq, kk, vv):
+            o, _ = orc.attn_fwd(qq, kk, vv, s, causal, None, **kw)
+            return float(np.sum(do * o))
+
+        for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            for i in range(N):
+                for c in range(d):
+                    xp, xm = x.copy(), x.copy()
+                    xp[0, 0, i, c] += h
+                    xm[0, 0, i, c] -= h
+                    a_p = {"q": q, "k": k, "v": v}
+                    a_m = {"q": q, "k": k, "v": v}
+                    a_p[name], a_m[name] = xp, xm
+                    fd = (loss(a_p["q"], a_p["k"], a_p["v"]) - loss(a_m["q"], a_m["k"], a_m["v"])) / (2 * h)
+                    an = grad[0, 0, i, c]
+                    assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, N, i, c, fd, an)
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_rows_sum_to_one,
@@ -317,4 +456,10 @@ ALL_PINS = [
     pin_rows_match_full,
     pin_finite_differences,
     pin_backward_identities,
+    pin_window_alibi_brute_force,
+    pin_window_special_cases,
+    pin_alibi_closed_form,
+    pin_alibi_is_additive_bias,
+    pin_window_alibi_chunked_and_rows,
+    pin_window_alibi_finite_differences,
 ]

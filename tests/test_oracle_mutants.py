@@ -13,7 +13,13 @@ import oracle
 from tests import oracle_pins as P
 
 MUTANTS = {
-    "drop_scale": ("S[i * N + j] = scale * acc;", "S[i * N + j] = acc;"),
+    "drop_scale": ("S[i * N + j] = scale * acc + ref_bias(i, j, var);", "S[i * N + j] = acc + ref_bias(i, j, var);"),
+    "alibi_sign": ("-var->slope * (double)(i > j ? i - j : j - i)", "var->slope * (double)(i > j ? i - j : j - i)"),
+    "alibi_signed_distance": ("(double)(i > j ? i - j : j - i)", "(double)(i - j)"),
+    "alibi_head_index": ("slopes[bh % H]", "slopes[0]"),
+    "window_left_off_by_one": ("j < i - var->wl", "j <= i - var->wl"),
+    "window_right_off_by_one": ("j > i + var->wr", "j >= i + var->wr"),
+    "window_sides_swapped": ("v.wl = wl;\n    v.wr = wr;", "v.wl = wr;\n    v.wr = wl;"),
     "causal_strict": ("if (causal && j > i) return 0;", "if (causal && j >= i) return 0;"),
     "mask_transposed": ("mask[(i / REF_MASK_BLOCK) * nb + (j / REF_MASK_BLOCK)]",
                         "mask[(j / REF_MASK_BLOCK) * nb + (i / REF_MASK_BLOCK)]"),
