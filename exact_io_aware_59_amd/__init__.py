@@ -11,7 +11,10 @@ call raises.
 
 Tensors are [B, H, N, d], contiguous; bf16 for fa_fwd/fa_bwd, float32 for the
 _f32 entry points; lse is float32 [B, H, N]; the optional block mask is a
-uint8 tensor [ceil(N/128), ceil(N/128)] on the same device.
+uint8 tensor [ceil(N/128), ceil(N/128)] on the same device.  The _ex entry
+points (and ``forward`` / ``backward`` given ``window`` or ``alibi_slopes``)
+take the local window (left, right) -- None or a negative bound is
+unbounded -- and ALiBi slopes as a float32 tensor [H] on the device.
 """
 from __future__ import annotations
 
@@ -23,6 +26,7 @@ from typing import Optional, Tuple
 __all__ = [
     "FAError", "library_path", "load", "fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32",
     "fa_bwd_workspace_size", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq", "fa_status_string", "fa_version",
+    "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex", "fa_bwd_dq_ex", "Variant",
     "forward", "backward", "workspace",
     "MASK_BLOCK",
 ]
@@ -30,6 +34,12 @@ __all__ = [
 MASK_BLOCK = 128
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
+
+
+class Variant(ctypes.Structure):
+    """fa_variant: local window (negative = unbounded) and a device pointer to ALiBi slopes (or 0)."""
+    _fields_ = [("window_left", ctypes.c_int), ("window_right", ctypes.c_int),
+                ("alibi_slopes", ctypes.c_void_p)]
 
 
 class FAError(RuntimeError):
@@ -59,8 +69,16 @@ def load():
     lib.fa_bwd_prep.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
+    vr = ctypes.POINTER(Variant)
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp]
+    lib.fa_fwd_f32_ex.argtypes = lib.fa_fwd_ex.argtypes
+    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp, sz, vp]
+    lib.fa_bwd_f32_ex.argtypes = lib.fa_bwd_ex.argtypes
+    lib.fa_bwd_main_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp, sz, vp]
+    lib.fa_bwd_dq_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp, sz, vp]
     for name in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq",
-                 "fa_version"):
+                 "fa_version", "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex",
+                 "fa_bwd_dq_ex"):
         getattr(lib, name).restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
@@ -109,6 +127,16 @@ def _dims(q) -> Tuple[int, int, int, int]:
         raise ValueError("expected [B, H, N, d]")
     B, H, N, d = q.shape
     return int(B), int(H), int(N), int(d)
+
+
+def _variant(window=None, alibi_slopes=None):
+    """ctypes fa_variant pointer (or None for the plain computation)."""
+    if window is None and alibi_slopes is None:
+        return None
+    wl, wr = window if window is not None else (None, None)
+    v = Variant(-1 if wl is None or wl < 0 else int(wl), -1 if wr is None or wr < 0 else int(wr),
+                _ptr(alibi_slopes) if alibi_slopes is not None else None)
+    return ctypes.pointer(v)
 
 
 def _check(status: int, where: str):
@@ -175,6 +203,56 @@ def fa_bwd_dq(q, k, v, do, dq, scale: float, causal: bool = False, blockmask=Non
                             _stream(stream)), "fa_bwd_dq")
 
 
+def fa_fwd_ex(q, k, v, o, lse, scale: float, causal: bool = False, blockmask=None, window=None,
+              alibi_slopes=None, stream=None):
+    B, H, N, d = _dims(q)
+    _check(load().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                            int(bool(causal)), _ptr(blockmask), _variant(window, alibi_slopes), _stream(stream)),
+           "fa_fwd_ex")
+
+
+def fa_fwd_f32_ex(q, k, v, o, lse, scale: float, causal: bool = False, blockmask=None, window=None,
+                  alibi_slopes=None, stream=None):
+    B, H, N, d = _dims(q)
+    _check(load().fa_fwd_f32_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                int(bool(causal)), _ptr(blockmask), _variant(window, alibi_slopes),
+                                _stream(stream)), "fa_fwd_f32_ex")
+
+
+def fa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, blockmask=None, window=None,
+              alibi_slopes=None, workspace=None, stream=None):
+    B, H, N, d = _dims(q)
+    _check(load().fa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                            _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(blockmask),
+                            _variant(window, alibi_slopes), _ptr(workspace), _nbytes(workspace),
+                            _stream(stream)), "fa_bwd_ex")
+
+
+def fa_bwd_f32_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, blockmask=None,
+                  window=None, alibi_slopes=None, workspace=None, stream=None):
+    B, H, N, d = _dims(q)
+    _check(load().fa_bwd_f32_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(blockmask),
+                                _variant(window, alibi_slopes), _ptr(workspace), _nbytes(workspace),
+                                _stream(stream)), "fa_bwd_f32_ex")
+
+
+def fa_bwd_main_ex(q, k, v, do, dk, dv, scale: float, causal: bool = False, blockmask=None, window=None,
+                   alibi_slopes=None, workspace=None, stream=None):
+    B, H, N, d = _dims(q)
+    _check(load().fa_bwd_main_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv), B, H, N, d,
+                                 float(scale), int(bool(causal)), _ptr(blockmask), _variant(window, alibi_slopes),
+                                 _ptr(workspace), _nbytes(workspace), _stream(stream)), "fa_bwd_main_ex")
+
+
+def fa_bwd_dq_ex(q, k, v, do, dq, scale: float, causal: bool = False, blockmask=None, window=None,
+                 alibi_slopes=None, workspace=None, stream=None):
+    B, H, N, d = _dims(q)
+    _check(load().fa_bwd_dq_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), B, H, N, d, float(scale),
+                               int(bool(causal)), _ptr(blockmask), _variant(window, alibi_slopes), _ptr(workspace),
+                               _nbytes(workspace), _stream(stream)), "fa_bwd_dq_ex")
+
+
 # ----------------------------------------------------------------------------
 # allocating wrappers
 # ----------------------------------------------------------------------------
@@ -183,15 +261,20 @@ def _default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
-def forward(q, k, v, scale: Optional[float] = None, causal: bool = False, blockmask=None, stream=None):
-    """Returns (o, lse).  bf16 inputs use fa_fwd, float32 inputs fa_fwd_f32."""
+def forward(q, k, v, scale: Optional[float] = None, causal: bool = False, blockmask=None, stream=None,
+            window=None, alibi_slopes=None):
+    """Returns (o, lse).  bf16 inputs use fa_fwd(_ex), float32 inputs fa_fwd_f32(_ex)."""
     import torch
     B, H, N, d = _dims(q)
     scale = _default_scale(d) if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
-    fn(q, k, v, o, lse, scale, causal, blockmask, stream)
+    if window is None and alibi_slopes is None:
+        fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+        fn(q, k, v, o, lse, scale, causal, blockmask, stream)
+    else:
+        fn = fa_fwd_ex if q.dtype == torch.bfloat16 else fa_fwd_f32_ex
+        fn(q, k, v, o, lse, scale, causal, blockmask, window, alibi_slopes, stream)
     return o, lse
 
 
@@ -202,14 +285,18 @@ def workspace(B: int, H: int, N: int, d: int, device):
 
 
 def backward(q, k, v, o, do, lse, scale: Optional[float] = None, causal: bool = False, blockmask=None,
-             ws=None, stream=None):
-    """Returns (dq, dk, dv).  bf16 inputs use fa_bwd, float32 inputs fa_bwd_f32."""
+             ws=None, stream=None, window=None, alibi_slopes=None):
+    """Returns (dq, dk, dv).  bf16 inputs use fa_bwd(_ex), float32 inputs fa_bwd_f32(_ex)."""
     import torch
     B, H, N, d = _dims(q)
     scale = _default_scale(d) if scale is None else scale
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if ws is None:
         ws = workspace(B, H, N, d, q.device)
-    fn = fa_bwd if q.dtype == torch.bfloat16 else fa_bwd_f32
-    fn(q, k, v, o, do, lse, dq, dk, dv, scale, causal, blockmask, ws, stream)
+    if window is None and alibi_slopes is None:
+        fn = fa_bwd if q.dtype == torch.bfloat16 else fa_bwd_f32
+        fn(q, k, v, o, do, lse, dq, dk, dv, scale, causal, blockmask, ws, stream)
+    else:
+        fn = fa_bwd_ex if q.dtype == torch.bfloat16 else fa_bwd_f32_ex
+        fn(q, k, v, o, do, lse, dq, dk, dv, scale, causal, blockmask, window, alibi_slopes, ws, stream)
     return dq, dk, dv

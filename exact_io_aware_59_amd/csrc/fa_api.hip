@@ -29,17 +29,37 @@ int check_sizes(int B, int H, int N, int d, float scale, const uint8_t* mask) {
     if (total >= (1LL << 31)) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (mask && N > kMaxMaskN) return FA_ERR_UNSUPPORTED;
+    // the bf16 kernels address one head with 32-bit byte offsets and may form
+    // offsets up to a few hundred rows past N (reads there fall outside the
+    // head's range and return zero): keep that below 2^32
+    if ((long long)(N + 256) * d * 2 >= (1LL << 32)) return FA_ERR_UNSUPPORTED;
     return FA_OK;
+}
+
+// window / ALiBi options: NULL = none; the slopes pointer must be 4-byte aligned
+int check_variant(const fa_variant* var) {
+    if (var && var->alibi_slopes && ((uintptr_t)var->alibi_slopes & 3)) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+template <typename Args>
+void set_variant(Args& a, int H, const fa_variant* var) {
+    a.H = H;
+    a.wl = (var && var->window_left >= 0) ? var->window_left : -1;
+    a.wr = (var && var->window_right >= 0) ? var->window_right : -1;
+    a.slopes = var ? var->alibi_slopes : nullptr;
 }
 
 template <typename T>
 int fwd_common(const T* q, const T* k, const T* v, T* o, float* lse, int B, int H, int N, int d, float scale,
-               int causal, const uint8_t* mask, void* stream, bool bf16) {
+               int causal, const uint8_t* mask, const fa_variant* var, void* stream, bool bf16) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3))
         return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     int st = check_sizes(B, H, N, d, scale, mask);
+    if (st != FA_OK) return st;
+    st = check_variant(var);
     if (st != FA_OK) return st;
     const size_t tb = (size_t)B * H * N * d * sizeof(T), lb = (size_t)B * H * N * sizeof(float);
     if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb) || overlap(lse, lb, o, tb) ||
@@ -54,6 +74,7 @@ int fwd_common(const T* q, const T* k, const T* v, T* o, float* lse, int B, int 
     a.causal = causal;
     a.mask = mask;
     a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+    set_variant(a, H, var);
     a.stream = (hipStream_t)stream;
     hipError_t e = bf16 ? fa::launch_fwd_bf16(a) : fa::launch_fwd_f32(a);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -65,8 +86,8 @@ enum Stage { kAll = 0, kPrep = 1, kMain = 2, kDq = 3 };
 // does not use may be NULL and are not checked.
 template <typename T>
 int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, const float* lse, T* dq, T* dk, T* dv,
-               int B, int H, int N, int d, float scale, int causal, const uint8_t* mask, void* ws, size_t ws_bytes,
-               void* stream, bool bf16, Stage stage) {
+               int B, int H, int N, int d, float scale, int causal, const uint8_t* mask, const fa_variant* var,
+               void* ws, size_t ws_bytes, void* stream, bool bf16, Stage stage) {
     const bool use_qkv = stage != kPrep;
     const bool use_o = stage == kAll || stage == kPrep;
     const bool use_lse = stage == kAll || stage == kPrep;
@@ -85,6 +106,8 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
     if (lse && ((uintptr_t)lse & 3)) return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     int st = check_sizes(B, H, N, d, scale, mask);
+    if (st != FA_OK) return st;
+    st = check_variant(var);
     if (st != FA_OK) return st;
     if (mask && N > kMaxMaskNBwd) return FA_ERR_UNSUPPORTED;
     const size_t tb = (size_t)B * H * N * d * sizeof(T), lb = (size_t)B * H * N * sizeof(float);
@@ -117,6 +140,7 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
     const size_t vec_bytes = align_up((size_t)B * H * N * sizeof(float));
     a.ws_D = (float*)ws;
     a.ws_lse2 = (float*)((char*)ws + vec_bytes);
+    set_variant(a, H, var);
     a.stream = (hipStream_t)stream;
     hipError_t e;
     if (!bf16) e = fa::launch_bwd_f32(a);
@@ -131,15 +155,25 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
 
 extern "C" {
 
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+              float scale, int causal, const uint8_t* blockmask, const fa_variant* variant, void* stream) {
+    return fwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, B,
+                                H, N, d, scale, causal, blockmask, variant, stream, true);
+}
+
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
            float scale, int causal, const uint8_t* blockmask, void* stream) {
-    return fwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, B,
-                                H, N, d, scale, causal, blockmask, stream, true);
+    return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, nullptr, stream);
+}
+
+int fa_fwd_f32_ex(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
+                  float scale, int causal, const uint8_t* blockmask, const fa_variant* variant, void* stream) {
+    return fwd_common<float>(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, variant, stream, false);
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
                float scale, int causal, const uint8_t* blockmask, void* stream) {
-    return fwd_common<float>(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, stream, false);
+    return fa_fwd_f32_ex(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, nullptr, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
@@ -148,42 +182,71 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
     return 2 * align_up(rows * sizeof(float));
 }
 
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
+              void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+              const fa_variant* variant, void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+                                (const uint16_t*)dO, lse, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, B, H, N, d,
+                                scale, causal, blockmask, variant, workspace, workspace_bytes, stream, true, kAll);
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
            void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
            void* workspace, size_t workspace_bytes, void* stream) {
-    return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
-                                (const uint16_t*)dO, lse, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, B, H, N, d,
-                                scale, causal, blockmask, workspace, workspace_bytes, stream, true, kAll);
+    return fa_bwd_ex(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, blockmask, nullptr, workspace,
+                     workspace_bytes, stream);
 }
 
 int fa_bwd_prep(const void* o, const void* dO, const float* lse, int B, int H, int N, int d, void* workspace,
                 size_t workspace_bytes, void* stream) {
     return bwd_common<uint16_t>(nullptr, nullptr, nullptr, (const uint16_t*)o, (const uint16_t*)dO, lse,
-                                nullptr, nullptr, nullptr, B, H, N, d, 1.0f, 0, nullptr, workspace, workspace_bytes,
-                                stream, true, kPrep);
+                                nullptr, nullptr, nullptr, B, H, N, d, 1.0f, 0, nullptr, nullptr, workspace,
+                                workspace_bytes, stream, true, kPrep);
+}
+
+int fa_bwd_main_ex(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv, int B, int H,
+                   int N, int d, float scale, int causal, const uint8_t* blockmask, const fa_variant* variant,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, nullptr,
+                                (const uint16_t*)dO, nullptr, nullptr, (uint16_t*)dk, (uint16_t*)dv, B, H, N, d, scale,
+                                causal, blockmask, variant, workspace, workspace_bytes, stream, true, kMain);
 }
 
 int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv, int B, int H, int N,
                 int d, float scale, int causal, const uint8_t* blockmask, void* workspace, size_t workspace_bytes,
                 void* stream) {
+    return fa_bwd_main_ex(q, k, v, dO, dk, dv, B, H, N, d, scale, causal, blockmask, nullptr, workspace,
+                          workspace_bytes, stream);
+}
+
+int fa_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO, void* dq, int B, int H, int N, int d,
+                 float scale, int causal, const uint8_t* blockmask, const fa_variant* variant, void* workspace,
+                 size_t workspace_bytes, void* stream) {
     return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, nullptr,
-                                (const uint16_t*)dO, nullptr, nullptr, (uint16_t*)dk, (uint16_t*)dv, B, H, N, d, scale,
-                                causal, blockmask, workspace, workspace_bytes, stream, true, kMain);
+                                (const uint16_t*)dO, nullptr, (uint16_t*)dq, nullptr, nullptr, B, H, N, d, scale,
+                                causal, blockmask, variant, workspace, workspace_bytes, stream, true, kDq);
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void* dq, int B, int H, int N, int d,
               float scale, int causal, const uint8_t* blockmask, void* workspace, size_t workspace_bytes,
               void* stream) {
-    return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, nullptr,
-                                (const uint16_t*)dO, nullptr, (uint16_t*)dq, nullptr, nullptr, B, H, N, d, scale,
-                                causal, blockmask, workspace, workspace_bytes, stream, true, kDq);
+    return fa_bwd_dq_ex(q, k, v, dO, dq, B, H, N, d, scale, causal, blockmask, nullptr, workspace, workspace_bytes,
+                        stream);
+}
+
+int fa_bwd_f32_ex(const float* q, const float* k, const float* v, const float* o, const float* dO, const float* lse,
+                  float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+                  const uint8_t* blockmask, const fa_variant* variant, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    return bwd_common<float>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, blockmask, variant,
+                             workspace, workspace_bytes, stream, false, kAll);
 }
 
 int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dO, const float* lse,
                float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
                const uint8_t* blockmask, void* workspace, size_t workspace_bytes, void* stream) {
-    return bwd_common<float>(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, blockmask, workspace,
-                             workspace_bytes, stream, false, kAll);
+    return fa_bwd_f32_ex(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, blockmask, nullptr, workspace,
+                         workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {

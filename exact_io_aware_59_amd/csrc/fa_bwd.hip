@@ -108,12 +108,14 @@ __device__ __forceinline__ void mfma32_acc(f32x16& d, bf16x8 a, bf16x8 b) { d = 
 template <int E, int S>
 constexpr int slot_first(int j) { return (j * E + S - 1) / S; }
 
-template <int D, bool CAUSAL, bool MASK>
+// VAR: local window and/or ALiBi (every step takes the masked path, P gets the bias).
+template <int D, bool CAUSAL, bool MASK, bool VAR>
 __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float c, float scale,
-    const uint8_t* __restrict__ mask, int nb, int nkb, int BH) {
+    const uint8_t* __restrict__ mask, int nb, int nkb, int BH, int H, int wl, int wr,
+    const float* __restrict__ slopes) {
     using C = BwdCfg<D>;
     // three-deep ring of query tiles (Q then dO): tile t+2 streams in while t and
     // t+1 are read.  Rows are unpadded; 16-byte chunk c of row r sits at chunk
@@ -158,19 +160,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
             vneg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off + 32 * kk) ^ 0x80008000u);
         }
     }
-    // ---- the query tiles to visit ----
+    // ---- the query tiles to visit: queries [q_lo, q_hi) can see this key block ----
+    Variant var{wl, wr, 0.f};
+    if (VAR && slopes != nullptr) var.slope2 = slopes[bh % H] * kLog2e;
+    int q_lo = CAUSAL ? k0 : 0, q_hi = N;
+    if (VAR) {
+        int lo, hi;
+        var.query_range(k0, min(N, k0 + kBck), N, lo, hi);
+        q_lo = max(q_lo, lo);
+        q_hi = min(q_hi, hi);
+    }
     int nsteps, n_masked;
     int q_first = 0;
     const bool key_tail = k0 + kBck > N;
     if (MASK) {
-        const int lo = CAUSAL ? kb : 0;
-        const int cnt = build_block_list<kWaves>(mask + kb, (size_t)nb, lo, nb - 1, rows_list, wave_cnt);
+        const int lo_blk = q_lo / kMaskBlock;
+        const int hi_blk = q_hi > q_lo ? (q_hi - 1) / kMaskBlock : lo_blk - 1;
+        const int cnt = hi_blk >= lo_blk
+                            ? build_block_list<kWaves>(mask + kb, (size_t)nb, lo_blk, hi_blk, rows_list, wave_cnt)
+                            : 0;
         nsteps = cnt * (kMaskBlock / kBrq);
-        n_masked = key_tail ? nsteps : ((CAUSAL && cnt > 0 && rows_list[0] == kb) ? kMaskBlock / kBrq : 0);
+        n_masked = (VAR || key_tail) ? nsteps
+                                     : ((CAUSAL && cnt > 0 && rows_list[0] == kb) ? kMaskBlock / kBrq : 0);
     } else {
-        q_first = CAUSAL ? k0 : 0;
-        nsteps = (N - q_first + kBrq - 1) / kBrq;
-        n_masked = key_tail ? nsteps : (CAUSAL ? min(nsteps, kBck / kBrq) : 0);
+        q_first = q_lo;
+        nsteps = q_hi > q_lo ? (q_hi - q_first + kBrq - 1) / kBrq : 0;
+        n_masked = (VAR || key_tail) ? nsteps : (CAUSAL ? min(nsteps, kBck / kBrq) : 0);
     }
     // first query of step st; steps past the end map to row N, whose copies
     // fall outside the buffers and fetch nothing
@@ -281,11 +296,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
         // P of half g+1, element r (row 8(r/4) + 4h + r%4 of the half)
         auto probs = [&](auto rc) {
             constexpr int r = decltype(rc)::value;
-            float p = exp2f_hw(__builtin_fmaf(nxt.s[r], c, -lvn[r / 4][r % 4]));
-            if constexpr (MASKED) {
-                const int qi = qn + 8 * (r / 4) + 4 * h + (r % 4);
-                p = ((CAUSAL && my_key > qi) || my_key >= N) ? 0.f : p;
-            }
+            const int qi = qn + 8 * (r / 4) + 4 * h + (r % 4);
+            float z = __builtin_fmaf(nxt.s[r], c, -lvn[r / 4][r % 4]);
+            if constexpr (VAR) z += var.bias2(qi, my_key);
+            float p = exp2f_hw(z);
+            if constexpr (MASKED || VAR)
+                p = ((CAUSAL && my_key > qi) || my_key >= N || (VAR && var.dead(qi, my_key))) ? 0.f : p;
             nxt.s[r] = p;
             if constexpr (r % 2 == 1) nxt.pb[r / 8][(r % 8) / 2] = cvt_pk_bf16(nxt.s[r - 1], p);
         };
@@ -368,9 +384,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
         const int q0 = step_q0(0);
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-            float p = exp2f_hw(__builtin_fmaf(X.s[r], c, -l4[r / 4][r % 4]));
             const int qi = q0 + 8 * (r / 4) + 4 * h + (r % 4);
-            p = ((CAUSAL && my_key > qi) || my_key >= N) ? 0.f : p;
+            float z = __builtin_fmaf(X.s[r], c, -l4[r / 4][r % 4]);
+            if constexpr (VAR) z += var.bias2(qi, my_key);
+            float p = exp2f_hw(z);
+            p = ((CAUSAL && my_key > qi) || my_key >= N || (VAR && var.dead(qi, my_key))) ? 0.f : p;
             X.s[r] = p;
         }
 #pragma unroll
@@ -458,12 +476,12 @@ __device__ __forceinline__ void dq_load_tile(rsrc_t r, bf16* tile, int kv0, int 
     }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool VAR>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
     bf16* __restrict__ dQ, int N, float c, float scale, const uint8_t* __restrict__ mask, int nb, int nqb,
-    int n_items) {
+    int n_items, int H, int wl, int wr, const float* __restrict__ slopes) {
     using C = DqCfg<D>;
     __shared__ __attribute__((aligned(1024))) bf16 kbuf0[C::KTILE];
     __shared__ __attribute__((aligned(1024))) bf16 kbuf1[C::KTILE];
@@ -503,6 +521,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const rsrc_t rdq = make_rsrc(dQ + head_off, head_bytes);
     const rsrc_t rl = make_rsrc(LSE2 + (size_t)bh * N, (uint32_t)N * 4);
     const rsrc_t rd = make_rsrc(Dv + (size_t)bh * N, (uint32_t)N * 4);
+    Variant var{wl, wr, 0.f};
+    if (VAR && slopes != nullptr) var.slope2 = slopes[bh % H] * kLog2e;
 
     for (int bi = 0; bi < nblk; bi++) {
         const int qb = qblk[bi];
@@ -513,17 +533,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         int ntiles;
         const uint16_t* cols = nullptr;
         const int q_end = min(N, q0 + kDqBr);
+        int k_lo = 0, k_hi = CAUSAL ? q_end : N;  // keys this block can see
+        if (VAR) {
+            int lo, hi;
+            var.key_range(q0, q_end, N, lo, hi);
+            k_lo = lo;
+            k_hi = min(k_hi, hi);
+        }
+        int k_first = 0;
         if (MASK) {
-            const int max_col = CAUSAL ? (q_end - 1) / kMaskBlock : nb - 1;
-            const int cnt = build_block_list<kWaves>(mask + (size_t)qb * nb, 1, 0, max_col, mask_cols, wave_cnt);
+            const int lo_col = k_lo / kMaskBlock;
+            const int max_col = k_hi > k_lo ? (k_hi - 1) / kMaskBlock : lo_col - 1;
+            const int cnt = max_col >= lo_col ? build_block_list<kWaves>(mask + (size_t)qb * nb, 1, lo_col, max_col,
+                                                                        mask_cols, wave_cnt)
+                                              : 0;
             cols = mask_cols;
             ntiles = cnt * (kMaskBlock / C::BC);
         } else {
-            ntiles = ((CAUSAL ? q_end : N) + C::BC - 1) / C::BC;
+            k_first = k_lo;
+            ntiles = k_hi > k_lo ? (k_hi - k_first + C::BC - 1) / C::BC : 0;
         }
         auto kv0_of = [&](int it) -> int {
             if (MASK) return cols[it / (kMaskBlock / C::BC)] * kMaskBlock + (it % (kMaskBlock / C::BC)) * C::BC;
-            return it * C::BC;
+            return k_first + it * C::BC;
         };
 
         // this lane's query: Q and dO fragments (B operands, k = head dim, n = query), lse2 and D
@@ -560,7 +592,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                 dq_load_tile<D, C::KS, C::KSEGS>(rk, P ? kbuf0 : kbuf1, kv0_of(it + 1), wave, lane);
                 dq_load_tile<D, C::VS, C::VSEGS>(rv, P ? vbuf0 : vbuf1, kv0_of(it + 1), wave, lane);
             }
-            const bool need_mask = (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N);
+            const bool need_mask = VAR || (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N);
             // two 32-key halves, software-pipelined as in the key-outer kernel
             f32x16 s[2], dp[2];
             auto scores = [&](int kb) {  // S^T and dP^T for 32 keys (keys x queries)
@@ -576,11 +608,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             auto probs = [&](int kb) {  // P = 2^(c s - lse2), dS = P (dP - D)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    float p = exp2f_hw(__builtin_fmaf(s[kb][r], c, ml2));
-                    if (need_mask) {
-                        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        p = ((CAUSAL && key > my_q) || key >= N) ? 0.f : p;
-                    }
+                    const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    float z = __builtin_fmaf(s[kb][r], c, ml2);
+                    if constexpr (VAR) z += var.bias2(my_q, key);
+                    float p = exp2f_hw(z);
+                    if (need_mask)
+                        p = ((CAUSAL && key > my_q) || key >= N || (VAR && var.dead(my_q, key))) ? 0.f : p;
                     dp[kb][r] = p * (dp[kb][r] - dd);
                 }
                 sb[kb][0] = pack8<0>(dp[kb]);
@@ -624,36 +657,36 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool VAR>
 hipError_t launch_dq(const BwdArgs& a) {
     const int nqb = (a.N + kDqBr - 1) / kDqBr;
     const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
     const int n_items = a.BH * per_head;
     const size_t dyn = MASK ? (size_t)a.nb * sizeof(uint16_t) : 0;
-    auto kern = bwd_dq_kernel<D, CAUSAL, MASK>;
+    auto kern = bwd_dq_kernel<D, CAUSAL, MASK, VAR>;
     if (dyn > 0) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads), dyn, a.stream, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (const bf16*)a.dO, a.ws_lse2, a.ws_D, (bf16*)a.dq, a.N,
-                       a.scale * kLog2e, a.scale, a.mask, a.nb, nqb, n_items);
+                       a.scale * kLog2e, a.scale, a.mask, a.nb, nqb, n_items, a.H, a.wl, a.wr, a.slopes);
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool VAR>
 hipError_t launch_main(const BwdArgs& a) {
     const int nkb = (a.N + kBck - 1) / kBck;
     const int n_items = a.BH * nkb;
     const size_t dyn = MASK ? (size_t)a.nb * sizeof(uint16_t) : 0;
-    auto kern = bwd_bf16_kernel<D, CAUSAL, MASK>;
+    auto kern = bwd_bf16_kernel<D, CAUSAL, MASK, VAR>;
     if (dyn > 0) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads), dyn, a.stream, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (const bf16*)a.dO, a.ws_lse2, a.ws_D, (bf16*)a.dk, (bf16*)a.dv,
-                       a.N, a.scale * kLog2e, a.scale, a.mask, a.nb, nkb, a.BH);
+                       a.N, a.scale * kLog2e, a.scale, a.mask, a.nb, nkb, a.BH, a.H, a.wl, a.wr, a.slopes);
     return hipGetLastError();
 }
 
@@ -666,11 +699,18 @@ hipError_t launch_prep(const BwdArgs& a) {
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool VAR>
 hipError_t launch_main_all(const BwdArgs& a) {
     const bool m = a.mask != nullptr;
-    if (a.causal) return m ? launch_main<D, true, true>(a) : launch_main<D, true, false>(a);
-    return m ? launch_main<D, false, true>(a) : launch_main<D, false, false>(a);
+    if (a.causal) return m ? launch_main<D, true, true, VAR>(a) : launch_main<D, true, false, VAR>(a);
+    return m ? launch_main<D, false, true, VAR>(a) : launch_main<D, false, false, VAR>(a);
+}
+
+template <int D, bool VAR>
+hipError_t launch_dq_all(const BwdArgs& a) {
+    const bool m = a.mask != nullptr;
+    if (a.causal) return m ? launch_dq<D, true, true, VAR>(a) : launch_dq<D, true, false, VAR>(a);
+    return m ? launch_dq<D, false, true, VAR>(a) : launch_dq<D, false, false, VAR>(a);
 }
 
 }  // namespace
@@ -680,17 +720,13 @@ hipError_t launch_bwd_prep_bf16(const BwdArgs& a) {
 }
 
 hipError_t launch_bwd_main_bf16(const BwdArgs& a) {
-    return a.d == 128 ? launch_main_all<128>(a) : launch_main_all<64>(a);
+    if (a.variant()) return a.d == 128 ? launch_main_all<128, true>(a) : launch_main_all<64, true>(a);
+    return a.d == 128 ? launch_main_all<128, false>(a) : launch_main_all<64, false>(a);
 }
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
-    const bool m = a.mask != nullptr;
-    if (a.d == 128) {
-        if (a.causal) return m ? launch_dq<128, true, true>(a) : launch_dq<128, true, false>(a);
-        return m ? launch_dq<128, false, true>(a) : launch_dq<128, false, false>(a);
-    }
-    if (a.causal) return m ? launch_dq<64, true, true>(a) : launch_dq<64, true, false>(a);
-    return m ? launch_dq<64, false, true>(a) : launch_dq<64, false, false>(a);
+    if (a.variant()) return a.d == 128 ? launch_dq_all<128, true>(a) : launch_dq_all<64, true>(a);
+    return a.d == 128 ? launch_dq_all<128, false>(a) : launch_dq_all<64, false>(a);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a) {

@@ -237,6 +237,32 @@ __device__ __forceinline__ uint32_t lds_addr_of(const T* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
 }
 
+// Local window and ALiBi of one head ("FlashAttention 深度解析" section 五
+// names both as built-in variants beside the causal mask): key j is allowed
+// for query i iff i - wl <= j <= i + wr (a negative bound is unbounded), and
+// the score of (i, j) gets -slope |i - j|; `slope2` is slope * log2(e).
+struct Variant {
+    int wl, wr;
+    float slope2;
+    __device__ __forceinline__ bool dead(int i, int j) const {
+        return (wl >= 0 && j < i - wl) || (wr >= 0 && j > i + wr);
+    }
+    // bias in log2 units
+    __device__ __forceinline__ float bias2(int i, int j) const {
+        return -slope2 * (float)(i > j ? i - j : j - i);
+    }
+    // keys [lo, hi) a block of queries [q_lo, q_hi) can see, within [0, n)
+    __device__ __forceinline__ void key_range(int q_lo, int q_hi, int n, int& lo, int& hi) const {
+        lo = wl >= 0 ? max(0, q_lo - wl) : 0;
+        hi = wr >= 0 ? min(n, q_hi - 1 + wr + 1) : n;
+    }
+    // queries [lo, hi) a block of keys [k_lo, k_hi) is seen by, within [0, n)
+    __device__ __forceinline__ void query_range(int k_lo, int k_hi, int n, int& lo, int& hi) const {
+        lo = wr >= 0 ? max(0, k_lo - wr) : 0;
+        hi = wl >= 0 ? min(n, k_hi - 1 + wl + 1) : n;
+    }
+};
+
 // Workgroup id -> logical work item such that consecutive logical items land
 // on the same XCD (the hardware deals workgroups round-robin over the 8 XCDs),
 // so tiles of one (batch, head) share that XCD's L2.

@@ -13,18 +13,26 @@
 namespace fa {
 namespace {
 
-__device__ __forceinline__ bool allowed(int i, int j, int causal, const uint8_t* mask, int nb) {
+__device__ __forceinline__ bool allowed(int i, int j, int causal, const uint8_t* mask, int nb, const Variant& var) {
     if (causal && j > i) return false;
     if (mask && !mask[(size_t)(i / kMaskBlock) * nb + (j / kMaskBlock)]) return false;
+    if (var.dead(i, j)) return false;
     return true;
+}
+
+// window / ALiBi parameters of head bh
+__device__ __forceinline__ Variant variant_of(int bh, int H, int wl, int wr, const float* slopes) {
+    return Variant{wl, wr, slopes ? slopes[bh % H] * kLog2e : 0.f};
 }
 
 template <int D>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                      const float* __restrict__ V, float* __restrict__ O,
                                                      float* __restrict__ LSE, int N, float c, int causal,
-                                                     const uint8_t* __restrict__ mask, int nb) {
+                                                     const uint8_t* __restrict__ mask, int nb, int H, int wl, int wr,
+                                                     const float* __restrict__ slopes) {
     const int bh = blockIdx.y;
+    const Variant var = variant_of(bh, H, wl, wr, slopes);
     const int i = blockIdx.x * 64 + threadIdx.x;
     const size_t head = (size_t)bh * N * D;
     const bool row_ok = i < N;
@@ -46,8 +54,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < D; e++) s = __builtin_fmaf(q[e], kj[e], s);
-        if (!row_ok || !allowed(i, j, causal, mask, nb)) continue;
-        const float t = s * c;
+        if (!row_ok || !allowed(i, j, causal, mask, nb, var)) continue;
+        const float t = __builtin_fmaf(s, c, var.bias2(i, j));
         const float m_new = fmaxf(m, t);
         const float alpha = (m == -INFINITY) ? 0.f : exp2f_hw(m - m_new);
         const float p = exp2f_hw(t - m_new);
@@ -81,8 +89,10 @@ __global__ __launch_bounds__(64) void dq_f32_kernel(const float* __restrict__ Q,
                                                     const float* __restrict__ V, const float* __restrict__ dO,
                                                     const float* __restrict__ LSE, const float* __restrict__ Dv,
                                                     float* __restrict__ dQ, int N, float c, float scale, int causal,
-                                                    const uint8_t* __restrict__ mask, int nb) {
+                                                    const uint8_t* __restrict__ mask, int nb, int H, int wl, int wr,
+                                                    const float* __restrict__ slopes) {
     const int bh = blockIdx.y;
+    const Variant var = variant_of(bh, H, wl, wr, slopes);
     const int i = blockIdx.x * 64 + threadIdx.x;
     if (i >= N) return;
     const size_t head = (size_t)bh * N * D;
@@ -96,7 +106,7 @@ __global__ __launch_bounds__(64) void dq_f32_kernel(const float* __restrict__ Q,
         acc[e] = 0.f;
     }
     for (int j = 0; j < N; j++) {
-        if (!allowed(i, j, causal, mask, nb)) continue;
+        if (!allowed(i, j, causal, mask, nb, var)) continue;
         const float* kj = K + head + (size_t)j * D;
         const float* vj = V + head + (size_t)j * D;
         float s = 0.f, dp = 0.f;
@@ -105,7 +115,7 @@ __global__ __launch_bounds__(64) void dq_f32_kernel(const float* __restrict__ Q,
             s = __builtin_fmaf(q[e], kj[e], s);
             dp = __builtin_fmaf(g[e], vj[e], dp);
         }
-        const float p = exp2f_hw(__builtin_fmaf(s, c, -lse2));
+        const float p = exp2f_hw(__builtin_fmaf(s, c, -lse2) + var.bias2(i, j));
         const float ds = p * (dp - Di);
 #pragma unroll
         for (int e = 0; e < D; e++) acc[e] = __builtin_fmaf(ds, kj[e], acc[e]);
@@ -121,9 +131,10 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ LSE, const float* __restrict__ Dv,
                                                       float* __restrict__ dK, float* __restrict__ dV, int N, float c,
                                                       float scale, int causal, const uint8_t* __restrict__ mask,
-                                                      int nb) {
+                                                      int nb, int H, int wl, int wr, const float* __restrict__ slopes) {
     __shared__ float kv[2][64][D + 1];  // this block's k and v rows (padded against bank conflicts)
     const int bh = blockIdx.y;
+    const Variant var = variant_of(bh, H, wl, wr, slopes);
     const int j0 = blockIdx.x * 64;
     const int t = threadIdx.x;
     const int j = j0 + t;
@@ -141,7 +152,7 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(const float* __restrict__ 
     for (int e = 0; e < D; e++) gk[e] = gv[e] = 0.f;
     const int i_start = causal ? j0 : 0;
     for (int i = i_start; i < N; i++) {
-        if (j >= N || !allowed(i, j, causal, mask, nb)) continue;
+        if (j >= N || !allowed(i, j, causal, mask, nb, var)) continue;
         const float* qi = Q + head + (size_t)i * D;
         const float* gi = dO + head + (size_t)i * D;
         float s = 0.f, dp = 0.f;
@@ -149,7 +160,7 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(const float* __restrict__ 
             s = __builtin_fmaf(qi[e], kv[0][t][e], s);
             dp = __builtin_fmaf(gi[e], kv[1][t][e], dp);
         }
-        const float p = exp2f_hw(__builtin_fmaf(s, c, -LSE[(size_t)bh * N + i] * kLog2e));
+        const float p = exp2f_hw(__builtin_fmaf(s, c, -LSE[(size_t)bh * N + i] * kLog2e) + var.bias2(i, j));
         const float ds = p * (dp - Dv[(size_t)bh * N + i]);
 #pragma unroll
         for (int e = 0; e < D; e++) {
@@ -169,7 +180,8 @@ template <int D>
 hipError_t fwd_f32(const FwdArgs& a) {
     dim3 grid((a.N + 63) / 64, a.BH);
     hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(64), 0, a.stream, (const float*)a.q, (const float*)a.k,
-                       (const float*)a.v, (float*)a.o, a.lse, a.N, a.scale * kLog2e, a.causal, a.mask, a.nb);
+                       (const float*)a.v, (float*)a.o, a.lse, a.N, a.scale * kLog2e, a.causal, a.mask, a.nb,
+                       a.H, a.wl, a.wr, a.slopes);
     return hipGetLastError();
 }
 
@@ -184,12 +196,12 @@ hipError_t bwd_f32(const BwdArgs& a) {
     const float c = a.scale * kLog2e;
     hipLaunchKernelGGL(dq_f32_kernel<D>, grid, dim3(64), 0, a.stream, (const float*)a.q, (const float*)a.k,
                        (const float*)a.v, (const float*)a.dO, a.lse, a.ws_D, (float*)a.dq, a.N, c, a.scale,
-                       a.causal, a.mask, a.nb);
+                       a.causal, a.mask, a.nb, a.H, a.wl, a.wr, a.slopes);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(dkdv_f32_kernel<D>, grid, dim3(64), 0, a.stream, (const float*)a.q, (const float*)a.k,
                        (const float*)a.v, (const float*)a.dO, a.lse, a.ws_D, (float*)a.dk, (float*)a.dv, a.N, c,
-                       a.scale, a.causal, a.mask, a.nb);
+                       a.scale, a.causal, a.mask, a.nb, a.H, a.wl, a.wr, a.slopes);
     return hipGetLastError();
 }
 

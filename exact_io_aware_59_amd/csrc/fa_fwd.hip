@@ -65,9 +65,10 @@ struct TileList {
     int n;                  // number of tiles
     int tpb;                // tiles per mask block (mask mode)
     int bc;
+    int first;              // dense mode: index of the first tile
     const uint16_t* cols;   // mask mode: allowed mask columns (LDS)
     __device__ __forceinline__ int kv0(int it) const {
-        if (cols == nullptr) return it * bc;
+        if (cols == nullptr) return (first + it) * bc;
         return cols[it / tpb] * kMaskBlock + (it % tpb) * bc;
     }
 };
@@ -106,6 +107,22 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[FwdCfg<D>::NKB], int kv0
         }
 }
 
+// Local window / ALiBi variant: scores to log2 units with the bias added,
+// z = cs * s - slope2 |i - j|, and -inf outside the causal range, the window or N.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void variant_scores(f32x16 (&s)[FwdCfg<D>::NKB], int kv0, int my_q, int N, int h,
+                                               float cs, const Variant& var) {
+    using C = FwdCfg<D>;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; kb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+            const bool dead = (CAUSAL && key > my_q) || key >= N || var.dead(my_q, key);
+            s[kb][r] = dead ? -INFINITY : __builtin_fmaf(s[kb][r], cs, var.bias2(my_q, key));
+        }
+}
+
 template <int D>
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[FwdCfg<D>::NKB]) {
     using C = FwdCfg<D>;
@@ -141,11 +158,15 @@ __device__ __forceinline__ void tile_pv(const bf16* vl, const bf16x8 (&pb)[FwdCf
             o[dm] = mfma32(lds_tr_operand_pad<C::VS>(vl, 16 * t, 32 * dm), pb[t], o[dm]);
 }
 
-template <int D, bool CAUSAL, bool MASK>
+// VAR: local window and/or ALiBi.  Every tile's scores are then taken to log2
+// units with the bias (variant_scores) and the kernel runs with c = 1; `cs` is
+// the true |scale| log2(e).
+template <int D, bool CAUSAL, bool MASK, bool VAR>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, float c, uint32_t qsign,
-    const uint8_t* __restrict__ mask, int nb, int nqb, int n_items) {
+    const uint8_t* __restrict__ mask, int nb, int nqb, int n_items, int H, int wl, int wr,
+    const float* __restrict__ slopes, float cs) {
     using C = FwdCfg<D>;
     // four separate arrays (not one 2-D array) so that alias analysis can tell
     // the tile being read from the tile the DMA is filling
@@ -185,6 +206,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const rsrc_t rv = make_rsrc(V + head_off, head_bytes);
     const rsrc_t ro = make_rsrc(O + head_off, head_bytes);
     const rsrc_t rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
+    Variant var{wl, wr, 0.f};
+    if (VAR && slopes != nullptr) var.slope2 = slopes[bh % H] * kLog2e;
 
     for (int bi = 0; bi < nblk; bi++) {
         const int qb = qblk[bi];
@@ -196,16 +219,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         TileList tl;
         tl.bc = C::BC;
         tl.tpb = kMaskBlock / C::BC;
+        tl.first = 0;
         tl.cols = nullptr;
         const int q_end = min(N, q0 + kBr);  // one past the last query of the block
+        int kv_lo = 0, kv_hi = CAUSAL ? q_end : N;  // keys this block can see
+        if (VAR) {
+            int lo, hi;
+            var.key_range(q0, q_end, N, lo, hi);
+            kv_lo = lo;
+            kv_hi = min(kv_hi, hi);
+        }
         if (MASK) {
-            const int max_col = CAUSAL ? (q_end - 1) / kMaskBlock : nb - 1;
-            const int cnt = build_block_list<kWaves>(mask + (size_t)qb * nb, 1, 0, max_col, mask_cols, wave_cnt);
+            const int lo_col = kv_lo / kMaskBlock;
+            const int max_col = kv_hi > kv_lo ? (kv_hi - 1) / kMaskBlock : lo_col - 1;
+            const int cnt = max_col >= lo_col
+                                ? build_block_list<kWaves>(mask + (size_t)qb * nb, 1, lo_col, max_col, mask_cols,
+                                                           wave_cnt)
+                                : 0;
             tl.cols = mask_cols;
             tl.n = cnt * tl.tpb;
         } else {
-            const int kv_end = CAUSAL ? q_end : N;
-            tl.n = (kv_end + C::BC - 1) / C::BC;
+            tl.first = kv_lo / C::BC;
+            tl.n = kv_hi > kv_lo ? (kv_hi + C::BC - 1) / C::BC - tl.first : 0;
         }
 
         // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
@@ -238,7 +273,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         if (tl.n > 0) {
             const int kv0 = tl.kv0(0);
             tile_scores<D>(kbuf0 + k_lane, qf, sa);
-            if (needs_mask(kv0)) mask_scores<D, CAUSAL>(sa, kv0, my_q, N, h);
+            if constexpr (VAR) variant_scores<D, CAUSAL>(sa, kv0, my_q, N, h, cs, var);
+            else if (needs_mask(kv0)) mask_scores<D, CAUSAL>(sa, kv0, my_q, N, h);
             mx_cur = tile_max<D>(sa);
         }
         __syncthreads();  // every wave is done with kbuf0 before K2 overwrites it
@@ -305,7 +341,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             // ---- phase B: O^T += V^T P^T for tile it; mask and max of tile it+1 ----
             tile_pv<D>(v_this + v_lane, pb, oacc);
             if (has_next) {
-                if (needs_mask(kv1)) mask_scores<D, CAUSAL>(sn, kv1, my_q, N, h);
+                if constexpr (VAR) variant_scores<D, CAUSAL>(sn, kv1, my_q, N, h, cs, var);
+                else if (needs_mask(kv1)) mask_scores<D, CAUSAL>(sn, kv1, my_q, N, h);
                 mx_cur = tile_max<D>(sn);
             }
             wait_vmem();
@@ -339,13 +376,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool VAR>
 hipError_t launch(const FwdArgs& a) {
     const int nqb = (a.N + kBr - 1) / kBr;
     const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
     const int n_items = a.BH * per_head;
     const size_t dyn = MASK ? (size_t)a.nb * sizeof(uint16_t) : 0;
-    auto kern = fwd_bf16_kernel<D, CAUSAL, MASK>;
+    auto kern = fwd_bf16_kernel<D, CAUSAL, MASK, VAR>;
     if (dyn > 0) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
@@ -355,20 +392,22 @@ hipError_t launch(const FwdArgs& a) {
     const float c = a.c < 1e-30f ? 1e-30f : a.c;
     hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads), dyn, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.N,
-                       c, a.qsign, a.mask, a.nb, nqb, n_items);
+                       VAR ? 1.0f : c, a.qsign, a.mask, a.nb, nqb, n_items, a.H, a.wl, a.wr, a.slopes, c);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a) {
+template <int D, bool VAR>
+hipError_t launch_d(const FwdArgs& a) {
     const bool m = a.mask != nullptr;
-    if (a.d == 128) {
-        if (a.causal) return m ? launch<128, true, true>(a) : launch<128, true, false>(a);
-        return m ? launch<128, false, true>(a) : launch<128, false, false>(a);
-    }
-    if (a.causal) return m ? launch<64, true, true>(a) : launch<64, true, false>(a);
-    return m ? launch<64, false, true>(a) : launch<64, false, false>(a);
+    if (a.causal) return m ? launch<D, true, true, VAR>(a) : launch<D, true, false, VAR>(a);
+    return m ? launch<D, false, true, VAR>(a) : launch<D, false, false, VAR>(a);
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a) {
+    if (a.variant()) return a.d == 128 ? launch_d<128, true>(a) : launch_d<64, true>(a);
+    return a.d == 128 ? launch_d<128, false>(a) : launch_d<64, false>(a);
 }
 
 }  // namespace fa

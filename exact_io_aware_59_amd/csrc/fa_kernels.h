@@ -22,7 +22,12 @@ struct FwdArgs {
     int causal;
     const uint8_t* mask;
     int nb;           // ceil(N / 128)
+    // local window and ALiBi: key j allowed for query i iff i - wl <= j <= i + wr
+    // (negative = unbounded); score += -slopes[h] |i - j| (slopes may be null)
+    int H, wl, wr;
+    const float* slopes;
     hipStream_t stream;
+    bool variant() const { return wl >= 0 || wr >= 0 || slopes != nullptr; }
 };
 
 struct BwdArgs {
@@ -42,7 +47,10 @@ struct BwdArgs {
     int nb;
     float* ws_D;      // [BH*N] fp32: D_i = rowsum(dO o O)
     float* ws_lse2;   // [BH*N] fp32: lse in log2 units (+inf for rows without keys)
+    int H, wl, wr;    // local window and ALiBi, as in FwdArgs
+    const float* slopes;
     hipStream_t stream;
+    bool variant() const { return wl >= 0 || wr >= 0 || slopes != nullptr; }
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);

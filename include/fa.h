@@ -13,8 +13,9 @@
  * section 3.2; IO-Awareness page section 2.5).
  *
  * Definition computed (per batch b, head h, row i):
- *   S_ij  = scale * sum_c q_ic k_jc
+ *   S_ij  = scale * sum_c q_ic k_jc   (- alibi_slope_h |i - j| with ALiBi, see fa_variant)
  *   allowed(i, j) = (!causal || j <= i) && (blockmask == NULL || blockmask[i/128][j/128] != 0)
+ *                   && (inside the local window, if one is given: see fa_variant)
  *   lse_i = log sum_{allowed j} exp(S_ij)         (natural log; -inf if no j is allowed)
  *   O_i   = sum_{allowed j} exp(S_ij - lse_i) v_j (0 if no j is allowed)
  * The causal mask is the lower triangle including the diagonal ("FlashAttention
@@ -41,8 +42,9 @@
  *           synchronized.  Kernel faults surface at the caller's next sync.
  * Limits    B, H, N >= 1; d in {64, 128} (the pages allow any multiple of 16 up
  *           to 256; other values return FA_ERR_UNSUPPORTED); B*H*N*d < 2^31;
- *           scale finite; with a blockmask, N <= 4194304 (forward) and
- *           N <= 524288 (backward).
+ *           (N + 256) * d * 2 < 2^32 (else FA_ERR_UNSUPPORTED: the kernels
+ *           address one head with 32-bit byte offsets); scale finite; with a
+ *           blockmask, N <= 4194304 (forward) and N <= 524288 (backward).
  * Errors    arguments are validated before anything is enqueued; on any
  *           error nothing is enqueued and the outputs are untouched.
  *           FA_ERR_HIP reports a failed kernel launch (hipGetLastError).
@@ -67,7 +69,28 @@ typedef enum {
 } fa_status;
 
 #define FA_MASK_BLOCK 128 /* block-mask granularity in rows and columns */
-#define FA_VERSION 1
+#define FA_VERSION 2
+
+/*
+ * Local window and ALiBi, the two further built-in variants "FlashAttention
+ * 深度解析" section 五 lists beside the causal mask (the pages give no formula;
+ * the definition taken here):
+ *   window_left, window_right: key j is allowed for query i only if
+ *       i - window_left <= j <= i + window_right; a negative value leaves that
+ *       side unbounded.  Intersected with causal and the block mask.
+ *   alibi_slopes: device float[H] (4-byte aligned) or NULL; the scaled score of
+ *       (i, j) in head h becomes S_ij - alibi_slopes[h] * |i - j|, before the
+ *       softmax (lse includes it).
+ * The struct itself is read on the host during the call (the caller keeps
+ * ownership); passing NULL, or {-1, -1, NULL}, is the plain computation.  The
+ * _ex entry points below take it; the backward must get the variant the
+ * forward used.
+ */
+typedef struct fa_variant {
+    int window_left;
+    int window_right;
+    const float* alibi_slopes;
+} fa_variant;
 
 /*
  * Forward, bfloat16.  q, k, v: const bf16 [B][H][N][d] (read).  o: bf16
@@ -81,6 +104,15 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 /* Forward, float32 tensors; same semantics as fa_fwd. */
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                int N, int d, float scale, int causal, const uint8_t* blockmask, void* stream);
+
+/* fa_fwd / fa_fwd_f32 with a local window and/or ALiBi (variant may be NULL).
+ * A misaligned alibi_slopes pointer returns FA_ERR_INVALID_ARG. */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+              int d, float scale, int causal, const uint8_t* blockmask, const fa_variant* variant,
+              void* stream);
+int fa_fwd_f32_ex(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                  int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+                  const fa_variant* variant, void* stream);
 
 /*
  * Bytes of device workspace fa_bwd and fa_bwd_f32 need: two fp32 row vectors
@@ -133,6 +165,23 @@ int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, c
                const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
                float scale, int causal, const uint8_t* blockmask, void* workspace,
                size_t workspace_bytes, void* stream);
+
+/* The backward entry points with a local window and/or ALiBi (variant may be
+ * NULL); the variant must be the one the forward used.  fa_bwd_prep needs none. */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dO,
+              const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+              float scale, int causal, const uint8_t* blockmask, const fa_variant* variant,
+              void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_main_ex(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+                   const fa_variant* variant, void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO, void* dq, int B, int H,
+                 int N, int d, float scale, int causal, const uint8_t* blockmask,
+                 const fa_variant* variant, void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_f32_ex(const float* q, const float* k, const float* v, const float* o, const float* dO,
+                  const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                  float scale, int causal, const uint8_t* blockmask, const fa_variant* variant,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status(lib):
-    assert fa.fa_version() == 1
+    assert fa.fa_version() == 2
     for s in range(5):
         assert fa.fa_status_string(s)
     assert fa.fa_status_string(99) == "unknown status"
@@ -76,6 +76,8 @@ def test_fwd_validation(lib):
         assert _fwd(lib, o=P1, f32=f32) == 1  # output aliases q
         assert _fwd(lib, lse=P1 + 3 * BIG + 100, f32=f32) == 1  # lse inside o
         assert _fwd(lib, N=4194305, mask=P9, f32=f32) == 2
+        # a head whose byte offsets (plus tail slack) would not fit 32 bits
+        assert _fwd(lib, N=(1 << 25) - 1, d=64, f32=f32) == 2
 
 
 def _bwd(lib, ws=P9, ws_bytes=None, B=1, H=1, N=128, d=64, dq=P1 + 6 * BIG, dk=P1 + 7 * BIG, dv=P1 + 8 * BIG,
@@ -130,3 +132,25 @@ def test_stage_validation(lib):
                            1, 1, 128, 64, ctypes.c_float(0.1), 0, None, ws, nbytes, None) == 1
     assert lib.fa_bwd_main(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 4 * BIG,
                            1, 1, 128, 64, ctypes.c_float(0.1), 0, None, ws, nbytes, None) == 1  # dk aliases dv
+
+
+def test_variant_validation(lib):
+    """The _ex entry points take a host fa_variant; a misaligned ALiBi slopes pointer is rejected."""
+    bad = ctypes.pointer(fa.Variant(16, 0, P1 + 2))
+    ok = ctypes.pointer(fa.Variant(-1, -1, None))
+    s = ctypes.c_float(0.125)
+    ws = P9 + 16 * BIG
+    nbytes = lib.fa_bwd_workspace_size(1, 1, 128, 64)
+    for fn in (lib.fa_fwd_ex, lib.fa_fwd_f32_ex):
+        assert fn(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, 1, 1, 128, 64, s, 0, None, bad,
+                  None) == 1
+        # other errors are still reported with a valid variant
+        assert fn(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, 1, 1, 128, 96, s, 0, None, ok,
+                  None) == 2
+    for fn in (lib.fa_bwd_ex, lib.fa_bwd_f32_ex):
+        assert fn(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG, P1 + 6 * BIG,
+                  P1 + 7 * BIG, P1 + 8 * BIG, 1, 1, 128, 64, s, 0, None, bad, ws, nbytes, None) == 1
+    assert lib.fa_bwd_main_ex(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG,
+                              1, 1, 128, 64, s, 0, None, bad, ws, nbytes, None) == 1
+    assert lib.fa_bwd_dq_ex(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, 1, 1, 128, 64, s, 0, None,
+                            bad, ws, nbytes, None) == 1
