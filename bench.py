@@ -16,7 +16,7 @@ the five products) against the bf16 dense matrix-core peak.  `cpu_baseline` time
 bounded sample of the same workload (a few heads).
 
 Options: --steps K --warmup W (timed / untimed steps), --gpus N (only 1 is
-supported: this build runs on a single GPU), --workload NAME (another
+supported: the implementation runs on a single GPU), --workload NAME (another
 workload of workloads.WORKLOADS, forward only unless it has a backward),
 --no-cpu-baseline, --copy-calib (run a plain device copy first, for the
 profiler's traffic calibration).
@@ -79,11 +79,11 @@ def measured_traffic(workload: str, kernel_api: str):
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
-            t = json.load(f)
+            t = json.load(f)["workloads"][workload]
         src = kernel_source_digest(t["sources"])
     except (OSError, KeyError, ValueError):
         return None
-    if t.get("workload") != workload or src != t.get("kernel_source_sha256"):
+    if src != t.get("kernel_source_sha256"):
         return None
     return t["per_launch"].get(kernel_api)
 
@@ -97,34 +97,57 @@ def cpu_baseline(w, x, mask_np, heads: int) -> dict:
     """
     import oracle
     sl = (slice(0, 1), slice(0, heads))
+    window, slopes = W.workload_variant(w)
+    var = {}
+    if w.variant:
+        var = dict(window=window, slopes=None if slopes is None else slopes[:heads].astype(np.float64))
     if w.N <= 8192:
         t0 = time.perf_counter()
-        oracle.attn_fwd(x["q"].values[sl], x["k"].values[sl], x["v"].values[sl], w.scale, w.causal, mask_np)
+        oracle.attn_fwd(x["q"].values[sl], x["k"].values[sl], x["v"].values[sl], w.scale, w.causal, mask_np,
+                        **var)
         if w.backward:
             oracle.attn_bwd(x["q"].values[sl], x["k"].values[sl], x["v"].values[sl], x["do"].values[sl],
-                            w.scale, w.causal, mask_np)
+                            w.scale, w.causal, mask_np, **var)
         dt = time.perf_counter() - t0
-        fl = A.fwd_flops(1, heads, w.N, w.d, w.causal, mask_np)
+        if window is not None:
+            fl = A.fwd_flops_window(1, heads, w.N, w.d, w.causal, window)
+        else:
+            fl = A.fwd_flops(1, heads, w.N, w.d, w.causal, mask_np)
         if w.backward:
-            fl += A.bwd_flops(1, heads, w.N, w.d, w.causal, mask_np)
+            fl *= 3.5
         what = (f"{'forward+backward' if w.backward else 'forward'} of heads (b=0, h=0..{heads - 1}) of "
                 f"{w.B * w.H}")
     else:
         rows = W.sample_rows(w.B * w.H, w.N, 512, seed=W.SEED_ROWS)
         t0 = time.perf_counter()
-        oracle.attn_fwd_rows(x["q"].values, x["k"].values, x["v"].values, w.scale, rows, w.causal, mask_np)
+        oracle.attn_fwd_rows(x["q"].values, x["k"].values, x["v"].values, w.scale, rows, w.causal, mask_np,
+                             **(dict(window=window, slopes=None if slopes is None else slopes.astype(np.float64))
+                                if w.variant else {}))
         dt = time.perf_counter() - t0
-        fl = A.fwd_flops(1, 1, w.N, w.d, w.causal, mask_np) * len(rows) / w.N
+        if window is not None:
+            fl = A.fwd_flops_window(1, 1, w.N, w.d, w.causal, window) * len(rows) / w.N
+        else:
+            fl = A.fwd_flops(1, 1, w.N, w.d, w.causal, mask_np) * len(rows) / w.N
         what = f"forward of 512 sampled rows of {w.B * w.H * w.N}"
     return {
         "value": fl / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"{what} (N={w.N}, d={w.d}, {'causal' if w.causal else 'non-causal'}), fp64, {dt:.2f} s",
+        "sample": (f"{what} (N={w.N}, d={w.d}, {'causal' if w.causal else 'non-causal'}"
+                   f"{variant_label(w)}), fp64, {dt:.2f} s"),
         "seconds": round(dt, 3),
         "host_cpu": host_cpu_model(),
     }
+
+
+def variant_label(w) -> str:
+    parts = []
+    if w.window is not None:
+        parts.append(f"window {tuple(w.window)}")
+    if w.alibi:
+        parts.append("ALiBi")
+    return "".join(", " + p for p in parts)
 
 
 def main() -> int:
@@ -139,7 +162,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on a single GPU; --gpus must be 1 "
+        print("bench.py: the implementation runs on a single GPU; --gpus must be 1 "
               "(no multi-GPU path is implemented)", file=sys.stderr)
         return 2
 
@@ -181,20 +204,33 @@ def main() -> int:
 
     n_ev = 5 if w.backward else 2
 
+    window, slopes_np = W.workload_variant(w)
+    slopes = torch.from_numpy(slopes_np).to(dev) if slopes_np is not None else None
+    var = dict(window=window, alibi_slopes=slopes)
+
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
-        fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, mask, stream)
+        if w.variant:
+            fa.fa_fwd_ex(q, k, v, o, lse, w.scale, w.causal, mask, stream=stream, **var)
+        else:
+            fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, mask, stream)
         if evs is not None:
             evs[1].record(stream)
         if w.backward:
             fa.fa_bwd_prep(o, do, lse, ws, stream)
             if evs is not None:
                 evs[2].record(stream)
-            fa.fa_bwd_main(q, k, v, do, dk, dv, w.scale, w.causal, mask, ws, stream)
+            if w.variant:
+                fa.fa_bwd_main_ex(q, k, v, do, dk, dv, w.scale, w.causal, mask, workspace=ws, stream=stream, **var)
+            else:
+                fa.fa_bwd_main(q, k, v, do, dk, dv, w.scale, w.causal, mask, ws, stream)
             if evs is not None:
                 evs[3].record(stream)
-            fa.fa_bwd_dq(q, k, v, do, dq, w.scale, w.causal, mask, ws, stream)
+            if w.variant:
+                fa.fa_bwd_dq_ex(q, k, v, do, dq, w.scale, w.causal, mask, workspace=ws, stream=stream, **var)
+            else:
+                fa.fa_bwd_dq(q, k, v, do, dq, w.scale, w.causal, mask, ws, stream)
             if evs is not None:
                 evs[4].record(stream)
 
@@ -280,8 +316,10 @@ def main() -> int:
             "workload": w.name,
             "B": B, "H": H, "N": N, "d": d,
             "causal": w.causal,
+            "window": None if w.window is None else list(w.window),
+            "alibi": w.alibi,
             "block_density": None if mask_np is None else float(mask_np.mean()),
-            "step": "fa_fwd + fa_bwd" if w.backward else "fa_fwd",
+            "step": ("fa_fwd + fa_bwd" if w.backward else "fa_fwd") + (" (_ex variant)" if w.variant else ""),
             "step_flops": total_flops,
             "algorithmic_bytes": sum(bytes_.values()),
         },

@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Summaries of rocprofv3 runs of bench.py, written under profiles/.
+
+Three summaries, each from the CSV files of one profiler run (or one pair):
+
+  traffic   HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE run of
+            `bench.py --copy-calib`: every count is scaled by what the same
+            counter reads for the 256 MiB device copy that --copy-calib runs
+            first (262,144 KiB read and written).  Writes
+            profiles/hbm_traffic.json (one entry per workload, tagged with a
+            digest of the kernel sources so that bench.py stops reporting it
+            once the kernels change) and a markdown table.
+  mfma      matrix-core busy fraction per SIMD and the clock, from
+            SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE.
+  trace     per-kernel durations from a --kernel-trace run, beside the HIP
+            event medians of the bench.py line that run printed.
+
+Usage:
+  python bench_counters.py traffic --workload NAME --fetch F.csv --write W.csv --command "..." [--command "..."]
+  python bench_counters.py mfma --workload NAME --csv M.csv --command "..."
+  python bench_counters.py trace --workload NAME --csv KT_kernel_trace.csv --bench-line B.json --command "..."
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads as W  # noqa: E402
+from workloads import accounting as A  # noqa: E402
+
+COPY_KIB = 262144.0
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ["fa_common.h", "fa_fwd.hip", "fa_bwd.hip"]
+
+# kernel-name substring -> entry point that launches it
+ENTRY = [("fwd_bf16_kernel", "fa_fwd"), ("rowdot_kernel", "fa_bwd_prep"),
+         ("bwd_bf16_kernel", "fa_bwd_main"), ("bwd_dq_kernel", "fa_bwd_dq")]
+ORDER = [e for _, e in ENTRY]
+
+
+def entry_of(kernel: str):
+    for key, api in ENTRY:
+        if key in kernel:
+            return api
+    return None
+
+
+def is_copy(kernel: str) -> bool:
+    return "copyBuffer" in kernel
+
+
+def read_counters(path: str):
+    """{(kernel, counter): [value per dispatch]} from a counter_collection CSV."""
+    d = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        d[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    return d
+
+
+def workload_title(w) -> str:
+    parts = [f"B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}", "causal" if w.causal else "non-causal"]
+    if w.window is not None:
+        parts.append(f"window {tuple(w.window)}")
+    if w.alibi:
+        parts.append("ALiBi")
+    if w.mask:
+        parts.append(f"block mask {w.mask}")
+    return ", ".join(parts) + (" (forward + backward step)" if w.backward else " (forward)")
+
+
+def commands_block(cmds) -> list:
+    return ["Commands (run from /tmp with TMPDIR=/tmp on the GPU host):", "", "```", *cmds, "```", ""]
+
+
+def traffic(args) -> None:
+    w = W.WORKLOADS[args.workload]
+    f, wr = read_counters(args.fetch), read_counters(args.write)
+    copy = [k for (k, c) in f if is_copy(k) and c == "FETCH_SIZE"]
+    copy_w = [k for (k, c) in wr if is_copy(k) and c == "WRITE_SIZE"]
+    if not copy or not copy_w:
+        raise SystemExit("no calibration copy in the profile: run bench.py with --copy-calib")
+    f_copy = statistics.mean(f[(copy[0], "FETCH_SIZE")])
+    w_copy = statistics.mean(wr[(copy_w[0], "WRITE_SIZE")])
+    fs, ws = COPY_KIB / f_copy, COPY_KIB / w_copy
+    alg = A.launch_bytes(w, W.workload_mask(w, seed=0))
+    per = {}
+    rows = []
+    for (k, c), vals in f.items():
+        api = entry_of(k)
+        if api is None or c != "FETCH_SIZE":
+            continue
+        fk = statistics.mean(vals)
+        wk = statistics.mean(wr[(k, "WRITE_SIZE")])
+        rb, wb = fk * fs * 1024, wk * ws * 1024
+        per[api] = {"read_bytes": round(rb), "write_bytes": round(wb), "traffic_bytes": round(rb + wb),
+                    "algorithmic_bytes": alg[api]}
+        rows.append((ORDER.index(api), f"| {api} | `{k[:60]}` | {len(vals)} | {fk:.1f} | {wk:.1f} | {rb / 1e6:.1f} | "
+                                       f"{wb / 1e6:.1f} | {(rb + wb) / 1e6:.1f} | {alg[api] / 1e6:.1f} | "
+                                       f"{(rb + wb) / alg[api]:.2f} |"))
+    try:
+        allw = json.load(open(TRAFFIC_JSON))
+        if "workloads" not in allw:
+            allw = {"workloads": {}}
+    except (OSError, ValueError):
+        allw = {"workloads": {}}
+    allw["workloads"][w.name] = {
+        "kernel_source_sha256": bench.kernel_source_digest(KERNEL_SOURCES), "sources": KERNEL_SOURCES,
+        "fetch_scale": fs, "write_scale": ws, "per_launch": per}
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(allw, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    lines = [f"# HBM traffic per launch: {workload_title(w)}", ""]
+    lines += commands_block(args.command)
+    lines += [f"Calibration: the 256 MiB device copy that `--copy-calib` runs first reads FETCH_SIZE = {f_copy:.1f} KiB "
+              f"and WRITE_SIZE = {w_copy:.1f} KiB per dispatch for {COPY_KIB:.0f} KiB moved each way, so fetch counts "
+              f"are scaled by {fs:.4f} and write counts by {ws:.4f}.", "",
+              "| entry point | kernel | dispatches | FETCH_SIZE KiB (raw) | WRITE_SIZE KiB (raw) | read MB | write MB | "
+              "traffic MB | algorithmic MB | ratio |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    lines += [r for _, r in sorted(rows)]
+    lines += ["", "Algorithmic bytes: each tensor read or written once per launch (bf16 Q, K, V, dO, O, dQ, dK, dV; "
+              "fp32 lse and D; the block mask).  Traffic above them is K/V (forward, dQ) and Q/dO (key-outer "
+              "backward) tiles that the workgroups sharing them re-read past L2."]
+    out = os.path.join(ROOT, "profiles", f"{args.workload}_hbm_traffic.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def mfma(args) -> None:
+    w = W.WORKLOADS[args.workload]
+    m = read_counters(args.csv)
+    dur = collections.defaultdict(list)
+    for r in csv.DictReader(open(args.csv)):
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    lines = [f"# Matrix-core busy fraction and clock: {workload_title(w)}", ""]
+    lines += commands_block(args.command)
+    lines += ["GRBM_GUI_ACTIVE is summed over the 8 XCDs; busy per SIMD = SQ_VALU_MFMA_BUSY_CYCLES / "
+              "(1024 SIMDs x GRBM_GUI_ACTIVE / 8); clock = (GRBM_GUI_ACTIVE / 8) / dispatch duration.", "",
+              "| entry point | dispatches | GRBM_GUI_ACTIVE | SQ_VALU_MFMA_BUSY_CYCLES | MFMA busy per SIMD | clock GHz |",
+              "|---|---|---|---|---|---|"]
+    rows = []
+    for k in sorted({k for k, _ in m}):
+        api = entry_of(k)
+        if api is None:
+            continue
+        g = statistics.mean(m[(k, "GRBM_GUI_ACTIVE")])
+        b = statistics.mean(m[(k, "SQ_VALU_MFMA_BUSY_CYCLES")])
+        d = statistics.mean(dur[k])
+        rows.append((ORDER.index(api), f"| {api} | {len(dur[k])} | {g:.4g} | {b:.4g} | {b / (1024 * g / 8):.3f} | "
+                                       f"{g / 8 / d / 1e9:.2f} |"))
+    lines += [r for _, r in sorted(rows)]
+    lines += ["", "The published peaks assume 2.4 GHz; a dispatch too short for the estimate (the rowdot stage) "
+              "reads a clock dominated by launch overhead."]
+    out = os.path.join(ROOT, "profiles", f"{args.workload}_mfma_busy.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def trace(args) -> None:
+    w = W.WORKLOADS[args.workload]
+    line = [json.loads(x) for x in open(args.bench_line) if x.startswith('{"metric"')][-1]
+    steps, warm = line["steps"], line["warmup"]
+    per = collections.defaultdict(list)
+    names = {}
+    for r in csv.DictReader(open(args.csv)):
+        api = entry_of(r["Kernel_Name"])
+        if api is None:
+            continue
+        per[api].append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
+        names[api] = r["Kernel_Name"]
+    ev = {"fa_fwd": line.get("fwd_ms"), "fa_bwd_prep": line.get("bwd_prep_ms"),
+          "fa_bwd_main": line.get("bwd_main_ms"), "fa_bwd_dq": line.get("bwd_dq_ms")}
+    lines = [f"# Kernel trace: {workload_title(w)}", ""]
+    lines += commands_block(args.command)
+    lines += [f"{warm} warm-up steps, then {steps} timed steps.  The last column is the median of the HIP-event "
+              f"times bench.py measured on the launch stream for the same timed steps.", "",
+              "| entry point | kernel | calls | avg µs (all) | avg µs (timed) | min µs | max µs | bench.py event median µs |",
+              "|---|---|---|---|---|---|---|---|"]
+    for api in ORDER:
+        if api not in per:
+            continue
+        d = [x for _, x in sorted(per[api])]
+        timed = d[-steps:]
+        e = ev.get(api)
+        lines.append(f"| {api} | `{names[api][:60]}` | {len(d)} | {statistics.mean(d):.1f} | "
+                     f"{statistics.mean(timed):.1f} | {min(d):.1f} | {max(d):.1f} | "
+                     f"{'' if e is None else f'{e * 1e3:.1f}'} |")
+    keep = {k: line[k] for k in ("metric", "value", "unit", "ms_per_step", "fwd_ms", "bwd_ms", "bwd_prep_ms",
+                                 "bwd_main_ms", "bwd_dq_ms") if k in line}
+    lines += ["", "bench.py line printed by the profiled run (abridged):", "", "```", json.dumps(keep), "```"]
+    out = os.path.join(ROOT, "profiles", f"{args.workload}_kernel_trace.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--csv", required=True)
+    k = sub.add_parser("trace")
+    k.add_argument("--csv", required=True)
+    k.add_argument("--bench-line", required=True)
+    for p in (t, m, k):
+        p.add_argument("--workload", default=bench.DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
+        p.add_argument("--command", action="append", default=[])
+    args = ap.parse_args()
+    {"traffic": traffic, "mfma": mfma, "trace": trace}[args.what](args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

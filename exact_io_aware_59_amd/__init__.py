@@ -28,10 +28,11 @@ __all__ = [
     "fa_bwd_workspace_size", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq", "fa_status_string", "fa_version",
     "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex", "fa_bwd_dq_ex", "Variant",
     "forward", "backward", "workspace",
-    "MASK_BLOCK",
+    "MASK_BLOCK", "ABI_VERSION",
 ]
 
 MASK_BLOCK = 128
+ABI_VERSION = 2  # FA_VERSION of the fa.h these argument lists follow
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
 
@@ -85,6 +86,9 @@ def load():
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
+    if lib.fa_version() != ABI_VERSION:
+        raise ImportError(f"{path} reports ABI version {lib.fa_version()}, the binding expects {ABI_VERSION}: "
+                          "rebuild it with `python -m exact_io_aware_59_amd.build`")
     _lib = lib
     return lib
 

@@ -222,3 +222,37 @@ def test_plain_equals_empty_variant():
     fa.fa_fwd_ex(q, k, v, o2, l2, scale, True, None, window=(-1, -1))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# full-size window + ALiBi workload (benchmark launch configuration), sampled
+# ----------------------------------------------------------------------------
+
+def test_full_size_window_alibi():
+    w = W.WORKLOADS["bf16_window_alibi_fwdbwd_b2h16n4096d128"]
+    say(f"[full variant] {w.name}")
+    x = W.workload_inputs(w, seed=0)
+    win, sl = W.workload_variant(w)
+    q, k, v, do = (to_device(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    kw = dict(window=win, alibi_slopes=_dev(sl))
+    o, lse = fa.forward(q, k, v, w.scale, w.causal, **kw)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, w.scale, w.causal, **kw)
+    torch.cuda.synchronize()
+    for name, t in (("O", o), ("lse", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert torch.isfinite(t).all(), name
+    rows = W.sample_rows(w.B * w.H, w.N, 512, seed=W.SEED_ROWS)
+    # slopes are per head: row (b*H + h, i) takes slope h
+    o_ref, l_ref = oracle.attn_fwd_rows(x["q"].values, x["k"].values, x["v"].values, w.scale, rows, w.causal,
+                                        None, window=win, slopes=sl.astype(np.float64))
+    idx0 = torch.from_numpy(rows[:, 0]).to("cuda:0")
+    idx1 = torch.from_numpy(rows[:, 1]).to("cuda:0")
+    check("O rows", to_host64(o.reshape(w.B * w.H, w.N, w.d)[idx0, idx1]), o_ref, TOL_BF16["o"])
+    check("lse rows", to_host64(lse.reshape(w.B * w.H, w.N)[idx0, idx1]), l_ref, TOL_BF16["lse"])
+    for b, h in ((0, 0), (1, 15)):
+        s = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = oracle.attn_bwd(x["q"].values[s], x["k"].values[s], x["v"].values[s], x["do"].values[s],
+                                     w.scale, w.causal, None, window=win, slopes=sl[h:h + 1].astype(np.float64))
+        say(f"  head b={b} h={h} slope={sl[h]:.5f}")
+        check("dQ", to_host64(dq[b:b + 1, h:h + 1]), rq, TOL_BF16["dq"])
+        check("dK", to_host64(dk[b:b + 1, h:h + 1]), rk, TOL_BF16["dk"])
+        check("dV", to_host64(dv[b:b + 1, h:h + 1]), rv, TOL_BF16["dv"])

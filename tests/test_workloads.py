@@ -91,3 +91,38 @@ def test_workload_table():
     w = W.WORKLOADS["bf16_blocksparse_fwd_b1h8n65536d64"]
     m = W.workload_mask(w)
     assert A.workload_flops(w, m)["fwd"] == 4.0 * 8 * 65536 ** 2 * 64 / 8
+
+
+def test_window_pairs_brute_force():
+    # count admitted pairs one by one against the closed-form per-row count
+    rng = np.random.default_rng(7)
+    for _ in range(40):
+        N = int(rng.integers(1, 70))
+        wl, wr = (int(rng.integers(-1, N + 2)) for _ in range(2))
+        causal = bool(rng.integers(0, 2))
+        n = 0
+        for i in range(N):
+            for j in range(N):
+                ok = (wl < 0 or j >= i - wl) and (wr < 0 or j <= i + wr) and (not causal or j <= i)
+                n += ok
+        assert A.window_pairs(N, causal, (wl, wr)) == n, (N, wl, wr, causal)
+    # an unbounded window is the dense or causal count
+    assert A.window_pairs(100, False, (-1, -1)) == 100 * 100
+    assert A.window_pairs(100, True, (-1, -1)) == 100 * 101 // 2
+    # a 1024-key causal window at N=4096: rows 0..1023 see i + 1 keys, the rest 1024
+    assert A.window_pairs(4096, True, (1023, -1)) == 1024 * 1025 // 2 + (4096 - 1024) * 1024
+
+
+def test_window_workload():
+    w = W.WORKLOADS["bf16_window_alibi_fwdbwd_b2h16n4096d128"]
+    assert w.variant and w.causal and w.backward and w.window == (1023, -1)
+    win, sl = W.workload_variant(w)
+    assert win == (1023, -1)
+    # slopes: 2^(-8(h+1)/H), a geometric sequence ending at 2^-8
+    assert sl.dtype == np.float32 and sl.shape == (16,)
+    assert sl[1] == np.float32(0.5) and sl[-1] == np.float32(2.0 ** -8)
+    assert np.allclose(sl[1:] / sl[:-1], 2.0 ** -0.5, rtol=1e-6)
+    f = A.workload_flops(w)
+    assert f["fwd"] == 4.0 * 2 * 16 * 128 * A.window_pairs(4096, True, (1023, -1))
+    assert f["bwd"] == 2.5 * f["fwd"]
+    assert W.workload_variant(W.WORKLOADS["bf16_causal_fwd_b1h8n8192d128"]) == (None, None)

@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field, asdict
-from typing import Dict, Optional
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 
@@ -35,6 +35,8 @@ class Workload:
     mask: Optional[str] = None   # None (dense) or "band2_random" (block-sparse)
     density: float = 1.0         # target block density when mask is set
     backward: bool = False       # the workload also runs the recompute backward
+    window: Optional[Tuple[int, int]] = None  # local window (left, right); negative = unbounded
+    alibi: bool = False          # add the per-head ALiBi bias with alibi_slopes(H)
     description: str = ""
 
     @property
@@ -45,6 +47,10 @@ class Workload:
     @property
     def nb(self) -> int:
         return (self.N + MASK_BLOCK - 1) // MASK_BLOCK
+
+    @property
+    def variant(self) -> bool:
+        return self.window is not None or self.alibi
 
     def to_dict(self) -> dict:
         return asdict(self)
@@ -65,6 +71,9 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("bf16_blocksparse_fwd_b1h8n65536d64", 1, 8, 65536, 64, "bf16",
                  mask="band2_random", density=1.0 / 8,
                  description="bf16 block-sparse forward at 64K, 128x128 blocks, density 1/8"),
+        Workload("bf16_window_alibi_fwdbwd_b2h16n4096d128", 2, 16, 4096, 128, "bf16", causal=True,
+                 backward=True, window=(1023, -1), alibi=True,
+                 description="bf16 causal sliding window of 1024 keys with ALiBi, forward + backward"),
     ]
 }
 
@@ -141,6 +150,24 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
 
 def workload_inputs(w: Workload, seed: int = 0) -> Dict[str, Tensor]:
     return make_inputs(w.B, w.H, w.N, w.d, w.dtype, seed, with_do=w.backward)
+
+
+# ----------------------------------------------------------------------------
+# ALiBi slopes
+# ----------------------------------------------------------------------------
+
+def alibi_slopes(H: int) -> np.ndarray:
+    """The geometric ALiBi slopes 2^(-8 (h+1) / H), h = 0..H-1, as float32.
+
+    They are inputs of the variant (one per head), passed unchanged to both
+    sides; for H a power of two this is the usual per-head sequence.
+    """
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=np.float32)
+
+
+def workload_variant(w: Workload):
+    """(window, slopes) of a workload: None for each part it does not use."""
+    return w.window, (alibi_slopes(w.H) if w.alibi else None)
 
 
 # ----------------------------------------------------------------------------

@@ -3,8 +3,10 @@
 FLOP convention (FlashAttention-2's, restated on "FlashAttention 深度解析"
 section 四): the forward does two matrix products of 2*N*N*d each per head,
 so 4*B*H*N^2*d; a causal mask halves it; a block mask scales it by the
-fraction of blocks kept.  The backward does five such products (S recompute,
-dV, dP, dK, dQ), i.e. 2.5x the forward.
+fraction of blocks kept; a local window counts its admitted (query, key)
+pairs exactly, 4*d FLOPs each.  The ALiBi bias and the masking are
+elementwise work and are not counted.  The backward does five such products
+(S recompute, dV, dP, dK, dQ), i.e. 2.5x the forward.
 
 Algorithmic bytes are the O(N*d) floor: every tensor crosses HBM exactly once.
 The N*N score/probability traffic of unfused attention ("FlashAttention原理概览"
@@ -52,6 +54,26 @@ def bwd_flops(B: int, H: int, N: int, d: int, causal: bool = False,
     return 2.5 * fwd_flops(B, H, N, d, causal, mask)
 
 
+def window_pairs(N: int, causal: bool, window) -> int:
+    """Number of (query, key) pairs a local window admits over an N x N head.
+
+    Query i sees keys max(0, i - wl) .. min(N - 1, i + wr), with i as the
+    upper end when causal and a negative bound meaning unbounded.
+    """
+    wl, wr = window
+    i = np.arange(N, dtype=np.int64)
+    lo = np.zeros(N, dtype=np.int64) if wl < 0 else np.maximum(0, i - wl)
+    hi = np.full(N, N - 1, dtype=np.int64) if wr < 0 else np.minimum(N - 1, i + wr)
+    if causal:
+        hi = np.minimum(hi, i)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def fwd_flops_window(B: int, H: int, N: int, d: int, causal: bool, window) -> float:
+    """4*d FLOPs (QK^T and PV) per admitted pair, counted exactly."""
+    return 4.0 * B * H * d * window_pairs(N, causal, window)
+
+
 def fwd_bytes(B: int, H: int, N: int, d: int, dtype: str, nb_mask: int = 0) -> int:
     """Read q, k, v; write o (each B*H*N*d) and lse (fp32 per row); read the mask."""
     e = elem_bytes(dtype)
@@ -90,7 +112,12 @@ def tile_sram_bytes(Br: int, Bc: int, d: int, dtype_bytes: int) -> int:
 
 
 def workload_flops(w: Workload, mask: Optional[np.ndarray] = None) -> dict:
-    f = fwd_flops(w.B, w.H, w.N, w.d, w.causal, mask)
+    if w.window is not None:
+        if mask is not None:
+            raise ValueError("a workload combines a window with no block mask")
+        f = fwd_flops_window(w.B, w.H, w.N, w.d, w.causal, w.window)
+    else:
+        f = fwd_flops(w.B, w.H, w.N, w.d, w.causal, mask)
     out = {"fwd": f}
     if w.backward:
         out["bwd"] = 2.5 * f
@@ -102,4 +129,24 @@ def workload_bytes(w: Workload, mask: Optional[np.ndarray] = None) -> dict:
     out = {"fwd": fwd_bytes(w.B, w.H, w.N, w.d, w.dtype, nbm)}
     if w.backward:
         out["bwd"] = bwd_bytes(w.B, w.H, w.N, w.d, w.dtype, nbm)
+    return out
+
+
+def launch_bytes(w: Workload, mask: Optional[np.ndarray] = None) -> dict:
+    """Algorithmic bytes of one launch of each entry point of the step.
+
+    fa_fwd reads q, k, v and writes o and lse; fa_bwd_prep reads o, do and lse
+    and writes D = rowsum(dO*O) and the scaled lse; fa_bwd_main reads q, k, v,
+    do, lse and D and writes dk and dv; fa_bwd_dq reads the same and writes dq.
+    The block mask, when there is one, is read by every launch that uses it.
+    """
+    e = elem_bytes(w.dtype)
+    t = w.B * w.H * w.N * w.d * e
+    r = w.B * w.H * w.N * F32_BYTES
+    m = 0 if mask is None else int(mask.size)
+    out = {"fa_fwd": 4 * t + r + m}
+    if w.backward:
+        out.update({"fa_bwd_prep": 2 * t + 3 * r,
+                    "fa_bwd_main": 6 * t + 2 * r + m,
+                    "fa_bwd_dq": 5 * t + 2 * r + m})
     return out
