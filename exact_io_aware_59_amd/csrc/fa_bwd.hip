@@ -108,8 +108,24 @@ __device__ __forceinline__ void mfma32_acc(f32x16& d, bf16x8 a, bf16x8 b) { d = 
 template <int E, int S>
 constexpr int slot_first(int j) { return (j * E + S - 1) / S; }
 
-// VAR: local window and/or ALiBi (every step takes the masked path, P gets the bias).
-template <int D, bool CAUSAL, bool MASK, bool VAR>
+// Key of accumulator element r relative to the lane's first key or query (32-row block + 4h).
+constexpr int row_in_block(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// Whether any (query, key) pair of queries [q0, q0 + nq) x keys [k0, k0 + nk) is
+// outside the causal range, the local window or N.
+template <bool CAUSAL>
+__device__ __forceinline__ bool block_has_dead(int q0, int nq, int k0, int nk, int N, const Variant& var) {
+    return (CAUSAL && k0 + nk - 1 > q0) || k0 + nk > N || (var.wl >= 0 && q0 + nq - 1 - k0 > var.wl) ||
+           (var.wr >= 0 && k0 + nk - 1 - q0 > var.wr);
+}
+
+// VK: 0 = plain; 1 = local window and/or an ALiBi bias linear in the key over
+// the live pairs (causal, or no slopes): the S chain starts from -slope2 r'/c
+// (r' = the row offset of element r) and the exponent's addend carries
+// slope2 (key - 4h - q0); only steps that reach an edge of the window, the
+// diagonal or N take the masked path; 2 = any window and ALiBi, every step
+// masked with the bias computed per element.
+template <int D, bool CAUSAL, bool MASK, int VK>
 __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
@@ -117,6 +133,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     const uint8_t* __restrict__ mask, int nb, int nkb, int BH, int H, int wl, int wr,
     const float* __restrict__ slopes) {
     using C = BwdCfg<D>;
+    constexpr bool VAR = VK != 0, LIN = VK == 1, GEN = VK == 2;
     // three-deep ring of query tiles (Q then dO): tile t+2 streams in while t and
     // t+1 are read.  Rows are unpadded; 16-byte chunk c of row r sits at chunk
     // position c ^ swz_sigma(r), which keeps both the 16-row operand reads and
@@ -180,12 +197,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
                             ? build_block_list<kWaves>(mask + kb, (size_t)nb, lo_blk, hi_blk, rows_list, wave_cnt)
                             : 0;
         nsteps = cnt * (kMaskBlock / kBrq);
-        n_masked = (VAR || key_tail) ? nsteps
+        n_masked = (GEN || key_tail) ? nsteps
                                      : ((CAUSAL && cnt > 0 && rows_list[0] == kb) ? kMaskBlock / kBrq : 0);
     } else {
         q_first = q_lo;
         nsteps = q_hi > q_lo ? (q_hi - q_first + kBrq - 1) / kBrq : 0;
-        n_masked = (VAR || key_tail) ? nsteps : (CAUSAL ? min(nsteps, kBck / kBrq) : 0);
+        n_masked = (GEN || key_tail) ? nsteps : (CAUSAL ? min(nsteps, kBck / kBrq) : 0);
     }
     // first query of step st; steps past the end map to row N, whose copies
     // fall outside the buffers and fetch nothing
@@ -225,6 +242,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     f32x16 dvacc[C::NDM], dkacc[C::NDM];
 #pragma unroll
     for (int dm = 0; dm < C::NDM; dm++) dvacc[dm] = dkacc[dm] = f32x16{};
+    // VK = 1: start of every S chain, -slope2 r' / c for row offset r' of element r
+    f32x16 sinit = {};
+    if constexpr (LIN) {
+        const float t = -var.slope2 / c;
+#pragma unroll
+        for (int r = 0; r < 16; r++) sinit[r] = t * (float)row_in_block(r);
+    }
 
     // Operand byte offsets inside a swizzled tile (loop invariant, per lane):
     //   a_off[kk]: row l32, logical chunk 2kk + h (B128 read of the S / dP A operand);
@@ -294,13 +318,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
             }
         };
         // P of half g+1, element r (row 8(r/4) + 4h + r%4 of the half)
+        const float kq = LIN ? var.slope2 * (float)(my_key - 4 * h - qn) : 0.f;
         auto probs = [&](auto rc) {
             constexpr int r = decltype(rc)::value;
             const int qi = qn + 8 * (r / 4) + 4 * h + (r % 4);
-            float z = __builtin_fmaf(nxt.s[r], c, -lvn[r / 4][r % 4]);
-            if constexpr (VAR) z += var.bias2(qi, my_key);
+            float z;
+            if constexpr (LIN) z = __builtin_fmaf(nxt.s[r], c, kq - lvn[r / 4][r % 4]);
+            else z = __builtin_fmaf(nxt.s[r], c, -lvn[r / 4][r % 4]);
+            if constexpr (GEN) z += var.bias2(qi, my_key);
             float p = exp2f_hw(z);
-            if constexpr (MASKED || VAR)
+            if constexpr (MASKED || GEN)
                 p = ((CAUSAL && my_key > qi) || my_key >= N || (VAR && var.dead(qi, my_key))) ? 0.f : p;
             nxt.s[r] = p;
             if constexpr (r % 2 == 1) nxt.pb[r / 8][(r % 8) / 2] = cvt_pk_bf16(nxt.s[r - 1], p);
@@ -316,7 +343,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
             if constexpr (j < C::NA) {
                 // ---- S / R of half g+1; dS' of half g; lse2 / D rows of half g+1 ----
                 if constexpr (j == 0) {
-                    mfma32_zero(nxt.s, opnd[j], kf[0]);
+                    if constexpr (LIN) nxt.s = mfma32(opnd[j], kf[0], sinit);
+                    else mfma32_zero(nxt.s, opnd[j], kf[0]);
                 } else if constexpr (j < C::NKK) {
                     mfma32_acc(nxt.s, opnd[j], kf[j]);
                 } else if constexpr (j == C::NKK) {
@@ -374,7 +402,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
             l4[e] = *reinterpret_cast<const f32x4*>(&lvec[0][8 * e + 4 * h]);
             d4[e] = *reinterpret_cast<const f32x4*>(&dvec[0][8 * e + 4 * h]);
         }
-        mfma32_zero(X.s, lds_read8_b(ring[0][0], a_off[0]), kf[0]);
+        if constexpr (LIN) X.s = mfma32(lds_read8_b(ring[0][0], a_off[0]), kf[0], sinit);
+        else mfma32_zero(X.s, lds_read8_b(ring[0][0], a_off[0]), kf[0]);
 #pragma unroll
         for (int kk = 1; kk < C::NKK; kk++) mfma32_acc(X.s, lds_read8_b(ring[0][0], a_off[kk]), kf[kk]);
         X.r = f32x16{d4[0][0], d4[0][1], d4[0][2], d4[0][3], d4[1][0], d4[1][1], d4[1][2], d4[1][3],
@@ -385,8 +414,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int qi = q0 + 8 * (r / 4) + 4 * h + (r % 4);
-            float z = __builtin_fmaf(X.s[r], c, -l4[r / 4][r % 4]);
-            if constexpr (VAR) z += var.bias2(qi, my_key);
+            float z;
+            if constexpr (LIN) z = __builtin_fmaf(X.s[r], c, var.slope2 * (float)(my_key - 4 * h - q0) - l4[r / 4][r % 4]);
+            else z = __builtin_fmaf(X.s[r], c, -l4[r / 4][r % 4]);
+            if constexpr (GEN) z += var.bias2(qi, my_key);
             float p = exp2f_hw(z);
             p = ((CAUSAL && my_key > qi) || my_key >= N || (VAR && var.dead(qi, my_key))) ? 0.f : p;
             X.s[r] = p;
@@ -417,9 +448,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
         cur = nxt;
     };
 
+    int n_plain_end = nsteps;  // steps [n_masked, n_plain_end) take the unmasked path, the rest (VK = 1) masked
+    if constexpr (LIN) {
+        // Steps holding a dead pair form a prefix (diagonal, upper window edge)
+        // and a suffix (lower window edge) of the increasing query order.  A
+        // step's P work covers its own second half and the next tile's first
+        // half, so the step before a dead one is masked too.
+        auto dead_at = [&](int st) { return block_has_dead<CAUSAL>(step_q0(st), kBrq, k0, kBck, N, var); };
+        int a = 0;
+        while (a < nsteps && dead_at(a)) a++;
+        int b = nsteps;
+        while (b > a && dead_at(b - 1)) b--;
+        n_masked = a;
+        n_plain_end = b < nsteps ? max(a, b - 1) : nsteps;
+    }
     int st = 0;
     for (; st < n_masked; st++) step(std::true_type{}, st);
-    for (; st < nsteps; st++) step(std::false_type{}, st);
+    for (; st < n_plain_end; st++) step(std::false_type{}, st);
+    if constexpr (LIN)
+        for (; st < nsteps; st++) step(std::true_type{}, st);
     wait_vmem();  // copies past the last tile fetch nothing, but must retire before exit
 
     // ---- epilogue: dK = -scale * acc, dV = acc, bf16 (rows >= N dropped) ----
@@ -476,13 +523,16 @@ __device__ __forceinline__ void dq_load_tile(rsrc_t r, bf16* tile, int kv0, int 
     }
 }
 
-template <int D, bool CAUSAL, bool MASK, bool VAR>
+// VK as for the key-outer kernel; with VK = 1 the bias enters the exponent's
+// addend, slope2 (kv0 + 32 kb + 4h - q) per 32-key block plus slope2 r' per element.
+template <int D, bool CAUSAL, bool MASK, int VK>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
     bf16* __restrict__ dQ, int N, float c, float scale, const uint8_t* __restrict__ mask, int nb, int nqb,
     int n_items, int H, int wl, int wr, const float* __restrict__ slopes) {
     using C = DqCfg<D>;
+    constexpr bool VAR = VK != 0, LIN = VK == 1, GEN = VK == 2;
     __shared__ __attribute__((aligned(1024))) bf16 kbuf0[C::KTILE];
     __shared__ __attribute__((aligned(1024))) bf16 kbuf1[C::KTILE];
     __shared__ __attribute__((aligned(1024))) bf16 vbuf0[C::VTILE];
@@ -592,7 +642,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                 dq_load_tile<D, C::KS, C::KSEGS>(rk, P ? kbuf0 : kbuf1, kv0_of(it + 1), wave, lane);
                 dq_load_tile<D, C::VS, C::VSEGS>(rv, P ? vbuf0 : vbuf1, kv0_of(it + 1), wave, lane);
             }
-            const bool need_mask = VAR || (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N);
+            const bool need_mask = GEN || (LIN ? block_has_dead<CAUSAL>(qw, 32, kv0, C::BC, N, var)
+                                               : (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N));
             // two 32-key halves, software-pipelined as in the key-outer kernel
             f32x16 s[2], dp[2];
             auto scores = [&](int kb) {  // S^T and dP^T for 32 keys (keys x queries)
@@ -606,11 +657,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             };
             bf16x8 sb[2][2];
             auto probs = [&](int kb) {  // P = 2^(c s - lse2), dS = P (dP - D)
+                const float mlk = LIN ? __builtin_fmaf(var.slope2, (float)(kv0 + 32 * kb + 4 * h - my_q), ml2) : ml2;
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    float z = __builtin_fmaf(s[kb][r], c, ml2);
-                    if constexpr (VAR) z += var.bias2(my_q, key);
+                    float z;
+                    if constexpr (LIN) z = __builtin_fmaf(s[kb][r], c, __builtin_fmaf(var.slope2, (float)row_in_block(r), mlk));
+                    else z = __builtin_fmaf(s[kb][r], c, ml2);
+                    if constexpr (GEN) z += var.bias2(my_q, key);
                     float p = exp2f_hw(z);
                     if (need_mask)
                         p = ((CAUSAL && key > my_q) || key >= N || (VAR && var.dead(my_q, key))) ? 0.f : p;
@@ -657,13 +711,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
 }
 
-template <int D, bool CAUSAL, bool MASK, bool VAR>
+template <int D, bool CAUSAL, bool MASK, int VK>
 hipError_t launch_dq(const BwdArgs& a) {
     const int nqb = (a.N + kDqBr - 1) / kDqBr;
     const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
     const int n_items = a.BH * per_head;
     const size_t dyn = MASK ? (size_t)a.nb * sizeof(uint16_t) : 0;
-    auto kern = bwd_dq_kernel<D, CAUSAL, MASK, VAR>;
+    auto kern = bwd_dq_kernel<D, CAUSAL, MASK, VK>;
     if (dyn > 0) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
@@ -674,12 +728,12 @@ hipError_t launch_dq(const BwdArgs& a) {
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool MASK, bool VAR>
+template <int D, bool CAUSAL, bool MASK, int VK>
 hipError_t launch_main(const BwdArgs& a) {
     const int nkb = (a.N + kBck - 1) / kBck;
     const int n_items = a.BH * nkb;
     const size_t dyn = MASK ? (size_t)a.nb * sizeof(uint16_t) : 0;
-    auto kern = bwd_bf16_kernel<D, CAUSAL, MASK, VAR>;
+    auto kern = bwd_bf16_kernel<D, CAUSAL, MASK, VK>;
     if (dyn > 0) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
@@ -699,18 +753,27 @@ hipError_t launch_prep(const BwdArgs& a) {
     return hipGetLastError();
 }
 
-template <int D, bool VAR>
+template <int D, int VK>
 hipError_t launch_main_all(const BwdArgs& a) {
     const bool m = a.mask != nullptr;
-    if (a.causal) return m ? launch_main<D, true, true, VAR>(a) : launch_main<D, true, false, VAR>(a);
-    return m ? launch_main<D, false, true, VAR>(a) : launch_main<D, false, false, VAR>(a);
+    if (a.causal) return m ? launch_main<D, true, true, VK>(a) : launch_main<D, true, false, VK>(a);
+    return m ? launch_main<D, false, true, VK>(a) : launch_main<D, false, false, VK>(a);
 }
 
-template <int D, bool VAR>
+template <int D, int VK>
 hipError_t launch_dq_all(const BwdArgs& a) {
     const bool m = a.mask != nullptr;
-    if (a.causal) return m ? launch_dq<D, true, true, VAR>(a) : launch_dq<D, true, false, VAR>(a);
-    return m ? launch_dq<D, false, true, VAR>(a) : launch_dq<D, false, false, VAR>(a);
+    if (a.causal) return m ? launch_dq<D, true, true, VK>(a) : launch_dq<D, true, false, VK>(a);
+    return m ? launch_dq<D, false, true, VK>(a) : launch_dq<D, false, false, VK>(a);
+}
+
+// The ALiBi bias is linear in the key over the live pairs only when they all
+// precede their query; the key-outer kernel also divides the slope by c.
+int variant_kind(const BwdArgs& a, bool divides_by_c) {
+    if (!a.variant()) return 0;
+    if (a.slopes == nullptr) return 1;
+    if (!a.causal) return 2;
+    return (divides_by_c && fabsf(a.scale * kLog2e) < 0x1p-40f) ? 2 : 1;
 }
 
 }  // namespace
@@ -720,13 +783,19 @@ hipError_t launch_bwd_prep_bf16(const BwdArgs& a) {
 }
 
 hipError_t launch_bwd_main_bf16(const BwdArgs& a) {
-    if (a.variant()) return a.d == 128 ? launch_main_all<128, true>(a) : launch_main_all<64, true>(a);
-    return a.d == 128 ? launch_main_all<128, false>(a) : launch_main_all<64, false>(a);
+    switch (variant_kind(a, true)) {
+        case 0: return a.d == 128 ? launch_main_all<128, 0>(a) : launch_main_all<64, 0>(a);
+        case 1: return a.d == 128 ? launch_main_all<128, 1>(a) : launch_main_all<64, 1>(a);
+        default: return a.d == 128 ? launch_main_all<128, 2>(a) : launch_main_all<64, 2>(a);
+    }
 }
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
-    if (a.variant()) return a.d == 128 ? launch_dq_all<128, true>(a) : launch_dq_all<64, true>(a);
-    return a.d == 128 ? launch_dq_all<128, false>(a) : launch_dq_all<64, false>(a);
+    switch (variant_kind(a, false)) {
+        case 0: return a.d == 128 ? launch_dq_all<128, 0>(a) : launch_dq_all<64, 0>(a);
+        case 1: return a.d == 128 ? launch_dq_all<128, 1>(a) : launch_dq_all<64, 1>(a);
+        default: return a.d == 128 ? launch_dq_all<128, 2>(a) : launch_dq_all<64, 2>(a);
+    }
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a) {

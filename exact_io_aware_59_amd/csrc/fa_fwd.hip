@@ -123,6 +123,40 @@ __device__ __forceinline__ void variant_scores(f32x16 (&s)[FwdCfg<D>::NKB], int 
         }
 }
 
+// Key of accumulator element r relative to the lane's first key (kv0 + 32 kb + 4h).
+constexpr int key_in_block(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// Window form of the variant, on tiles that reach an edge: scores outside the
+// causal range, the window or N become -inf.  The bias is not applied here.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void window_mask(f32x16 (&s)[FwdCfg<D>::NKB], int kv0, int my_q, int N, int h,
+                                            const Variant& var) {
+    using C = FwdCfg<D>;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; kb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int key = kv0 + 32 * kb + 4 * h + key_in_block(r);
+            const bool dead = (CAUSAL && key > my_q) || key >= N || var.dead(my_q, key);
+            s[kb][r] = dead ? -INFINITY : s[kb][r];
+        }
+}
+
+// Scores to log2 units with a bias linear in the key, z = cs s + slope2 (key - q),
+// for tiles whose live keys all precede their query (causal) or whose slope is
+// zero; off0 = slope2 (kv0 + 4h - q).  Two FMAs per score; -inf stays -inf.
+template <int D>
+__device__ __forceinline__ void linear_bias_scores(f32x16 (&s)[FwdCfg<D>::NKB], float cs, float off0, float slope2) {
+    using C = FwdCfg<D>;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; kb++) {
+        const float off = __builtin_fmaf(slope2, (float)(32 * kb), off0);
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+            s[kb][r] = __builtin_fmaf(s[kb][r], cs, __builtin_fmaf(slope2, (float)key_in_block(r), off));
+    }
+}
+
 template <int D>
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[FwdCfg<D>::NKB]) {
     using C = FwdCfg<D>;
@@ -158,16 +192,20 @@ __device__ __forceinline__ void tile_pv(const bf16* vl, const bf16x8 (&pb)[FwdCf
             o[dm] = mfma32(lds_tr_operand_pad<C::VS>(vl, 16 * t, 32 * dm), pb[t], o[dm]);
 }
 
-// VAR: local window and/or ALiBi.  Every tile's scores are then taken to log2
-// units with the bias (variant_scores) and the kernel runs with c = 1; `cs` is
-// the true |scale| log2(e).
-template <int D, bool CAUSAL, bool MASK, bool VAR>
+// VK: 0 = plain; 1 and 2 = local window and/or ALiBi: every tile's scores are
+// taken to log2 units with the bias and the kernel runs with c = 1 (`cs` is
+// the true |scale| log2(e)).  With 1 the bias is linear in the key over every
+// live pair (causal, or no slopes): two FMAs per score (linear_bias_scores),
+// and only tiles that reach an edge of the window, the diagonal or N are
+// masked; 2 handles any window and slopes (variant_scores on every tile).
+template <int D, bool CAUSAL, bool MASK, int VK>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, float c, uint32_t qsign,
     const uint8_t* __restrict__ mask, int nb, int nqb, int n_items, int H, int wl, int wr,
     const float* __restrict__ slopes, float cs) {
     using C = FwdCfg<D>;
+    constexpr bool VAR = VK != 0, LIN = VK == 1, GEN = VK == 2;
     // four separate arrays (not one 2-D array) so that alias analysis can tell
     // the tile being read from the tile the DMA is filling
     __shared__ __attribute__((aligned(1024))) bf16 kbuf0[C::KTILE];
@@ -258,7 +296,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         float m_ref = -INFINITY;  // reference max of raw scores (moves lazily)
         float l_part = 0.f;       // this lane's half of the running sum
 
-        auto needs_mask = [&](int kv0) { return (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N); };
+        auto needs_mask = [&](int kv0) {
+            bool m = (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N);
+            if (LIN) m = m || (var.wl >= 0 && kv0 < qw + (kQPerWave - 1) - var.wl) ||
+                         (var.wr >= 0 && kv0 + C::BC - 1 > qw + var.wr);
+            return m;
+        };
+        // scores of the tile at kv0 -> masked in place, and their row max
+        auto finish_scores = [&](f32x16 (&sv)[C::NKB], int kv0) -> float {
+            if constexpr (GEN) {
+                variant_scores<D, CAUSAL>(sv, kv0, my_q, N, h, cs, var);
+                return tile_max<D>(sv);
+            } else if constexpr (LIN) {
+                if (needs_mask(kv0)) window_mask<D, CAUSAL>(sv, kv0, my_q, N, h, var);
+                linear_bias_scores<D>(sv, cs, var.slope2 * (float)(kv0 + 4 * h - my_q), var.slope2);
+                return tile_max<D>(sv);
+            } else {
+                if (needs_mask(kv0)) mask_scores<D, CAUSAL>(sv, kv0, my_q, N, h);
+                return tile_max<D>(sv);
+            }
+        };
 
         // ---- prologue: K0, V0, K1 in flight; S(0) and its max ----
         f32x16 sa[C::NKB], sb[C::NKB];
@@ -271,11 +328,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         }
         __syncthreads();
         if (tl.n > 0) {
-            const int kv0 = tl.kv0(0);
             tile_scores<D>(kbuf0 + k_lane, qf, sa);
-            if constexpr (VAR) variant_scores<D, CAUSAL>(sa, kv0, my_q, N, h, cs, var);
-            else if (needs_mask(kv0)) mask_scores<D, CAUSAL>(sa, kv0, my_q, N, h);
-            mx_cur = tile_max<D>(sa);
+            mx_cur = finish_scores(sa, tl.kv0(0));
         }
         __syncthreads();  // every wave is done with kbuf0 before K2 overwrites it
 
@@ -340,11 +394,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             }
             // ---- phase B: O^T += V^T P^T for tile it; mask and max of tile it+1 ----
             tile_pv<D>(v_this + v_lane, pb, oacc);
-            if (has_next) {
-                if constexpr (VAR) variant_scores<D, CAUSAL>(sn, kv1, my_q, N, h, cs, var);
-                else if (needs_mask(kv1)) mask_scores<D, CAUSAL>(sn, kv1, my_q, N, h);
-                mx_cur = tile_max<D>(sn);
-            }
+            if (has_next) mx_cur = finish_scores(sn, kv1);
             wait_vmem();
             __syncthreads();
         };
@@ -376,13 +426,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
 }
 
-template <int D, bool CAUSAL, bool MASK, bool VAR>
+template <int D, bool CAUSAL, bool MASK, int VK>
 hipError_t launch(const FwdArgs& a) {
     const int nqb = (a.N + kBr - 1) / kBr;
     const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
     const int n_items = a.BH * per_head;
     const size_t dyn = MASK ? (size_t)a.nb * sizeof(uint16_t) : 0;
-    auto kern = fwd_bf16_kernel<D, CAUSAL, MASK, VAR>;
+    auto kern = fwd_bf16_kernel<D, CAUSAL, MASK, VK>;
     if (dyn > 0) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
@@ -392,22 +442,28 @@ hipError_t launch(const FwdArgs& a) {
     const float c = a.c < 1e-30f ? 1e-30f : a.c;
     hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads), dyn, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.N,
-                       VAR ? 1.0f : c, a.qsign, a.mask, a.nb, nqb, n_items, a.H, a.wl, a.wr, a.slopes, c);
+                       VK != 0 ? 1.0f : c, a.qsign, a.mask, a.nb, nqb, n_items, a.H, a.wl, a.wr, a.slopes, c);
     return hipGetLastError();
 }
 
 }  // namespace
 
-template <int D, bool VAR>
+template <int D, int VK>
 hipError_t launch_d(const FwdArgs& a) {
     const bool m = a.mask != nullptr;
-    if (a.causal) return m ? launch<D, true, true, VAR>(a) : launch<D, true, false, VAR>(a);
-    return m ? launch<D, false, true, VAR>(a) : launch<D, false, false, VAR>(a);
+    if (a.causal) return m ? launch<D, true, true, VK>(a) : launch<D, true, false, VK>(a);
+    return m ? launch<D, false, true, VK>(a) : launch<D, false, false, VK>(a);
+}
+
+template <int VK>
+hipError_t launch_vk(const FwdArgs& a) {
+    return a.d == 128 ? launch_d<128, VK>(a) : launch_d<64, VK>(a);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-    if (a.variant()) return a.d == 128 ? launch_d<128, true>(a) : launch_d<64, true>(a);
-    return a.d == 128 ? launch_d<128, false>(a) : launch_d<64, false>(a);
+    if (!a.variant()) return launch_vk<0>(a);
+    // the ALiBi bias is linear in the key over the live pairs only when they all precede their query
+    return (a.slopes == nullptr || a.causal) ? launch_vk<1>(a) : launch_vk<2>(a);
 }
 
 }  // namespace fa

@@ -93,6 +93,9 @@ FWD = [
     (1, 1, 260, 128, False, "rand_empty_rows", (30, 30), False, None),
     (1, 1, 200, 128, True, None, (50, None), True, -0.09),
     (1, 1, 150, 64, False, None, (20, 20), True, 0.0),
+    (1, 2, 700, 64, True, "rand", None, True, None),
+    (1, 1, 300, 128, True, None, None, True, 0.0),
+    (2, 2, 1100, 128, True, None, (400, None), True, None),
 ]
 
 
@@ -122,6 +125,11 @@ BWD = [
     (1, 1, 260, 64, False, "rand_empty_rows", (30, 30), True, None),
     (1, 1, 256, 128, True, None, (40, None), True, -0.1),
     (1, 2, 640, 64, False, None, (0, 0), False, None),
+    (1, 2, 1100, 128, True, None, (400, None), True, None),
+    (1, 2, 900, 64, True, "rand", (300, None), True, None),
+    (1, 1, 700, 128, True, None, None, True, None),
+    (1, 1, 200, 64, True, None, None, True, 0.0),
+    (1, 1, 600, 128, False, None, (200, 50), False, None),
 ]
 
 
