@@ -11,7 +11,7 @@ take and return float64 arrays of shape [B, H, N, d] (lse: [B, H, N]), an
 optional uint8 block mask [nb, nb], nb = ceil(N / 128), and optionally a local
 window ``window=(wl, wr)`` (key j allowed for query i iff i - wl <= j <= i + wr,
 a negative bound = unbounded) and ALiBi slopes ``slopes`` [H] (the score gets
--slope_h * |i - j|).
+-slope_h * |i - j|).  ``attn_paged_fwd`` is decode over a paged KV cache.
 
 Every function is pinned by tests/test_oracle.py against facts that do not
 come from this code: a brute-force evaluation with a different softmax
@@ -71,9 +71,12 @@ class _Lib:
                                                c_int, _u8p, c_int, c_int, _dp, c_int, _dp, _dp]
         lib.ref_attn_bwd_ex.argtypes = [_dp, _dp, _dp, _dp, c_int, c_int, c_int, c_int, c_double,
                                         c_int, _u8p, c_int, c_int, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        _i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.ref_attn_paged_fwd.argtypes = [_dp, _dp, _dp, _i32p, _i32p, c_int, c_int, c_int, c_int, c_int,
+                                           c_int, c_int, c_int, c_double, c_int, _dp, _dp]
         for f in ("ref_attn_probs", "ref_attn_fwd", "ref_attn_fwd_rows", "ref_attn_fwd_online",
                   "ref_attn_bwd", "ref_attn_fwd_ex", "ref_attn_fwd_rows_ex", "ref_attn_fwd_online_ex",
-                  "ref_attn_bwd_ex"):
+                  "ref_attn_bwd_ex", "ref_attn_paged_fwd"):
             getattr(lib, f).restype = c_int
         self.lib = lib
 
@@ -154,6 +157,36 @@ def attn_fwd(q, k, v, scale: float, causal: bool = False, mask=None, window=None
     rc = _load().ref_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(causal),
                                  _ptr(m, _u8p), wl, wr, _ptr(sl), _ptr(o), _ptr(lse))
     _check(rc, "fwd")
+    return o, lse
+
+
+def attn_paged_fwd(q, k_cache, v_cache, block_table, seqlens, scale: float,
+                   causal: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """Decode over a paged KV cache: (O [B,H,Nq,d], lse [B,H,Nq]).
+
+    q: [B, H, Nq, d]; k_cache, v_cache: [num_pages, page_size, Hkv, d];
+    block_table: [B, max_pages] int32 (logical page -> physical page);
+    seqlens: [B] int32.  Query head h reads KV head h // (H // Hkv); the Nq
+    queries are the last Nq positions of their sequence (causal: query i sees
+    positions <= L - Nq + i).
+    """
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    B, H, Nq, d = _shape(q)
+    if kc.ndim != 4 or kc.shape != vc.shape or kc.shape[3] != d:
+        raise ValueError("k_cache and v_cache must be [num_pages, page_size, Hkv, d]")
+    num_pages, page_size, Hkv, _ = kc.shape
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32).reshape(-1)
+    if bt.ndim != 2 or bt.shape[0] != B or sl.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seqlens [B]")
+    o = np.empty_like(q)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    rc = _load().ref_attn_paged_fwd(_ptr(q), _ptr(kc), _ptr(vc), _ptr(bt, i32p), _ptr(sl, i32p), B, H, Hkv, Nq,
+                                    d, num_pages, page_size, bt.shape[1], float(scale), int(causal),
+                                    _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle paged_fwd rejected its arguments (code {rc})")
     return o, lse
 
 
@@ -268,6 +301,9 @@ class Oracle:
 
     def attn_bwd(self, *a, **kw):
         return self._swap(attn_bwd, *a, **kw)
+
+    def attn_paged_fwd(self, *a, **kw):
+        return self._swap(attn_paged_fwd, *a, **kw)
 
 
 def build_variant(src_text: str, out_path: str) -> str:

@@ -403,3 +403,81 @@ int ref_attn_bwd(const double* q, const double* k, const double* v, const double
     return ref_attn_bwd_ex(q, k, v, dO, B, H, N, d, scale, causal, mask, -1, -1, NULL, dq, dk, dv, o_out,
                            lse_out, D_out);
 }
+
+/*
+ * Attention of a few new queries over a paged KV cache (decode).
+ * "FlashAttention 深度解析" section 五: since version 2.5 FlashAttention reads
+ * the KV cache straight from the paged layout that PagedAttention manages;
+ * "FlashAttention原理概览" section 3.2 notes that inference needs no score
+ * matrix, only the cache.  The result is the same exact attention as above,
+ * taken over the keys the page table names.
+ *
+ * Layout (choices where the pages are silent):
+ *   q, o: [B][H][Nq][d]; lse: [B][H][Nq];
+ *   k_cache, v_cache: [num_pages][page_size][Hkv][d];
+ *   block_table: [B][max_pages] int32, logical page p of sequence b is the
+ *     physical page block_table[b * max_pages + p];
+ *   seqlens: [B] int32, sequence b holds keys at positions 0 .. L_b - 1, the
+ *     key at position t in row t % page_size of logical page t / page_size.
+ *   Query head h reads KV head h / (H / Hkv) (grouped heads, H % Hkv == 0).
+ *   The Nq queries are the last Nq positions L_b - Nq .. L_b - 1: with causal,
+ *   query i sees positions t <= L_b - Nq + i, otherwise all L_b keys.
+ *   A query with no key: O = 0, lse = -inf.
+ * Returns 0, or -1 (bad sizes), -2 (a page index outside [0, num_pages)),
+ * -3 (a length outside [0, max_pages * page_size]).
+ */
+int ref_attn_paged_fwd(const double* q, const double* k_cache, const double* v_cache,
+                       const int32_t* block_table, const int32_t* seqlens, int B, int H, int Hkv, int Nq,
+                       int d, int num_pages, int page_size, int max_pages, double scale, int causal,
+                       double* o, double* lse) {
+    if (B < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || Nq < 1 || d < 1 || num_pages < 1 || page_size < 1 ||
+        max_pages < 1)
+        return -1;
+    for (long b = 0; b < B; b++) {
+        long L = seqlens[b];
+        if (L < 0 || L > (long)max_pages * page_size) return -3;
+        for (long p = 0; p < (L + page_size - 1) / page_size; p++) {
+            int32_t pg = block_table[b * max_pages + p];
+            if (pg < 0 || pg >= num_pages) return -2;
+        }
+    }
+    const long group = H / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (long b = 0; b < B; b++)
+        for (long h = 0; h < H; h++) {
+            const long L = seqlens[b], hk = h / group;
+            double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+            for (long i = 0; i < Nq; i++) {
+                const double* qi = q + ((b * H + h) * Nq + i) * d;
+                double* oi = o + ((b * H + h) * Nq + i) * d;
+                /* keys 0 .. n-1 are allowed */
+                long n = causal ? L - Nq + i + 1 : L;
+                if (n > L) n = L;
+                for (long c = 0; c < d; c++) oi[c] = 0.0;
+                if (n <= 0) {
+                    lse[(b * H + h) * Nq + i] = -INFINITY;
+                    continue;
+                }
+                double m = -INFINITY;
+                for (long t = 0; t < n; t++) {
+                    const long pg = block_table[b * max_pages + t / page_size];
+                    const double* kt = k_cache + ((pg * page_size + t % page_size) * Hkv + hk) * d;
+                    double acc = 0.0;
+                    for (long c = 0; c < d; c++) acc += qi[c] * kt[c];
+                    s[t] = scale * acc;
+                    if (s[t] > m) m = s[t];
+                }
+                double z = 0.0;
+                for (long t = 0; t < n; t++) z += exp(s[t] - m);
+                for (long t = 0; t < n; t++) {
+                    const long pg = block_table[b * max_pages + t / page_size];
+                    const double* vt = v_cache + ((pg * page_size + t % page_size) * Hkv + hk) * d;
+                    const double p = exp(s[t] - m) / z;
+                    for (long c = 0; c < d; c++) oi[c] += p * vt[c];
+                }
+                lse[(b * H + h) * Nq + i] = m + log(z);
+            }
+            free(s);
+        }
+    return 0;
+}

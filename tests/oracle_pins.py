@@ -445,6 +445,137 @@ def pin_window_alibi_finite_differences(orc):
                     assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, N, i, c, fd, an)
 
 
+# ---------------------------------------------------------------------------
+# Decode over a paged KV cache ("FlashAttention 深度解析" section 五: the
+# paged KV-cache interface).  Sources of truth: brute force that assembles each
+# sequence's keys page by page in Python with the plain softmax formula; the
+# square oracle (already pinned above) on contiguous pages; invariances.
+# ---------------------------------------------------------------------------
+
+def _paged_case(seed, B, H, Hkv, Nq, d, page_size, num_pages, max_pages, lens):
+    r = _rng(seed)
+    q = r.standard_normal((B, H, Nq, d))
+    kc = r.standard_normal((num_pages, page_size, Hkv, d))
+    vc = r.standard_normal((num_pages, page_size, Hkv, d))
+    # distinct physical pages per sequence, in a shuffled order
+    perm = r.permutation(num_pages)
+    bt = np.full((B, max_pages), -7, dtype=np.int32)  # unused entries hold garbage
+    used = 0
+    for b in range(B):
+        need = -(-lens[b] // page_size)
+        bt[b, :need] = perm[used:used + need]
+        used += need
+    return q, kc, vc, bt, np.array(lens, dtype=np.int32)
+
+
+def _paged_brute(q, kc, vc, bt, lens, scale, causal):
+    B, H, Nq, d = q.shape
+    page_size, Hkv = kc.shape[1], kc.shape[2]
+    G = H // Hkv
+    o = np.zeros_like(q)
+    lse = np.zeros((B, H, Nq))
+    for b in range(B):
+        L = int(lens[b])
+        keys, vals = [], []
+        for t in range(L):
+            page = int(bt[b, t // page_size])
+            keys.append(kc[page, t % page_size])
+            vals.append(vc[page, t % page_size])
+        for h in range(H):
+            for i in range(Nq):
+                last = L - Nq + i if causal else L - 1
+                cols = list(range(0, min(last, L - 1) + 1))
+                if not cols:
+                    lse[b, h, i] = -math.inf
+                    continue
+                e = [math.exp(scale * math.fsum(float(q[b, h, i, c]) * float(keys[t][h // G, c]) for c in range(d)))
+                     for t in cols]
+                z = math.fsum(e)
+                for c in range(d):
+                    o[b, h, i, c] = math.fsum(e[u] / z * float(vals[t][h // G, c]) for u, t in enumerate(cols))
+                lse[b, h, i] = math.log(z)
+    return o, lse
+
+
+def pin_paged_brute_force(orc):
+    """Grouped heads, several page sizes, lengths that end inside a page, a
+    length shorter than the query count (first queries see nothing), an
+    empty sequence; causal and not."""
+    cases = [
+        # B, H, Hkv, Nq, d, page_size, num_pages, max_pages, lens
+        (3, 4, 2, 3, 8, 4, 12, 4, [13, 2, 0]),
+        (2, 3, 3, 1, 5, 8, 6, 3, [17, 24]),
+        (2, 6, 1, 2, 4, 2, 20, 10, [7, 19]),
+    ]
+    for seed, (B, H, Hkv, Nq, d, ps, npg, mp, lens) in enumerate(cases):
+        q, kc, vc, bt, sl = _paged_case(100 + seed, B, H, Hkv, Nq, d, ps, npg, mp, lens)
+        for causal in (False, True):
+            o, lse = orc.attn_paged_fwd(q, kc, vc, bt, sl, 0.6, causal)
+            ob, lb = _paged_brute(q, kc, vc, bt, sl, 0.6, causal)
+            _close(o, ob, 1e-12, f"paged O case {seed} causal={causal}")
+            _close(lse, lb, 1e-12, f"paged lse case {seed} causal={causal}")
+
+
+def pin_paged_equals_square(orc):
+    """Contiguous pages in order, one KV head per query head and every position
+    a query: decode is the square causal (and dense) attention."""
+    B, H, N, d, ps = 2, 3, 40, 16, 8
+    r = _rng(110)
+    q = r.standard_normal((B, H, N, d))
+    k = r.standard_normal((B, H, N, d))
+    v = r.standard_normal((B, H, N, d))
+    npg = B * N // ps
+    kc = np.zeros((npg, ps, H, d))
+    vc = np.zeros((npg, ps, H, d))
+    bt = np.zeros((B, N // ps), dtype=np.int32)
+    for b in range(B):
+        for p in range(N // ps):
+            bt[b, p] = b * (N // ps) + p
+            kc[bt[b, p]] = k[b, :, p * ps:(p + 1) * ps].transpose(1, 0, 2)
+            vc[bt[b, p]] = v[b, :, p * ps:(p + 1) * ps].transpose(1, 0, 2)
+    sl = np.full(B, N, dtype=np.int32)
+    for causal in (True, False):
+        o, lse = orc.attn_paged_fwd(q, kc, vc, bt, sl, 0.45, causal)
+        o2, l2 = orc.attn_fwd(q, k, v, 0.45, causal)
+        _close(o, o2, 1e-13, f"paged = square causal={causal}")
+        _close(lse, l2, 1e-13, f"paged lse = square causal={causal}")
+
+
+def pin_paged_invariances(orc):
+    """Moving pages to other physical slots (table updated) and NaN in every
+    cache row no sequence owns change nothing; repeating each KV head G times
+    equals grouped heads; a single query sees all keys with or without causal."""
+    B, H, Hkv, Nq, d, ps, npg, mp = 2, 4, 2, 2, 8, 4, 16, 6
+    q, kc, vc, bt, sl = _paged_case(120, B, H, Hkv, Nq, d, ps, npg, mp, [21, 10])
+    o, lse = orc.attn_paged_fwd(q, kc, vc, bt, sl, 0.5, True)
+    # relocate: physical page p -> perm[p], cache rows past each length and unused pages -> NaN
+    perm = _rng(121).permutation(npg)
+    kc2 = np.full_like(kc, np.nan)
+    vc2 = np.full_like(vc, np.nan)
+    bt2 = bt.copy()
+    for b in range(B):
+        for pgi in range(-(-int(sl[b]) // ps)):
+            src = bt[b, pgi]
+            dst = perm[src]
+            bt2[b, pgi] = dst
+            rows = min(ps, int(sl[b]) - pgi * ps)
+            kc2[dst, :rows] = kc[src, :rows]
+            vc2[dst, :rows] = vc[src, :rows]
+    o2, l2 = orc.attn_paged_fwd(q, kc2, vc2, bt2, sl, 0.5, True)
+    _close(o2, o, 0.0, "paged relocation / NaN outside the sequences")
+    _close(l2, lse, 0.0, "paged lse relocation")
+    # grouped heads = KV heads repeated
+    G = H // Hkv
+    o3, l3 = orc.attn_paged_fwd(q, np.repeat(kc, G, axis=2), np.repeat(vc, G, axis=2), bt, sl, 0.5, True)
+    _close(o3, o, 1e-14, "grouped heads = repeated KV heads")
+    _close(l3, lse, 1e-14, "grouped heads lse")
+    # one query: causal and dense agree
+    o4, l4 = orc.attn_paged_fwd(q[:, :, :1], kc, vc, bt, sl, 0.5, True)
+    o5, l5 = orc.attn_paged_fwd(q[:, :, :1], kc, vc, bt, sl, 0.5, False)
+    _close(o4, o5, 0.0, "single query causal = dense")
+    _close(l4, l5, 0.0, "single query lse")
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_rows_sum_to_one,
@@ -462,4 +593,7 @@ ALL_PINS = [
     pin_alibi_is_additive_bias,
     pin_window_alibi_chunked_and_rows,
     pin_window_alibi_finite_differences,
+    pin_paged_brute_force,
+    pin_paged_equals_square,
+    pin_paged_invariances,
 ]

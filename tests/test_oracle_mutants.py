@@ -35,6 +35,10 @@ MUTANTS = {
     "bwd_dv_uses_dS": ("dvh[j * d + c] += p * doh[i * d + c];", "dvh[j * d + c] += s * doh[i * d + c];"),
     "bwd_dP_transposed": ("acc += doh[i * d + c] * vh[j * d + c];", "acc += doh[j * d + c] * vh[i * d + c];"),
     "online_no_rescale": ("oi[c] *= corr;", "oi[c] *= 1.0;"),
+    "paged_group_map": ("hk = h / group;", "hk = h % Hkv;"),
+    "paged_causal_offset": ("long n = causal ? L - Nq + i + 1 : L;", "long n = causal ? L - Nq + i : L;"),
+    "paged_no_scale": ("s[t] = scale * acc;", "s[t] = acc;"),
+    "paged_v_from_k": ("const double* vt = v_cache +", "const double* vt = k_cache +"),
 }
 
 
