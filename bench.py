@@ -17,7 +17,8 @@ bounded sample of the same workload (a few heads).
 
 Options: --steps K --warmup W (timed / untimed steps), --gpus N (only 1 is
 supported: the implementation runs on a single GPU), --workload NAME (another
-workload of workloads.WORKLOADS, forward only unless it has a backward),
+workload of workloads.WORKLOADS, forward only unless it has a backward; the
+paged decode workload reports GB/s against the HBM peak),
 --no-cpu-baseline, --copy-calib (run a plain device copy first, for the
 profiler's traffic calibration).
 """
@@ -150,6 +151,113 @@ def variant_label(w) -> str:
     return "".join(", " + p for p in parts)
 
 
+DECODE_METRIC = "paged-KV decode throughput (algorithmic HBM bytes / s) and % of HBM peak"
+
+
+def bench_decode(args, w) -> int:
+    """One step = one fa_decode_paged call over the workload's paged cache."""
+    import torch
+    import exact_io_aware_59_amd as fa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    x = W.decode_inputs(w, seed=0)
+
+    def to_dev(t):
+        return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, kc, vc = (to_dev(x[n]) for n in ("q", "k_cache", "v_cache"))
+    bt = torch.from_numpy(x["block_table"]).to(dev)
+    sl = torch.from_numpy(x["seqlens"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    ws = fa.decode_workspace(q, kc, bt)
+    if args.copy_calib:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        fa.fa_decode_paged(q, kc, vc, bt, sl, o, lse, w.scale, w.causal, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = sorted(a.elapsed_time(b) for a, b in ev)
+    med = statistics.median(times)
+    lens = x["seqlens"]
+    nbytes = A.decode_bytes(w, lens)
+    flops = A.decode_flops(w, lens)
+    ms_per_step = wall / args.steps * 1e3
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (med * 1e-3) / 1e9
+    out = {
+        "metric": DECODE_METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "Nq": w.Nq, "d": w.d,
+            "page_size": w.page_size, "max_pages": w.max_pages, "causal": w.causal,
+            "seqlens_total": int(np.sum(lens)), "step": "fa_decode_paged (split keys + merge)",
+            "algorithmic_bytes": nbytes, "step_flops": flops,
+            "workspace_bytes": 0 if ws is None else int(ws.numel()),
+        },
+        "pct_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "call_us": {"median": round(med * 1e3, 2), "p10": round(times[len(times) // 10] * 1e3, 2),
+                    "p90": round(times[(9 * len(times)) // 10] * 1e3, 2)},
+        "tflops": round(flops / (med * 1e-3) / 1e12, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None if measured_traffic(w.name, "fa_decode_paged") is None
+            else measured_traffic(w.name, "fa_decode_paged")["traffic_bytes"],
+            "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "kernel": "decode_kernel + decode_merge_kernel (fa_decode_paged)",
+            "kernel_ms": round(med, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        nb = min(4, w.B)
+        t1 = time.perf_counter()
+        oracle.attn_paged_fwd(x["q"].values[:nb], x["k_cache"].values, x["v_cache"].values, x["block_table"][:nb],
+                              lens[:nb], w.scale, w.causal)
+        dt = time.perf_counter() - t1
+        sub = A.decode_bytes(w, lens[:nb])
+        out["cpu_baseline"] = {
+            "value": round(sub / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"decode of the first {nb} of {w.B} sequences ({int(np.sum(lens[:nb]))} cached tokens), "
+                      f"fp64, {dt:.2f} s",
+            "seconds": round(dt, 3), "host_cpu": host_cpu_model(),
+        }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +278,8 @@ def main() -> int:
     import exact_io_aware_59_amd as fa
 
     w = W.WORKLOADS[args.workload]
+    if getattr(w, "kind", "attn") == "decode":
+        return bench_decode(args, w)
     if w.dtype != "bf16":
         print("bench.py: only bf16 workloads are benchmarked", file=sys.stderr)
         return 2

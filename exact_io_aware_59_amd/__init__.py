@@ -27,12 +27,13 @@ __all__ = [
     "FAError", "library_path", "load", "fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32",
     "fa_bwd_workspace_size", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq", "fa_status_string", "fa_version",
     "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex", "fa_bwd_dq_ex", "Variant",
-    "forward", "backward", "workspace",
+    "forward", "backward", "workspace", "fa_decode_workspace_size", "fa_decode_paged", "decode_workspace",
+    "decode_paged",
     "MASK_BLOCK", "ABI_VERSION",
 ]
 
 MASK_BLOCK = 128
-ABI_VERSION = 2  # FA_VERSION of the fa.h these argument lists follow
+ABI_VERSION = 3  # FA_VERSION of the fa.h these argument lists follow
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
 
@@ -79,8 +80,12 @@ def load():
     lib.fa_bwd_dq_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp, sz, vp]
     for name in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq",
                  "fa_version", "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex",
-                 "fa_bwd_dq_ex"):
+                 "fa_bwd_dq_ex", "fa_decode_paged"):
         getattr(lib, name).restype = i
+    lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_decode_workspace_size.restype = sz
+    lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_decode_paged.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -260,6 +265,48 @@ def fa_bwd_dq_ex(q, k, v, do, dq, scale: float, causal: bool = False, blockmask=
 # ----------------------------------------------------------------------------
 # allocating wrappers
 # ----------------------------------------------------------------------------
+
+def fa_decode_workspace_size(B: int, H: int, H_kv: int, Nq: int, d: int, page_size: int, max_pages: int) -> int:
+    return int(load().fa_decode_workspace_size(B, H, H_kv, Nq, d, page_size, max_pages))
+
+
+def fa_decode_paged(q, k_cache, v_cache, block_table, seqlens, o, lse, scale: float, causal: bool = True,
+                    workspace=None, stream=None):
+    """Decode over a paged KV cache (bf16): q [B,H,Nq,d]; caches [num_pages,page_size,H_kv,d];
+    block_table int32 [B,max_pages]; seqlens int32 [B]; writes o [B,H,Nq,d] and lse [B,H,Nq]."""
+    B, H, Nq, d = _dims(q)
+    num_pages, page_size, H_kv, dk = (int(x) for x in k_cache.shape)
+    if dk != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache must be [num_pages, page_size, H_kv, d]")
+    max_pages = int(block_table.shape[1])
+    _check(load().fa_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seqlens),
+                                  _ptr(o), _ptr(lse), B, H, H_kv, Nq, d, num_pages, page_size, max_pages,
+                                  float(scale), int(bool(causal)), _ptr(workspace), _nbytes(workspace),
+                                  _stream(stream)), "fa_decode_paged")
+
+
+def decode_workspace(q, k_cache, block_table):
+    """A workspace tensor for decode_paged / fa_decode_paged, or None when none is needed."""
+    import torch
+    B, H, Nq, d = _dims(q)
+    _, page_size, H_kv, _ = (int(x) for x in k_cache.shape)
+    n = fa_decode_workspace_size(B, H, H_kv, Nq, d, page_size, int(block_table.shape[1]))
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seqlens, scale: Optional[float] = None, causal: bool = True,
+                 ws=None, stream=None):
+    """Allocate o and lse (and a workspace) on q's device and run fa_decode_paged."""
+    import torch
+    B, H, Nq, d = _dims(q)
+    scale = _default_scale(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = decode_workspace(q, k_cache, block_table)
+    fa_decode_paged(q, k_cache, v_cache, block_table, seqlens, o, lse, scale, causal, ws, stream)
+    return o, lse
+
 
 def _default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)

@@ -249,6 +249,91 @@ int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, c
                          workspace_bytes, stream);
 }
 
+// Key ranges of the decode: enough waves to fill the chip about twice (256 CUs
+// x 4 waves), at least 256 keys per range; kpp is a multiple of the 32-key tile.
+static void decode_plan(int B, int H, int H_kv, int Nq, int page_size, int max_pages, int& n_parts, int& kpp) {
+    const long long cap = (long long)max_pages * page_size;
+    const long long groups = (long long)B * H_kv * (((long long)(H / H_kv) * Nq + 31) / 32);
+    const long long want = (2048 + groups - 1) / groups;
+    const long long most = (cap + 255) / 256;
+    long long parts = want < 1 ? 1 : want;
+    if (parts > most) parts = most;
+    long long per = (cap + parts - 1) / parts;
+    per = (per + 31) / 32 * 32;
+    kpp = (int)per;
+    n_parts = (int)((cap + per - 1) / per);
+}
+
+static int decode_check(int B, int H, int H_kv, int Nq, int d, int page_size, int max_pages) {
+    if (B < 1 || H < 1 || H_kv < 1 || Nq < 1 || d < 1 || page_size < 1 || max_pages < 1) return FA_ERR_INVALID_ARG;
+    if (H % H_kv != 0) return FA_ERR_INVALID_ARG;
+    if ((long long)B * H * Nq * d >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+    if ((long long)max_pages * page_size >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (page_size % 32 != 0) return FA_ERR_UNSUPPORTED;
+    if ((long long)page_size * H_kv * d * 2 >= (1LL << 32)) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+size_t fa_decode_workspace_size(int B, int H, int H_kv, int Nq, int d, int page_size, int max_pages) {
+    if (decode_check(B, H, H_kv, Nq, d, page_size, max_pages) != FA_OK) return 0;
+    int n_parts, kpp;
+    decode_plan(B, H, H_kv, Nq, page_size, max_pages, n_parts, kpp);
+    if (n_parts == 1) return 0;
+    const size_t rows = (size_t)B * H * Nq * n_parts;
+    return align_up(rows * d * sizeof(float)) + align_up(rows * 2 * sizeof(float));
+}
+
+int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                    const int32_t* seqlens, void* o, float* lse, int B, int H, int H_kv, int Nq, int d,
+                    int num_pages, int page_size, int max_pages, float scale, int causal, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !block_table || !seqlens || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || ((uintptr_t)lse & 3) ||
+        ((uintptr_t)block_table & 3) || ((uintptr_t)seqlens & 3))
+        return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || num_pages < 1) return FA_ERR_INVALID_ARG;
+    int st = decode_check(B, H, H_kv, Nq, d, page_size, max_pages);
+    if (st != FA_OK) return st;
+    const size_t qb = (size_t)B * H * Nq * d * 2, lb = (size_t)B * H * Nq * 4;
+    const size_t cb = (size_t)num_pages * page_size * H_kv * d * 2;
+    const size_t tb = (size_t)B * max_pages * 4, sb = (size_t)B * 4;
+    const void* ins[] = {q, k_cache, v_cache};
+    const size_t in_bytes[] = {qb, cb, cb};
+    for (int i = 0; i < 3; i++)
+        if (overlap(o, qb, ins[i], in_bytes[i]) || overlap(lse, lb, ins[i], in_bytes[i])) return FA_ERR_INVALID_ARG;
+    if (overlap(o, qb, lse, lb) || overlap(o, qb, block_table, tb) || overlap(o, qb, seqlens, sb) ||
+        overlap(lse, lb, block_table, tb) || overlap(lse, lb, seqlens, sb))
+        return FA_ERR_INVALID_ARG;
+    fa::DecArgs a;
+    decode_plan(B, H, H_kv, Nq, page_size, max_pages, a.n_parts, a.kpp);
+    const size_t need = fa_decode_workspace_size(B, H, H_kv, Nq, d, page_size, max_pages);
+    a.ws_o = nullptr;
+    a.ws_ml = nullptr;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0) return FA_ERR_WORKSPACE;
+        const void* all[] = {q, k_cache, v_cache, o, lse, block_table, seqlens};
+        const size_t all_bytes[] = {qb, cb, cb, qb, lb, tb, sb};
+        for (int i = 0; i < 7; i++)
+            if (overlap(workspace, need, all[i], all_bytes[i])) return FA_ERR_INVALID_ARG;
+        const size_t rows = (size_t)B * H * Nq * a.n_parts;
+        a.ws_o = (float*)workspace;
+        a.ws_ml = (float*)((char*)workspace + align_up(rows * d * sizeof(float)));
+    }
+    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+    a.block_table = block_table; a.seqlens = seqlens;
+    a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.Hkv = H_kv; a.Nq = Nq; a.d = d;
+    a.num_pages = num_pages; a.page_size = page_size; a.max_pages = max_pages;
+    a.causal = causal;
+    // scale 0 would turn -inf * 0 into NaN; any c below 1e-30 gives the same fp32 probabilities
+    a.c = fmaxf(fabsf(scale) * fa::kLog2eHost, 1e-30f);
+    a.qsign = scale < 0.f ? 0x80008000u : 0u;
+    a.stream = (hipStream_t)stream;
+    return fa::launch_decode_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";

@@ -64,12 +64,12 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, non-finite scale, aliasing, too large */
     FA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. head dimension not 64 or 128) */
-    FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than fa_bwd_workspace_size() */
+    FA_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or smaller than the *_workspace_size() */
     FA_ERR_HIP = 4          /* the HIP runtime reported an error while enqueueing */
 } fa_status;
 
 #define FA_MASK_BLOCK 128 /* block-mask granularity in rows and columns */
-#define FA_VERSION 2
+#define FA_VERSION 3
 
 /*
  * Local window and ALiBi, the two further built-in variants "FlashAttention
@@ -182,6 +182,40 @@ int fa_bwd_f32_ex(const float* q, const float* k, const float* v, const float* o
                   const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
                   float scale, int causal, const uint8_t* blockmask, const fa_variant* variant,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode over a paged KV cache, bfloat16 ("FlashAttention 深度解析" section 五:
+ * since version 2.5 FlashAttention reads the KV cache from the paged layout
+ * PagedAttention manages; the layout below is the one taken, the pages give
+ * none).  For each sequence b, its Nq new queries (the last Nq positions
+ * L_b - Nq .. L_b - 1) attend to its L_b cached keys:
+ *   q:           const bf16 [B][H][Nq][d]
+ *   k_cache,
+ *   v_cache:     const bf16 [num_pages][page_size][H_kv][d]: page p holds
+ *                page_size consecutive positions of one sequence, every KV head
+ *   block_table: const int32 [B][max_pages]: logical page j of sequence b (its
+ *                positions j*page_size ..) is physical page block_table[b][j]
+ *   seqlens:     const int32 [B]: L_b, 0 <= L_b <= max_pages * page_size
+ *   o:           bf16 [B][H][Nq][d] (written); lse: float [B][H][Nq] (written,
+ *                natural log; -inf and o = 0 for a query with no key)
+ * Query head h reads KV head h / (H / H_kv) (grouped heads; H % H_kv == 0).
+ * causal = 1: query i of sequence b sees positions <= L_b - Nq + i; causal = 0:
+ * all L_b keys.  block_table and seqlens are device memory read by the
+ * kernels: a length outside [0, max_pages * page_size] is clamped into it, and
+ * a page index outside [0, num_pages) reads as zeros (its sequence's result is
+ * then meaningless, but nothing outside the cache is touched).
+ * Limits: d in {64, 128}; page_size a multiple of 32; B*H*Nq*d < 2^31;
+ * max_pages * page_size < 2^31; page_size * H_kv * d * 2 < 2^32.
+ * workspace: device, 256-byte aligned, at least fa_decode_workspace_size()
+ * bytes (0 when one key range covers every sequence: NULL is then allowed).
+ * The keys are split into ranges processed in parallel and merged exactly
+ * with the running max / sum rule; the result does not depend on the split.
+ */
+size_t fa_decode_workspace_size(int B, int H, int H_kv, int Nq, int d, int page_size, int max_pages);
+int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                    const int32_t* seqlens, void* o, float* lse, int B, int H, int H_kv, int Nq, int d,
+                    int num_pages, int page_size, int max_pages, float scale, int causal, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -34,13 +34,13 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_bwd_workspace_size",
-                          "fa_status_string", "fa_version"}
+                          "fa_status_string", "fa_version", "fa_decode_paged", "fa_decode_workspace_size"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status(lib):
-    assert fa.fa_version() == 2
+    assert fa.fa_version() == fa.ABI_VERSION == 3
     for s in range(5):
         assert fa.fa_status_string(s)
     assert fa.fa_status_string(99) == "unknown status"
@@ -154,3 +154,45 @@ def test_variant_validation(lib):
                               1, 1, 128, 64, s, 0, None, bad, ws, nbytes, None) == 1
     assert lib.fa_bwd_dq_ex(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, 1, 1, 128, 64, s, 0, None,
                             bad, ws, nbytes, None) == 1
+
+
+def _dec(lib, q=P1, kc=P1 + BIG, vc=P1 + 2 * BIG, bt=P1 + 3 * BIG, sl=P1 + 4 * BIG, o=P1 + 5 * BIG,
+         lse=P1 + 6 * BIG, B=2, H=8, Hkv=2, Nq=1, d=128, num_pages=16, page_size=64, max_pages=8, scale=0.1,
+         causal=1, ws=P1 + 7 * BIG, ws_bytes=1 << 30):
+    return lib.fa_decode_paged(q, kc, vc, bt, sl, o, lse, B, H, Hkv, Nq, d, num_pages, page_size, max_pages,
+                               ctypes.c_float(scale), causal, ws, ws_bytes, None)
+
+
+def test_decode_workspace_plan(lib):
+    # 2 sequences x 2 KV heads: the keys split into ranges of >= 256 keys
+    ws = fa.fa_decode_workspace_size(2, 8, 2, 1, 128, 64, 8)
+    rows = 2 * 8 * 1
+    parts = 2  # capacity 512 keys, at least 256 per range
+    assert ws == (rows * parts * 128 * 4 + 255) // 256 * 256 + (rows * parts * 2 * 4 + 255) // 256 * 256
+    # enough (sequence, KV head) pairs to fill the chip: one range, no workspace
+    assert fa.fa_decode_workspace_size(64, 64, 64, 1, 64, 32, 4) == 0
+    assert fa.fa_decode_workspace_size(2, 8, 3, 1, 128, 64, 8) == 0  # H % H_kv != 0: invalid
+
+
+def test_decode_validation(lib):
+    ok = fa.fa_decode_workspace_size(2, 8, 2, 1, 128, 64, 8)
+    assert ok > 0
+    E, U, W = 1, 2, 3
+    assert _dec(lib, q=0) == E
+    assert _dec(lib, bt=0) == E
+    assert _dec(lib, sl=0) == E
+    assert _dec(lib, Hkv=3) == E                 # H % H_kv
+    assert _dec(lib, d=96) == U
+    assert _dec(lib, page_size=48) == U          # not a multiple of 32
+    assert _dec(lib, scale=float("nan")) == E
+    assert _dec(lib, causal=2) == E
+    assert _dec(lib, num_pages=0) == E
+    assert _dec(lib, Nq=0) == E
+    assert _dec(lib, q=P1 + 8) == E              # misaligned
+    assert _dec(lib, sl=P1 + 4 * BIG + 2) == E   # misaligned int32
+    assert _dec(lib, ws=0) == W
+    assert _dec(lib, ws_bytes=ok - 1) == W
+    assert _dec(lib, ws=P1 + 7 * BIG + 64) == W  # not 256-byte aligned
+    assert _dec(lib, o=P1) == E                  # o aliases q
+    assert _dec(lib, ws=P1 + BIG) == E           # workspace inside the K cache
+    assert _dec(lib, max_pages=1 << 26, page_size=64) == E  # capacity >= 2^31

@@ -126,3 +126,19 @@ def test_window_workload():
     assert f["fwd"] == 4.0 * 2 * 16 * 128 * A.window_pairs(4096, True, (1023, -1))
     assert f["bwd"] == 2.5 * f["fwd"]
     assert W.workload_variant(W.WORKLOADS["bf16_causal_fwd_b1h8n8192d128"]) == (None, None)
+
+
+def test_decode_workload_and_accounting():
+    w = W.WORKLOADS["bf16_paged_decode_b16h32kv8d128_len1k_8k"]
+    x = W.decode_inputs(w)
+    lens = x["seqlens"]
+    assert lens.dtype == np.int32 and lens.shape == (16,) and lens.min() >= 1024 and lens.max() <= 8192
+    bt = x["block_table"]
+    assert bt.shape == (16, 32) and len(set(bt.ravel().tolist())) == bt.size  # distinct physical pages
+    assert x["k_cache"].bits.shape == (16 * 32, 256, 8, 128)
+    # pairs: one query at the end of each sequence sees every key
+    assert A.decode_pairs(1, lens, True) == int(lens.sum())
+    assert A.decode_pairs(3, [5], True) == 3 + 4 + 5 and A.decode_pairs(3, [1], True) == 1
+    assert A.decode_flops(w, lens) == 4.0 * 128 * 32 * int(lens.sum())
+    assert A.decode_bytes(w, lens) == (2 * int(lens.sum()) * 8 * 128 * 2 + 2 * 16 * 32 * 128 * 2 + 4 * 16 * 32
+                                       + 4 * 16 * 33)

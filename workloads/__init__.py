@@ -77,8 +77,51 @@ WORKLOADS: Dict[str, Workload] = {
     ]
 }
 
-# Seed offsets per tensor (base seed s): q=s, k=s+1, v=s+2, do=s+3, mask=s+4, rows=s+5.
-SEED_Q, SEED_K, SEED_V, SEED_DO, SEED_MASK, SEED_ROWS = range(6)
+# Seed offsets per tensor (base seed s): q=s, k=s+1, v=s+2, do=s+3, mask=s+4, rows=s+5,
+# page table=s+6, sequence lengths=s+7.
+SEED_Q, SEED_K, SEED_V, SEED_DO, SEED_MASK, SEED_ROWS, SEED_PAGES, SEED_LENS = range(8)
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Decode over a paged KV cache: Nq new queries per sequence, B sequences
+    whose lengths are drawn uniformly from [min_len, max_len], H query heads
+    grouped onto Hkv KV heads, pages of page_size positions."""
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    Nq: int
+    d: int
+    page_size: int
+    min_len: int
+    max_len: int
+    causal: bool = True
+    dtype: str = "bf16"
+    description: str = ""
+    kind: str = "decode"
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def max_pages(self) -> int:
+        return -(-self.max_len // self.page_size)
+
+    @property
+    def num_pages(self) -> int:
+        return self.B * self.max_pages
+
+    def to_dict(self) -> dict:
+        return asdict(self)
+
+
+WORKLOADS["bf16_paged_decode_b16h32kv8d128_len1k_8k"] = DecodeWorkload(
+    "bf16_paged_decode_b16h32kv8d128_len1k_8k", B=16, H=32, Hkv=8, Nq=1, d=128, page_size=256,
+    min_len=1024, max_len=8192,
+    description="bf16 decode, one new token per sequence, 16 sequences of 1K-8K cached tokens in 256-token pages, "
+                "32 query heads on 8 KV heads")
 
 
 # ----------------------------------------------------------------------------
@@ -246,3 +289,34 @@ def sample_rows(BH: int, N: int, nrows: int, seed: int) -> np.ndarray:
     flat = [bh * N + i for bh, i in forced] + picked
     flat = np.array(sorted(flat), dtype=np.int64)
     return np.stack([flat // N, flat % N], axis=1)
+
+
+# ----------------------------------------------------------------------------
+# Paged KV cache (decode)
+# ----------------------------------------------------------------------------
+
+def make_paged(B: int, H: int, Hkv: int, Nq: int, d: int, page_size: int, max_pages: int, lens, seed: int,
+               dtype: str = "bf16", num_pages: Optional[int] = None) -> Dict[str, object]:
+    """q [B,H,Nq,d], k_cache / v_cache [num_pages, page_size, Hkv, d] (iid N(0,1)
+    encoded as dtype), block_table [B, max_pages] int32 and seqlens [B] int32.
+
+    Every sequence owns max_pages distinct physical pages in a seeded random
+    order (a shuffled allocator); cache rows past a sequence's length hold
+    draws too, which the computation must ignore.
+    """
+    num_pages = B * max_pages if num_pages is None else num_pages
+    if num_pages < B * max_pages:
+        raise ValueError("num_pages must cover every sequence's pages")
+    perm = np.random.default_rng(seed + SEED_PAGES).permutation(num_pages)[:B * max_pages]
+    return {
+        "q": make_tensor((B, H, Nq, d), seed + SEED_Q, dtype),
+        "k_cache": make_tensor((num_pages, page_size, Hkv, d), seed + SEED_K, dtype),
+        "v_cache": make_tensor((num_pages, page_size, Hkv, d), seed + SEED_V, dtype),
+        "block_table": perm.reshape(B, max_pages).astype(np.int32),
+        "seqlens": np.asarray(lens, dtype=np.int32),
+    }
+
+
+def decode_inputs(w: DecodeWorkload, seed: int = 0) -> Dict[str, object]:
+    lens = np.random.default_rng(seed + SEED_LENS).integers(w.min_len, w.max_len + 1, size=w.B)
+    return make_paged(w.B, w.H, w.Hkv, w.Nq, w.d, w.page_size, w.max_pages, lens, seed, w.dtype)

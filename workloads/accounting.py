@@ -150,3 +150,29 @@ def launch_bytes(w: Workload, mask: Optional[np.ndarray] = None) -> dict:
                     "fa_bwd_main": 6 * t + 2 * r + m,
                     "fa_bwd_dq": 5 * t + 2 * r + m})
     return out
+
+
+def decode_pairs(Nq: int, lens, causal: bool) -> int:
+    """(query, key) pairs of one query head over all sequences."""
+    n = 0
+    for L in np.asarray(lens, dtype=np.int64):
+        for i in range(Nq):
+            last = (L - Nq + i) if causal else (L - 1)
+            n += int(max(0, min(last, L - 1) + 1))
+    return n
+
+
+def decode_flops(w, lens) -> float:
+    """4*d FLOPs per (query, key) pair (QK^T and PV), every query head."""
+    return 4.0 * w.d * w.H * decode_pairs(w.Nq, lens, w.causal)
+
+
+def decode_bytes(w, lens) -> int:
+    """Each used K and V row read once, q read, o and lse written, the page
+    table and lengths read, for the sequences whose lengths are given."""
+    e = elem_bytes(w.dtype)
+    lens = np.asarray(lens, dtype=np.int64)
+    B = int(lens.size)
+    kv = 2 * int(lens.sum()) * w.Hkv * w.d * e
+    qo = 2 * B * w.H * w.Nq * w.d * e
+    return kv + qo + F32_BYTES * B * w.H * w.Nq + 4 * B * (w.max_pages + 1)
