@@ -249,8 +249,9 @@ int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, c
                          workspace_bytes, stream);
 }
 
-// Key ranges of the decode: enough waves to fill the chip about twice (256 CUs
-// x 4 waves), at least 256 keys per range; kpp is a multiple of the 32-key tile.
+// Key ranges of the decode: about one wave per resident wave slot of the chip
+// (256 CUs x 8) when every sequence is full, at least 256 keys (eight tiles)
+// per range; kpp is a multiple of the 32-key tile.
 static void decode_plan(int B, int H, int H_kv, int Nq, int page_size, int max_pages, int& n_parts, int& kpp) {
     const long long cap = (long long)max_pages * page_size;
     const long long groups = (long long)B * H_kv * (((long long)(H / H_kv) * Nq + 31) / 32);

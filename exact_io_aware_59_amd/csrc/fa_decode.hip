@@ -17,12 +17,13 @@
 //      max and sum and accumulates O^T += V^T P^T, like the forward kernel.
 //      K tiles go from HBM straight into registers (their rows are the MFMA A
 //      operand); V tiles go HBM -> LDS by buffer_load ... lds into a swizzled
-//      per-wave ring of three and are read transposed.  Two tiles stay in
-//      flight behind the one being computed.  The wave writes (O unnormalized, max,
+//      per-wave ring of two and are read transposed; the next tile is in
+//      flight while one is computed, and two workgroups (eight waves) share a
+//      CU.  The wave writes (O unnormalized, max,
 //      sum) for its key range, or the final O and lse when one range covers
 //      the sequence.
-//   2. decode_merge_kernel: per query row, O = sum_p w_p O_p / sum_p w_p l_p
-//      with w_p = 2^(m_p - max_p m_p), lse = ln 2 (max + log2 sum).
+//   2. decode_merge_kernel: per query row (one wave), O = sum_p w_p O_p /
+//      sum_p w_p l_p with w_p = 2^(m_p - max_p m_p), lse = ln 2 (max + log2 sum).
 // Rows past a sequence's length and pages outside the cache read as zero
 // (buffer range checks), so nothing outside the caller's buffers is touched.
 #include <type_traits>
@@ -46,7 +47,7 @@ __device__ __forceinline__ bf16x8 lds_tr_pair_v(const bf16* base, uint32_t lo_of
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecBC = 32;     // keys per tile
-constexpr int kDecStages = 3;  // per-wave ring: the tile being computed and two in flight
+constexpr int kDecStages = 2;  // per-wave ring: the tile being computed and the next in flight
 constexpr float kDecRescale = 8.0f;
 
 template <int D>
@@ -61,19 +62,18 @@ struct DecCfg {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(
+__global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ Kc, const bf16* __restrict__ Vc,
     const int* __restrict__ block_table, const int* __restrict__ seqlens, bf16* __restrict__ O,
     float* __restrict__ LSE, float* __restrict__ ws_o, float* __restrict__ ws_ml, int H, int Hkv, int Nq,
     int page_size, int max_pages, int num_pages, int nqg, int n_parts, int kpp, int n_items, float c,
     uint32_t qsign) {
     using C = DecCfg<D>;
-    // the three V slots are separate arrays so the compiler can tell the copy
+    // the two V slots are separate arrays so the compiler can tell the copy
     // in flight into one from the reads of another (it then waits for exactly
     // the copies a tile needs)
     __shared__ __attribute__((aligned(1024))) bf16 vring0[kDecWaves][C::VTILE];
     __shared__ __attribute__((aligned(1024))) bf16 vring1[kDecWaves][C::VTILE];
-    __shared__ __attribute__((aligned(1024))) bf16 vring2[kDecWaves][C::VTILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(
     }
     auto slot_of = [&](auto sc) -> bf16* {
         constexpr int s = decltype(sc)::value;
-        return s == 0 ? &vring0[wave][0] : s == 1 ? &vring1[wave][0] : &vring2[wave][0];
+        return s == 0 ? &vring0[wave][0] : &vring1[wave][0];
     };
     auto issue = [&](auto sc, int t) {
         constexpr int s = decltype(sc)::value;
@@ -185,9 +185,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(
     float l_part = 0.f;       // this lane's half of the running sum
 
     // One tile from ring slot s (the compiler waits for exactly its loads; the
-    // two later tiles stay in flight), then refill the slot with tile t + 3.
-    // Tiles past the range (the last round of three) read zeros, are masked
-    // out completely and cost matrix work only.
+    // next tile stays in flight), then refill the slot with tile t + 2.  A tile
+    // past the range (the last round of two) reads zeros, is masked out
+    // completely and costs matrix work only.
     auto tile = [&](auto sc, int t) {
         constexpr int s = decltype(sc)::value;
         const int t0 = k_begin + kDecBC * t;
@@ -238,11 +238,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(
 
     issue(std::integral_constant<int, 0>{}, 0);
     issue(std::integral_constant<int, 1>{}, 1);
-    issue(std::integral_constant<int, 2>{}, 2);
     for (int t = 0; t < nt; t += kDecStages) {
         tile(std::integral_constant<int, 0>{}, t);
         tile(std::integral_constant<int, 1>{}, t + 1);
-        tile(std::integral_constant<int, 2>{}, t + 2);
     }
     wait_vmem();  // copies past the last tile fetch nothing but must retire before the wave ends
 
@@ -279,40 +277,61 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(
     }
 }
 
-// Per query row: merge the key ranges' (O, max, sum).  32 threads per row.
+// Per query row: merge the key ranges' (O, max, sum).  One wave per row: the
+// lanes take the ranges' maxima in parallel (wave max), then every lane owns
+// D/64 output columns and sums the ranges' partial rows with their weights.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ ws_o,
                                                            const float* __restrict__ ws_ml,
                                                            const int* __restrict__ seqlens, bf16* __restrict__ O,
                                                            float* __restrict__ LSE, int rows, int H, int Nq,
                                                            int n_parts, int kpp, int max_keys) {
-    constexpr int PER = D / 32;
-    const int row = blockIdx.x * 8 + (threadIdx.x >> 5);
-    const int t = threadIdx.x & 31;
+    constexpr int PER = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const int b = row / (H * Nq);
     const int L = max(0, min(seqlens[b], max_keys));
     const int nvalid = min(n_parts, (L + kpp - 1) / kpp);
     const float* ml = ws_ml + (size_t)row * n_parts * 2;
     float M = -INFINITY;
-    for (int p = 0; p < nvalid; p++) M = fmaxf(M, ml[2 * p]);
+    for (int p = lane; p < nvalid; p += 64) M = fmaxf(M, ml[2 * p]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; e++) acc[e] = 0.f;
     float lsum = 0.f;
     if (M != -INFINITY) {
-        for (int p = 0; p < nvalid; p++) {
-            const float w = exp2f_hw(ml[2 * p] - M);  // 0 for a range with no allowed key
-            lsum += w * ml[2 * p + 1];
-            const float* src = ws_o + ((size_t)row * n_parts + p) * D + t * PER;
+        const float* src = ws_o + (size_t)row * n_parts * D + lane * PER;
+        int p = 0;
+        for (; p + 4 <= nvalid; p += 4) {  // four ranges' loads in flight
+            float w[4], ov[4][PER];
 #pragma unroll
-            for (int e = 0; e < PER; e++) acc[e] += w * src[e];
+            for (int u = 0; u < 4; u++) {
+                w[u] = ml[2 * (p + u)];
+#pragma unroll
+                for (int e = 0; e < PER; e++) ov[u][e] = src[(size_t)(p + u) * D + e];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const float wu = exp2f_hw(w[u] - M);  // 0 for a range with no allowed key
+                lsum += wu * ml[2 * (p + u) + 1];
+#pragma unroll
+                for (int e = 0; e < PER; e++) acc[e] += wu * ov[u][e];
+            }
+        }
+        for (; p < nvalid; p++) {
+            const float wu = exp2f_hw(ml[2 * p] - M);
+            lsum += wu * ml[2 * p + 1];
+#pragma unroll
+            for (int e = 0; e < PER; e++) acc[e] += wu * src[(size_t)p * D + e];
         }
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
-    for (int e = 0; e < PER; e++) O[(size_t)row * D + t * PER + e] = (bf16)(acc[e] * inv);
-    if (t == 0) LSE[row] = lsum > 0.f ? (M + log2f_hw(lsum)) * kLn2 : -INFINITY;
+    for (int e = 0; e < PER; e++) O[(size_t)row * D + lane * PER + e] = (bf16)(acc[e] * inv);
+    if (lane == 0) LSE[row] = lsum > 0.f ? (M + log2f_hw(lsum)) * kLn2 : -INFINITY;
 }
 
 template <int D, bool CAUSAL>
@@ -328,7 +347,7 @@ hipError_t launch_decode_d(const DecArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_parts == 1) return e;
     const int rows = a.B * a.H * a.Nq;
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((rows + 7) / 8), dim3(256), 0, a.stream, a.ws_o, a.ws_ml,
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, a.stream, a.ws_o, a.ws_ml,
                        a.seqlens, (bf16*)a.o, a.lse, rows, a.H, a.Nq, a.n_parts, a.kpp, a.max_pages * a.page_size);
     return hipGetLastError();
 }
