@@ -74,9 +74,16 @@ class _Lib:
         _i32p = ctypes.POINTER(ctypes.c_int32)
         lib.ref_attn_paged_fwd.argtypes = [_dp, _dp, _dp, _i32p, _i32p, c_int, c_int, c_int, c_int, c_int,
                                            c_int, c_int, c_int, c_double, c_int, _dp, _dp]
+        _u8 = ctypes.POINTER(ctypes.c_uint8)
+        _i8 = ctypes.POINTER(ctypes.c_int8)
+        lib.ref_e4m3_encode.argtypes = [_dp, ctypes.c_long, _u8]
+        lib.ref_e4m3_decode.argtypes = [_u8, ctypes.c_long, _dp]
+        lib.ref_fp8_quantize.argtypes = [_dp, c_int, c_int, c_int, c_int, c_int, _dp, c_int, _u8, _i8]
+        lib.ref_hadamard.argtypes = [_dp, ctypes.c_long, c_int, _dp, c_int, _dp]
         for f in ("ref_attn_probs", "ref_attn_fwd", "ref_attn_fwd_rows", "ref_attn_fwd_online",
                   "ref_attn_bwd", "ref_attn_fwd_ex", "ref_attn_fwd_rows_ex", "ref_attn_fwd_online_ex",
-                  "ref_attn_bwd_ex", "ref_attn_paged_fwd"):
+                  "ref_attn_bwd_ex", "ref_attn_paged_fwd", "ref_e4m3_encode", "ref_e4m3_decode",
+                  "ref_fp8_quantize", "ref_hadamard"):
             getattr(lib, f).restype = c_int
         self.lib = lib
 
@@ -188,6 +195,67 @@ def attn_paged_fwd(q, k_cache, v_cache, block_table, seqlens, scale: float,
     if rc != 0:
         raise ValueError(f"oracle paged_fwd rejected its arguments (code {rc})")
     return o, lse
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest FP8 E4M3 (OCP E4M3FN) codes of x, ties to even, saturating at +-448."""
+    a = _f64(x)
+    out = np.empty(a.shape, dtype=np.uint8)
+    _load().ref_e4m3_encode(_ptr(a), a.size, _ptr(out, ctypes.POINTER(ctypes.c_uint8)))
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().ref_e4m3_decode(_ptr(c, ctypes.POINTER(ctypes.c_uint8)), c.size, _ptr(out))
+    return out
+
+
+def hadamard(x, sigma, inverse_side: bool = False) -> np.ndarray:
+    """Rows of x [..., d] -> H (sigma o x) (times 1/d when inverse_side), H Sylvester of order d."""
+    a = _f64(x)
+    d = a.shape[-1]
+    sg = _f64(sigma).reshape(-1)
+    out = np.empty_like(a)
+    rc = _load().ref_hadamard(_ptr(a), a.size // d, d, _ptr(sg), int(inverse_side), _ptr(out))
+    if rc != 0:
+        raise ValueError("hadamard needs d a power of two")
+    return out
+
+
+def fp8_quantize(x, block: int, sigma=None, inverse_side: bool = False):
+    """Block quantization of [B, H, N, d] (after the optional incoherent map):
+    (codes uint8 [B,H,N,d], exponents int8 [B,H,ceil(N/block)])."""
+    a = _f64(x)
+    B, H, N, d = _shape(a)
+    sg = None if sigma is None else _f64(sigma).reshape(-1)
+    codes = np.empty(a.shape, dtype=np.uint8)
+    exps = np.empty((B, H, -(-N // block)), dtype=np.int8)
+    rc = _load().ref_fp8_quantize(_ptr(a), B, H, N, d, int(block), _ptr(sg), int(inverse_side),
+                                  _ptr(codes, ctypes.POINTER(ctypes.c_uint8)), _ptr(exps, ctypes.POINTER(ctypes.c_int8)))
+    if rc != 0:
+        raise ValueError("fp8_quantize: bad block or d")
+    return codes, exps
+
+
+def fp8_dequantize(codes, exps, block: int) -> np.ndarray:
+    v = e4m3_decode(codes)
+    N = v.shape[2]
+    e = np.repeat(np.asarray(exps, dtype=np.float64), block, axis=2)[:, :, :N]
+    return v * np.exp2(e)[..., None]
+
+
+def attn_fp8_fwd(q, k, v, scale: float, causal: bool = False, block: int = 64, sigma=None):
+    """FP8 forward reference: Q and K through the incoherent map (if sigma), Q, K
+    and V block-quantized to E4M3, exact attention of the dequantized values.
+    Returns (O, lse, quantized) with quantized = {name: (codes, exps)}."""
+    qc = fp8_quantize(q, block, sigma, False)
+    kc = fp8_quantize(k, block, sigma, True)
+    vc = fp8_quantize(v, block, None, False)
+    o, lse = attn_fwd(fp8_dequantize(*qc, block), fp8_dequantize(*kc, block), fp8_dequantize(*vc, block),
+                      scale, causal)
+    return o, lse, {"q": qc, "k": kc, "v": vc}
 
 
 def attn_fwd_rows(q, k, v, scale: float, rows, causal: bool = False, mask=None, window=None, slopes=None):
@@ -304,6 +372,24 @@ class Oracle:
 
     def attn_paged_fwd(self, *a, **kw):
         return self._swap(attn_paged_fwd, *a, **kw)
+
+    def e4m3_encode(self, *a, **kw):
+        return self._swap(e4m3_encode, *a, **kw)
+
+    def e4m3_decode(self, *a, **kw):
+        return self._swap(e4m3_decode, *a, **kw)
+
+    def hadamard(self, *a, **kw):
+        return self._swap(hadamard, *a, **kw)
+
+    def fp8_quantize(self, *a, **kw):
+        return self._swap(fp8_quantize, *a, **kw)
+
+    def fp8_dequantize(self, *a, **kw):
+        return self._swap(fp8_dequantize, *a, **kw)
+
+    def attn_fp8_fwd(self, *a, **kw):
+        return self._swap(attn_fp8_fwd, *a, **kw)
 
 
 def build_variant(src_text: str, out_path: str) -> str:

@@ -576,6 +576,113 @@ def pin_paged_invariances(orc):
     _close(l4, l5, 0.0, "single query lse")
 
 
+# ---------------------------------------------------------------------------
+# FP8 block quantization and incoherent processing ("FlashAttention 深度解析"
+# section 四).  Sources of truth: torch's float8_e4m3fn conversion (an
+# independent implementation of the OCP E4M3 format), scipy's Hadamard
+# matrix, exactness properties, and the pages' statement that block
+# quantization with incoherent processing has lower error than plain FP8.
+# ---------------------------------------------------------------------------
+
+def pin_e4m3_format(orc):
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.e4m3_decode(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref)), "NaN codes"
+    fin = ~np.isnan(ref)
+    assert np.array_equal(mine[fin], ref[fin]), "E4M3 code values"
+    assert mine[0x38] == 1.0 and mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9 and mine[0x08] == 2.0 ** -6
+    # encoding: round to nearest even within range (torch rounds the same way), saturation above
+    x = np.concatenate([np.linspace(-448, 448, 20001), _rng(130).standard_normal(5000) * 3,
+                        _rng(131).standard_normal(2000) * 1e-3, mine[fin],
+                        (mine[fin][:-1] + mine[fin][1:]) / 2])  # exact midpoints of neighbours
+    x = x[np.abs(x) <= 448]
+    enc = orc.e4m3_encode(x)
+    tref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # torch maps -0.0 results to 0x80 too; compare values, then signs of zeros
+    assert np.array_equal(orc.e4m3_decode(enc), torch.from_numpy(tref).view(torch.float8_e4m3fn)
+                          .to(torch.float64).numpy()), "E4M3 rounding"
+    sat = orc.e4m3_encode(np.array([448.5, 1e6, -500.0, -1e30]))
+    assert sat.tolist() == [0x7E, 0x7E, 0xFE, 0xFE], "saturation at 448"
+
+
+def pin_incoherent_map(orc):
+    from scipy.linalg import hadamard as sp_hadamard
+    for d in (4, 64, 128):
+        r = _rng(140 + d)
+        x = r.standard_normal((7, d))
+        sigma = r.choice([-1.0, 1.0], size=d)
+        H = sp_hadamard(d).astype(np.float64)
+        _close(orc.hadamard(x, sigma), (x * sigma) @ H.T, 1e-12, f"H (sigma o x), d={d}")
+        _close(orc.hadamard(x, sigma, True), (x * sigma) @ H.T / d, 1e-12, f"inverse side, d={d}")
+        # the pair of maps leaves every dot product unchanged
+        y = r.standard_normal((5, d))
+        _close(orc.hadamard(x, sigma) @ orc.hadamard(y, sigma, True).T, x @ y.T, 1e-11, f"QK^T kept, d={d}")
+
+
+def pin_block_quantization(orc):
+    r = _rng(150)
+    B, H, N, d, blk = 1, 2, 150, 16, 64
+    x = r.standard_normal((B, H, N, d)) * np.exp(r.standard_normal((B, H, N, 1)))
+    x[0, 1, 64:128] = 0.0                      # an all-zero block
+    x[0, 0, 5, 3] = 1e4                         # an outlier
+    codes, exps = orc.fp8_quantize(x, blk)
+    assert exps.shape == (1, 2, 3)
+    vals = orc.e4m3_decode(codes)
+    for h in range(H):
+        for bi in range(3):
+            blkx = x[0, h, bi * blk:(bi + 1) * blk]
+            e = int(exps[0, h, bi])
+            amax = np.abs(blkx).max()
+            if amax == 0:
+                assert e == 0 and np.all(codes[0, h, bi * blk:(bi + 1) * blk] == 0)
+                continue
+            assert amax / 2.0 ** e <= 448 < amax / 2.0 ** (e - 1), "smallest power-of-two scale"
+            # codes are the nearest E4M3 values of x / 2^e
+            assert np.array_equal(codes[0, h, bi * blk:(bi + 1) * blk], orc.e4m3_encode(blkx / 2.0 ** e))
+            deq = vals[0, h, bi * blk:(bi + 1) * blk] * 2.0 ** e
+            # error within half a step of the format at each magnitude (and below the subnormal step)
+            mag = np.maximum(np.abs(blkx) / 2.0 ** e, 2.0 ** -6)
+            step = 2.0 ** (np.floor(np.log2(mag)) - 3) * 2.0 ** e
+            assert np.all(np.abs(deq - blkx) <= step / 2 * (1 + 1e-12)), "within half a step"
+    deq_all = orc.fp8_dequantize(codes, exps, blk)
+    assert np.array_equal(deq_all, vals * np.exp2(np.repeat(exps.astype(float), blk, axis=2)[:, :, :N])[..., None])
+
+
+def pin_fp8_attention(orc):
+    # values already on the E4M3 grid with every block's largest magnitude in (224, 448]: no rounding
+    r = _rng(160)
+    B, H, N, d = 1, 2, 96, 16
+    grid = orc.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    def on_grid(seed):
+        g = _rng(seed).choice(grid[grid <= 8], size=(B, H, N, d)) * _rng(seed + 1).choice([-1, 1], size=(B, H, N, d))
+        g[:, :, ::64, 0] = 256.0  # pin each block's amax into (224, 448]
+        return g / 64.0 * 64.0
+    q, k, v = on_grid(161), on_grid(163), on_grid(165)
+    o8, l8, _ = orc.attn_fp8_fwd(q, k, v, 0.003, True, block=64)
+    o, l = orc.attn_fwd(q, k, v, 0.003, True)
+    _close(o8, o, 0.0, "fp8 path on exact inputs")
+    _close(l8, l, 0.0, "fp8 lse on exact inputs")
+    # the pages: block quantization with incoherent processing has lower error
+    # than plain (per-tensor) FP8, on inputs with rare large entries
+    N, d = 256, 64
+    def outliers(seed):
+        z = _rng(seed).standard_normal((1, 2, N, d))
+        m = _rng(seed + 1).random((1, 2, N, d)) < 0.001
+        return z + m * _rng(seed + 2).standard_normal((1, 2, N, d)) * 10.0
+    sc = 1 / np.sqrt(d)
+    for seed in (170, 200, 300):
+        q, k, v = outliers(seed), outliers(seed + 3), outliers(seed + 6)
+        o_ex, _ = orc.attn_fwd(q, k, v, sc, False)
+        sigma = _rng(seed + 9).choice([-1.0, 1.0], size=d)
+        o_plain, _, _ = orc.attn_fp8_fwd(q, k, v, sc, False, block=N)
+        o_blk, _, _ = orc.attn_fp8_fwd(q, k, v, sc, False, block=64, sigma=sigma)
+        e_plain = np.sqrt(np.mean((o_plain - o_ex) ** 2))
+        e_blk = np.sqrt(np.mean((o_blk - o_ex) ** 2))
+        assert e_blk < 0.9 * e_plain, f"block + incoherent {e_blk:.3e} vs plain {e_plain:.3e}"
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_rows_sum_to_one,
@@ -596,4 +703,8 @@ ALL_PINS = [
     pin_paged_brute_force,
     pin_paged_equals_square,
     pin_paged_invariances,
+    pin_e4m3_format,
+    pin_incoherent_map,
+    pin_block_quantization,
+    pin_fp8_attention,
 ]

@@ -39,6 +39,12 @@ MUTANTS = {
     "paged_causal_offset": ("long n = causal ? L - Nq + i + 1 : L;", "long n = causal ? L - Nq + i : L;"),
     "paged_no_scale": ("s[t] = scale * acc;", "s[t] = acc;"),
     "paged_v_from_k": ("const double* vt = v_cache +", "const double* vt = k_cache +"),
+    "e4m3_bias": ("ldexp(8.0 + m, e - 10)", "ldexp(8.0 + m, e - 9)"),
+    "e4m3_ties_odd": ("c = (lo & 1) ? hi : lo;", "c = (lo & 1) ? lo : hi;"),
+    "hadamard_sign": ("acc += (__builtin_popcountl((unsigned long)(i & j)) & 1) ? -t : t;",
+                      "acc += (__builtin_popcountl((unsigned long)(i | j)) & 1) ? -t : t;"),
+    "hadamard_k_side": ("y[i] = inverse_side ? acc / (double)d : acc;", "y[i] = acc;"),
+    "block_scale_floor": ("while (ldexp(amax, -(e - 1)) <= 448.0) e--;", "e--;"),
 }
 
 
