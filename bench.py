@@ -44,6 +44,7 @@ from workloads import accounting as A  # noqa: E402
 
 METRIC = "attention fwd/bwd TFLOP/s (4·B·H·N²·d, causal halved) and % of MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 bf16 FLOP/clk x 2.4 GHz, dense
+PEAK_FP8_TFLOPS = 5033.2   # 256 CU x 8192 fp8 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "bf16_causal_fwdbwd_b2h16n4096d128"
 
@@ -317,11 +318,20 @@ def main() -> int:
     window, slopes_np = W.workload_variant(w)
     slopes = torch.from_numpy(slopes_np).to(dev) if slopes_np is not None else None
     var = dict(window=window, alibi_slopes=slopes)
+    fp8 = w.precision == "fp8"
+    if fp8:
+        # inputs quantized once, outside the timed steps (the quantization is timed on its own below)
+        signs = torch.from_numpy(W.fp8_signs(w.d)).to(dev)
+        q8, qe = fa.quantize_fp8(q, signs, False, stream)
+        k8, ke = fa.quantize_fp8(k, signs, True, stream)
+        v8, ve = fa.quantize_fp8(v, None, False, stream)
 
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
-        if w.variant:
+        if fp8:
+            fa.fa_fwd_fp8(q8, qe, k8, ke, v8, ve, o, lse, w.scale, w.causal, stream)
+        elif w.variant:
             fa.fa_fwd_ex(q, k, v, o, lse, w.scale, w.causal, mask, stream=stream, **var)
         else:
             fa.fa_fwd(q, k, v, o, lse, w.scale, w.causal, mask, stream)
@@ -365,6 +375,17 @@ def main() -> int:
         res.update(bwd_prep_ms=statistics.median(t_prep), bwd_main_ms=statistics.median(t_main),
                    bwd_dq_ms=statistics.median(t_dq))
 
+    quant_ms = None
+    if fp8:
+        qa, qb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        qa.record(stream)
+        for _ in range(10):
+            fa.quantize_fp8(q, signs, False, stream)
+            fa.quantize_fp8(k, signs, True, stream)
+            fa.quantize_fp8(v, None, False, stream)
+        qb.record(stream)
+        torch.cuda.synchronize()
+        quant_ms = qa.elapsed_time(qb) / 10
     flops = A.workload_flops(w, mask_np)
     bytes_ = A.workload_bytes(w, mask_np)
     total_flops = flops["fwd"] + flops.get("bwd", 0.0)
@@ -391,17 +412,23 @@ def main() -> int:
         # fa_bwd_main computes four of the backward's five products (S, dP, dV, dK): 4/5 of its FLOPs
         dom_name, dom_ms, dom_flops = "bwd_bf16_kernel (fa_bwd_main)", res["bwd_main_ms"], flops["bwd"] * 4 / 5
         dom_api = "fa_bwd_main"
+    elif fp8:
+        dom_name, dom_ms, dom_flops = "fwd_fp8_kernel (fa_fwd_fp8)", res["fwd_ms"], flops["fwd"]
+        dom_api = "fa_fwd_fp8"
+        extra["fwd_pct_peak_fp8"] = round(100 * fwd_tflops / PEAK_FP8_TFLOPS, 2)
+        extra["quantize_ms"] = round(quant_ms, 4)
     else:
         dom_name, dom_ms, dom_flops = "fwd_bf16_kernel (fa_fwd)", res["fwd_ms"], flops["fwd"]
         dom_api = "fa_fwd"
     tr = measured_traffic(w.name, dom_api)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     roofline = {
         "bound": "mfma",
         "achieved": round(achieved, 2),
-        "peak": PEAK_BF16_TFLOPS,
+        "peak": peak,
         "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "frac": round(achieved / peak, 4),
         "traffic": None if tr is None else tr["traffic_bytes"],
         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         "traffic_vs_algorithmic": None if tr is None else round(tr["traffic_bytes"] / tr["algorithmic_bytes"], 3),
@@ -420,7 +447,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 e4m3 (fp32 accumulate)" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": w.name,
@@ -429,7 +456,8 @@ def main() -> int:
             "window": None if w.window is None else list(w.window),
             "alibi": w.alibi,
             "block_density": None if mask_np is None else float(mask_np.mean()),
-            "step": ("fa_fwd + fa_bwd" if w.backward else "fa_fwd") + (" (_ex variant)" if w.variant else ""),
+            "step": ("fa_fwd_fp8 (inputs quantized beforehand)" if fp8 else
+                     ("fa_fwd + fa_bwd" if w.backward else "fa_fwd") + (" (_ex variant)" if w.variant else "")),
             "step_flops": total_flops,
             "algorithmic_bytes": sum(bytes_.values()),
         },

@@ -28,12 +28,12 @@ __all__ = [
     "fa_bwd_workspace_size", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq", "fa_status_string", "fa_version",
     "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex", "fa_bwd_dq_ex", "Variant",
     "forward", "backward", "workspace", "fa_decode_workspace_size", "fa_decode_paged", "decode_workspace",
-    "decode_paged",
+    "decode_paged", "fa_fp8_quantize", "fa_fwd_fp8", "quantize_fp8", "forward_fp8", "FP8_BLOCK",
     "MASK_BLOCK", "ABI_VERSION",
 ]
 
 MASK_BLOCK = 128
-ABI_VERSION = 3  # FA_VERSION of the fa.h these argument lists follow
+ABI_VERSION = 4  # FA_VERSION of the fa.h these argument lists follow
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
 
@@ -80,12 +80,16 @@ def load():
     lib.fa_bwd_dq_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp, sz, vp]
     for name in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq",
                  "fa_version", "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex",
-                 "fa_bwd_dq_ex", "fa_decode_paged"):
+                 "fa_bwd_dq_ex", "fa_decode_paged", "fa_fp8_quantize", "fa_fwd_fp8"):
         getattr(lib, name).restype = i
     lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_decode_workspace_size.restype = sz
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_decode_paged.restype = i
+    lib.fa_fp8_quantize.argtypes = [vp, vp, vp, i, i, i, i, vp, i, vp]
+    lib.fa_fp8_quantize.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -305,6 +309,48 @@ def decode_paged(q, k_cache, v_cache, block_table, seqlens, scale: Optional[floa
     if ws is None:
         ws = decode_workspace(q, k_cache, block_table)
     fa_decode_paged(q, k_cache, v_cache, block_table, seqlens, o, lse, scale, causal, ws, stream)
+    return o, lse
+
+
+FP8_BLOCK = 64
+
+
+def fa_fp8_quantize(x, codes, exps, signs=None, k_side: bool = False, stream=None):
+    """Block-quantize bf16 x [B,H,N,d] to E4M3 codes (uint8, same shape) and int8
+    block exponents [B,H,ceil(N/64)]; signs (float [d] of +-1) applies the incoherent map."""
+    B, H, N, d = _dims(x)
+    _check(load().fa_fp8_quantize(_ptr(x), _ptr(codes), _ptr(exps), B, H, N, d, _ptr(signs), int(bool(k_side)),
+                                  _stream(stream)), "fa_fp8_quantize")
+
+
+def fa_fwd_fp8(q8, qe, k8, ke, v8, ve, o, lse, scale: float, causal: bool = False, stream=None):
+    B, H, N, d = _dims(q8)
+    _check(load().fa_fwd_fp8(_ptr(q8), _ptr(qe), _ptr(k8), _ptr(ke), _ptr(v8), _ptr(ve), _ptr(o), _ptr(lse), B, H,
+                             N, d, float(scale), int(bool(causal)), _stream(stream)), "fa_fwd_fp8")
+
+
+def quantize_fp8(x, signs=None, k_side: bool = False, stream=None):
+    """Allocate and fill (codes, exps) for a bf16 tensor on its device."""
+    import torch
+    B, H, N, d = _dims(x)
+    codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    exps = torch.empty((B, H, (N + FP8_BLOCK - 1) // FP8_BLOCK), dtype=torch.int8, device=x.device)
+    fa_fp8_quantize(x, codes, exps, signs, k_side, stream)
+    return codes, exps
+
+
+def forward_fp8(q, k, v, scale: Optional[float] = None, causal: bool = False, signs=None, stream=None):
+    """Quantize bf16 q, k, v (q and k through the incoherent map when signs is given)
+    and run the FP8 forward; returns (o bf16, lse)."""
+    import torch
+    B, H, N, d = _dims(q)
+    scale = _default_scale(d) if scale is None else scale
+    q8, qe = quantize_fp8(q, signs, False, stream)
+    k8, ke = quantize_fp8(k, signs, True, stream)
+    v8, ve = quantize_fp8(v, None, False, stream)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd_fp8(q8, qe, k8, ke, v8, ve, o, lse, scale, causal, stream)
     return o, lse
 
 

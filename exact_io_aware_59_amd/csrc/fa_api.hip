@@ -335,6 +335,52 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, con
     return fa::launch_decode_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_fp8_quantize(const void* x, uint8_t* codes, int8_t* exps, int B, int H, int N, int d, const float* signs,
+                    int k_side, void* stream) {
+    if (!x || !codes || !exps) return FA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(codes) || (signs && ((uintptr_t)signs & 3))) return FA_ERR_INVALID_ARG;
+    if (k_side != 0 && k_side != 1) return FA_ERR_INVALID_ARG;
+    const int st = check_sizes(B, H, N, d, 1.0f, nullptr);
+    if (st != FA_OK) return st;
+    const size_t xb = (size_t)B * H * N * d * 2, cb = (size_t)B * H * N * d;
+    const size_t eb = (size_t)B * H * ((N + FA_FP8_BLOCK - 1) / FA_FP8_BLOCK);
+    if (overlap(codes, cb, x, xb) || overlap(exps, eb, x, xb) || overlap(exps, eb, codes, cb)) return FA_ERR_INVALID_ARG;
+    if (signs && (overlap(codes, cb, signs, (size_t)d * 4) || overlap(exps, eb, signs, (size_t)d * 4)))
+        return FA_ERR_INVALID_ARG;
+    fa::F8QuantArgs a;
+    a.x = x; a.codes = codes; a.exps = exps;
+    a.BH = B * H; a.N = N; a.d = d;
+    a.signs = signs; a.k_side = k_side;
+    a.stream = (hipStream_t)stream;
+    return fa::launch_fp8_quantize(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8(const uint8_t* q, const int8_t* q_exps, const uint8_t* k, const int8_t* k_exps, const uint8_t* v,
+               const int8_t* v_exps, void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+               void* stream) {
+    if (!q || !q_exps || !k || !k_exps || !v || !v_exps || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3))
+        return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    const int st = check_sizes(B, H, N, d, scale, nullptr);
+    if (st != FA_OK) return st;
+    const size_t cb = (size_t)B * H * N * d, ob = cb * 2, lb = (size_t)B * H * N * 4;
+    const size_t eb = (size_t)B * H * ((N + FA_FP8_BLOCK - 1) / FA_FP8_BLOCK);
+    const void* ins[] = {q, k, v, q_exps, k_exps, v_exps};
+    const size_t in_bytes[] = {cb, cb, cb, eb, eb, eb};
+    for (int i = 0; i < 6; i++)
+        if (overlap(o, ob, ins[i], in_bytes[i]) || overlap(lse, lb, ins[i], in_bytes[i])) return FA_ERR_INVALID_ARG;
+    if (overlap(o, ob, lse, lb)) return FA_ERR_INVALID_ARG;
+    fa::F8FwdArgs a;
+    a.q = q; a.qe = q_exps; a.k = k; a.ke = k_exps; a.v = v; a.ve = v_exps;
+    a.o = o; a.lse = lse;
+    a.BH = B * H; a.N = N; a.d = d; a.causal = causal;
+    a.c = fmaxf(fabsf(scale) * fa::kLog2eHost, 1e-30f);
+    a.qsign = scale < 0.f ? 0x80808080u : 0u;
+    a.stream = (hipStream_t)stream;
+    return fa::launch_fwd_fp8(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";

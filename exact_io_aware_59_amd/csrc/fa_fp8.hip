@@ -1,0 +1,386 @@
+// FP8 forward for gfx950: block quantization with the incoherent map, and the
+// fused forward on the FP8 matrix cores ("FlashAttention 深度解析" section 四:
+// FlashAttention-3 adds FP8 block quantization with incoherent processing).
+//
+//  1. fp8_quant_kernel: one workgroup per 64-row block of one (b, h) slice of
+//     Q, K or V.  Rows are widened to fp64 in LDS; with a sign vector the
+//     incoherent map x -> H (sigma o x) (Sylvester Hadamard matrix, a fast
+//     Walsh-Hadamard transform in log2(d) butterfly stages; times 1/d for K) is
+//     applied exactly (sums of bf16 values fit fp64).  The block gets the
+//     smallest power-of-two scale 2^e with amax / 2^e <= 448, and every value
+//     becomes the nearest FP8 E4M3 code of x / 2^e (ties to even, computed in
+//     fp64 with round-to-nearest-even).  Power-of-two scales are exactly the
+//     E8M0 block scales the gfx950 matrix instructions apply.
+//  2. fwd_fp8_kernel: the Q-outer forward of the bf16 kernel (4 waves x 32
+//     queries, 64-key K/V tiles copied HBM -> LDS with buffer_load ... lds,
+//     two stages) with both products on v_mfma_scale_f32_32x32x64_f8f6f4:
+//     S^T = K Q^T with the K and Q block exponents as the instruction's scales
+//     (S comes out dequantized), then O^T += V^T P^T with P = 2^(c s - c m)
+//     times 2^8 rounded to E4M3 (its scale 2^-8 and the V block exponent are
+//     again the instruction's scales).  The reference max follows the row max
+//     exactly, so P <= 1 and 2^8 P stays inside E4M3's range with 17 binades
+//     below it.  V^T is read with ds_read_b64_tr_b8 in the key order of the
+//     S^T accumulator, so P never leaves registers.  The row sum uses the fp32
+//     probabilities.
+#include <type_traits>
+
+#include "fa_common.h"
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+constexpr int kF8Block = 64;   // rows per quantization block = keys per tile
+constexpr int kF8Waves = 4;
+constexpr int kF8Threads = 64 * kF8Waves;
+constexpr int kF8Br = 32 * kF8Waves;  // queries per workgroup
+constexpr int kPExp = 8;              // P is stored as 2^8 p
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// 1. quantization
+// ---------------------------------------------------------------------------
+
+// Nearest E4M3 code of x (ties to even), saturating at +-448.
+__device__ __forceinline__ uint32_t e4m3_rne(double x) {
+    const uint32_t sign = signbit(x) ? 0x80u : 0u;
+    const double a = fabs(x);
+    if (!(a < 448.0)) return sign | 0x7Eu;
+    int e2;
+    frexp(a, &e2);                  // a = f 2^e2, f in [0.5, 1) (a > 0)
+    int E = a > 0.0 ? max(e2 - 1, -6) : -6;  // binade; subnormals share the quantum 2^-9
+    double q = rint(ldexp(a, 3 - E));       // units of the binade's quantum
+    if (q >= 16.0) {                         // rounded up into the next binade
+        q = 8.0;
+        E++;
+    }
+    if (E > 8 || (E == 8 && q > 14.0)) return sign | 0x7Eu;
+    const uint32_t code = q < 8.0 ? (uint32_t)q : ((uint32_t)(E + 7) << 3) | (uint32_t)(q - 8.0);
+    return sign | code;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void fp8_quant_kernel(const bf16* __restrict__ X, uint8_t* __restrict__ codes,
+                                                        int8_t* __restrict__ exps, int N, int nblk,
+                                                        const float* __restrict__ signs, int k_side) {
+    __shared__ double t[kF8Block][D];
+    __shared__ double red[256];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+    const int r0 = blk * kF8Block;
+    const int rows = min(kF8Block, N - r0);
+    const bf16* xh = X + ((size_t)bh * N + r0) * D;
+    // widen (and multiply by the signs)
+    for (int i = tid; i < kF8Block * D; i += 256) {
+        const int r = i / D, c = i % D;
+        double v = r < rows ? (double)(float)xh[i] : 0.0;
+        if (signs) v *= (double)signs[c];
+        t[r][c] = v;
+    }
+    __syncthreads();
+    if (signs) {
+        // fast Walsh-Hadamard transform of every row: (u, v) -> (u + v, u - v)
+        for (int len = 1; len < D; len <<= 1) {
+            for (int p = tid; p < kF8Block * D / 2; p += 256) {
+                const int r = p / (D / 2), pr = p % (D / 2);
+                const int i = (pr / len) * 2 * len + (pr % len), j = i + len;
+                const double u = t[r][i], v = t[r][j];
+                t[r][i] = u + v;
+                t[r][j] = u - v;
+            }
+            __syncthreads();
+        }
+        if (k_side)
+            for (int i = tid; i < kF8Block * D; i += 256) t[i / D][i % D] *= 1.0 / D;  // exact: D a power of two
+        __syncthreads();
+    }
+    // block amax
+    double m = 0.0;
+    for (int i = tid; i < rows * D; i += 256) m = fmax(m, fabs(t[i / D][i % D]));
+    red[tid] = m;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) red[tid] = fmax(red[tid], red[tid + s]);
+        __syncthreads();
+    }
+    const double amax = red[0];
+    // smallest e with amax / 2^e <= 448, within the E8M0 range
+    int e = 0;
+    if (amax > 0.0) {
+        int e2;
+        frexp(amax / 448.0, &e2);
+        e = e2;
+        while (ldexp(amax, -e) > 448.0) e++;
+        while (ldexp(amax, -(e - 1)) <= 448.0) e--;
+    }
+    e = max(-127, min(127, e));
+    if (tid == 0) exps[(size_t)bh * nblk + blk] = (int8_t)e;
+    // codes, four per 32-bit store
+    uint8_t* ch = codes + ((size_t)bh * N + r0) * D;
+    for (int i = 4 * tid; i < rows * D; i += 4 * 256) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) w |= e4m3_rne(ldexp(t[(i + j) / D][(i + j) % D], -e)) << (8 * j);
+        *reinterpret_cast<uint32_t*>(ch + i) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2. forward
+// ---------------------------------------------------------------------------
+template <int D>
+struct F8Cfg {
+    static constexpr int RS = D + 16;                  // LDS row stride in bytes (16 * odd mod 256)
+    static constexpr int TILE = kF8Block * RS;         // bytes of one padded 64-row tile
+    static constexpr int SEGS = TILE / 1024;           // 1 KB copies per tile
+    static constexpr int NKK = D / 64;                 // k-steps of S^T (64 dims each)
+    static constexpr int NDM = D / 32;                 // 32-dim blocks of O^T
+    static_assert(SEGS * 1024 == TILE, "tiles must be whole 1 KB copies");
+};
+
+template <int D>
+__device__ __forceinline__ void f8_load_tile(rsrc_t r, uint8_t* tile, int kv0, int wave, int lane) {
+    using C = F8Cfg<D>;
+#pragma unroll
+    for (int i = 0; i < (C::SEGS + kF8Waves - 1) / kF8Waves; i++) {
+        const int s = i * kF8Waves + wave;
+        if (s < C::SEGS) {
+            const int el = s * 1024 + lane * 16;
+            const int row = el / C::RS;
+            int col = el - row * C::RS;
+            col = col < D ? col : 0;  // padding: re-read the row's first chunk (never used)
+            buf_load16_lds(r, tile + s * 1024, (uint32_t)(kv0 + row) * D + col);
+        }
+    }
+}
+
+__device__ __forceinline__ i32x8 lds_read32(const uint8_t* p) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
+    return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+__device__ __forceinline__ i32x2 lds_tr8(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (i32x2 __attribute__((address_space(3)))*)((__attribute__((address_space(3))) uint8_t*)p));
+}
+
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int scale_a, int scale_b) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
+    const uint8_t* __restrict__ Q, const int8_t* __restrict__ QE, const uint8_t* __restrict__ K,
+    const int8_t* __restrict__ KE, const uint8_t* __restrict__ V, const int8_t* __restrict__ VE,
+    bf16* __restrict__ O, float* __restrict__ LSE, int N, float c, uint32_t qsign, int nqb, int n_items) {
+    using C = F8Cfg<D>;
+    __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[C::TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int nblk = (N + kF8Block - 1) / kF8Block;
+
+    // work item -> (bh, up to two query blocks); causal pairs block p with nqb-1-p
+    const int item = xcd_remap(blockIdx.x, n_items);
+    int bh, qblk[2], nb;
+    if (CAUSAL) {
+        const int npair = (nqb + 1) / 2;
+        bh = item / npair;
+        const int p = item % npair;
+        qblk[0] = nqb - 1 - p;
+        qblk[1] = p;
+        nb = (qblk[1] == qblk[0]) ? 1 : 2;
+    } else {
+        bh = item / nqb;
+        qblk[0] = item % nqb;
+        qblk[1] = -1;
+        nb = 1;
+    }
+    const size_t head_off = (size_t)bh * N * D;
+    const uint32_t head_bytes = (uint32_t)N * D;
+    const rsrc_t rk = make_rsrc(K + head_off, head_bytes);
+    const rsrc_t rv = make_rsrc(V + head_off, head_bytes);
+    const int8_t* ke = KE + (size_t)bh * nblk;
+    const int8_t* ve = VE + (size_t)bh * nblk;
+
+    // per-lane LDS offsets: K rows (A operand of S^T), V^T transposing reads
+    const int k_lane = l32 * C::RS + 32 * h;
+    int v_lane;
+    {
+        const int G = lane >> 4, i = lane & 15;
+        const int jj = i >> 1, half = i & 1;
+        const int key = 8 * (jj >> 2) + 4 * (G >> 1) + (jj & 3);   // + 16 r8 per read
+        v_lane = key * C::RS + 16 * (G & 1) + 8 * half;            // + 32 dm per 32-dim block
+    }
+
+    for (int bi = 0; bi < nb; bi++) {
+        const int q0 = qblk[bi] * kF8Br;
+        const int qw = q0 + wave * 32;
+        const int my_q = qw + l32;
+        const int q_end = min(N, q0 + kF8Br);
+        const int kv_hi = CAUSAL ? q_end : N;
+        const int ntiles = (kv_hi + kF8Block - 1) / kF8Block;
+        const int sq = 127 + QE[(size_t)bh * nblk + min(qw, N - 1) / kF8Block];
+
+        // Q fragments (B operand of S^T): 32 bytes of this lane's query per 64 dims
+        i32x8 qf[C::NKK];
+        {
+            const rsrc_t rq = make_rsrc(Q + head_off, head_bytes);
+#pragma unroll
+            for (int kk = 0; kk < C::NKK; kk++) {
+                const uint32_t off = (uint32_t)my_q * D + 64 * kk + 32 * h;
+                const u32x4 a = buf_load16(rq, off) ^ qsign;
+                const u32x4 b = buf_load16(rq, off + 16) ^ qsign;
+                qf[kk] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+            }
+        }
+        f32x16 oacc[C::NDM];
+#pragma unroll
+        for (int dm = 0; dm < C::NDM; dm++) oacc[dm] = f32x16{};
+        float m_ref = -INFINITY, l_part = 0.f;
+
+        if (ntiles > 0) {
+            f8_load_tile<D>(rk, kbuf0, 0, wave, lane);
+            f8_load_tile<D>(rv, vbuf0, 0, wave, lane);
+        }
+        wait_vmem();
+        __syncthreads();
+
+        auto step = [&](auto parity, int it) {
+            constexpr int P = decltype(parity)::value;
+            const uint8_t* kt = P ? kbuf1 : kbuf0;
+            const uint8_t* vt = P ? vbuf1 : vbuf0;
+            const int kv0 = it * kF8Block;
+            if (it + 1 < ntiles) {
+                f8_load_tile<D>(rk, P ? kbuf0 : kbuf1, kv0 + kF8Block, wave, lane);
+                f8_load_tile<D>(rv, P ? vbuf0 : vbuf1, kv0 + kF8Block, wave, lane);
+            }
+            const int sk = 127 + ke[it], sv_ = 127 + ve[it];
+            // S^T for 64 keys: two 32-key blocks
+            f32x16 s[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+                s[kb] = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < C::NKK; kk++)
+                    s[kb] = mfma_f8(lds_read32(kt + k_lane + kb * 32 * C::RS + 64 * kk), qf[kk], s[kb], sk, sq);
+            }
+            if ((CAUSAL && kv0 + kF8Block - 1 > qw) || kv0 + kF8Block > N) {
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        s[kb][r] = ((CAUSAL && key > my_q) || key >= N) ? -INFINITY : s[kb][r];
+                    }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[kb][r]);
+            mx = xhalf_max(mx);
+            // the reference follows the exact running max, so p <= 1
+            if (mx > m_ref) {
+                const float alpha = m_ref == -INFINITY ? 0.f : exp2f_hw((m_ref - mx) * c);
+                m_ref = mx;
+                l_part *= alpha;
+#pragma unroll
+                for (int dm = 0; dm < C::NDM; dm++) oacc[dm] *= alpha;
+            }
+            const float mc = m_ref == -INFINITY ? 0.f : m_ref * c;
+            // P (times 2^8) to E4M3, in the accumulator's key order: byte 16 kb + r
+            i32x8 pb;
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int w = 0; w < 4; w++) {
+                    float p[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        p[e] = exp2f_hw(__builtin_fmaf(s[kb][4 * w + e], c, -mc));
+                        ls += p[e];
+                    }
+                    int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * 256.f, p[1] * 256.f, 0, false);
+                    word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * 256.f, p[3] * 256.f, word, true);
+                    pb[4 * kb + w] = word;
+                }
+            l_part += ls;
+            // O^T += V^T P^T: A = V^T from four transposing reads (8 keys each)
+#pragma unroll
+            for (int dm = 0; dm < C::NDM; dm++) {
+                i32x8 va;
+#pragma unroll
+                for (int r8 = 0; r8 < 4; r8++) {
+                    const i32x2 t2 = lds_tr8(vt + v_lane + r8 * 16 * C::RS + 32 * dm);
+                    va[2 * r8] = t2[0];
+                    va[2 * r8 + 1] = t2[1];
+                }
+                oacc[dm] = mfma_f8(va, pb, oacc[dm], sv_, 127 - kPExp);
+            }
+            wait_vmem();
+            __syncthreads();
+        };
+        int it = 0;
+        for (; it + 1 < ntiles; it += 2) {
+            step(std::integral_constant<int, 0>{}, it);
+            step(std::integral_constant<int, 1>{}, it + 1);
+        }
+        if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
+
+        // epilogue: one division per row, bf16 output, lse (rows >= N dropped)
+        const float l = xhalf_sum(l_part);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const rsrc_t ro = make_rsrc(O + head_off, head_bytes * 2);
+#pragma unroll
+        for (int dm = 0; dm < C::NDM; dm++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                bf16x4 v4;
+#pragma unroll
+                for (int e = 0; e < 4; e++) v4[e] = (bf16)(oacc[dm][4 * g + e] * inv);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), ro,
+                                                      (uint32_t)(my_q * D + 32 * dm + 8 * g + 4 * h) * 2, 0, 0);
+            }
+        if (h == 0 && my_q < N) LSE[(size_t)bh * N + my_q] = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
+        __syncthreads();  // the next query block reuses the tiles
+    }
+}
+
+template <int D>
+hipError_t launch_quant_d(const F8QuantArgs& a) {
+    const int nblk = (a.N + kF8Block - 1) / kF8Block;
+    hipLaunchKernelGGL(fp8_quant_kernel<D>, dim3(a.BH * nblk), dim3(256), 0, a.stream, (const bf16*)a.x, a.codes,
+                       a.exps, a.N, nblk, a.signs, a.k_side);
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd8_d(const F8FwdArgs& a) {
+    const int nqb = (a.N + kF8Br - 1) / kF8Br;
+    const int n_items = a.BH * (CAUSAL ? (nqb + 1) / 2 : nqb);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(n_items), dim3(kF8Threads), 0, a.stream, a.q, a.qe, a.k,
+                       a.ke, a.v, a.ve, (bf16*)a.o, a.lse, a.N, a.c, a.qsign, nqb, n_items);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fp8_quantize(const F8QuantArgs& a) {
+    return a.d == 128 ? launch_quant_d<128>(a) : launch_quant_d<64>(a);
+}
+
+hipError_t launch_fwd_fp8(const F8FwdArgs& a) {
+    if (a.d == 128) return a.causal ? launch_fwd8_d<128, true>(a) : launch_fwd8_d<128, false>(a);
+    return a.causal ? launch_fwd8_d<64, true>(a) : launch_fwd8_d<64, false>(a);
+}
+
+}  // namespace fa

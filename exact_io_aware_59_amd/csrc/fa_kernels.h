@@ -73,6 +73,33 @@ struct DecArgs {
     hipStream_t stream;
 };
 
+// FP8 block quantization (see fa_fp8_quantize in fa.h).
+struct F8QuantArgs {
+    const void* x;          // bf16 [BH][N][d]
+    uint8_t* codes;         // [BH][N][d] E4M3
+    int8_t* exps;           // [BH][ceil(N/64)] block exponents
+    int BH, N, d;
+    const float* signs;     // [d] +-1 or null (incoherent map)
+    int k_side;             // 1: times 1/d (the K side of the map)
+    hipStream_t stream;
+};
+
+// FP8 forward (see fa_fwd_fp8 in fa.h).
+struct F8FwdArgs {
+    const uint8_t* q;
+    const int8_t* qe;
+    const uint8_t* k;
+    const int8_t* ke;
+    const uint8_t* v;
+    const int8_t* ve;
+    void* o;                // bf16 [BH][N][d]
+    float* lse;
+    int BH, N, d, causal;
+    float c;                // |scale| * log2(e)
+    uint32_t qsign;         // 0x80808080 when scale < 0 (Q codes negated), else 0
+    hipStream_t stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_bwd_bf16(const BwdArgs& a);  // the three stages below, in order
 hipError_t launch_bwd_prep_bf16(const BwdArgs& a);
@@ -81,5 +108,7 @@ hipError_t launch_bwd_dq_bf16(const BwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_f32(const BwdArgs& a);
 hipError_t launch_decode_bf16(const DecArgs& a);
+hipError_t launch_fp8_quantize(const F8QuantArgs& a);
+hipError_t launch_fwd_fp8(const F8FwdArgs& a);
 
 }  // namespace fa

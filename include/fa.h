@@ -69,7 +69,7 @@ typedef enum {
 } fa_status;
 
 #define FA_MASK_BLOCK 128 /* block-mask granularity in rows and columns */
-#define FA_VERSION 3
+#define FA_VERSION 4
 
 /*
  * Local window and ALiBi, the two further built-in variants "FlashAttention
@@ -216,6 +216,38 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, con
                     const int32_t* seqlens, void* o, float* lse, int B, int H, int H_kv, int Nq, int d,
                     int num_pages, int page_size, int max_pages, float scale, int causal, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * FP8 forward ("FlashAttention 深度解析" section 四: FlashAttention-3's FP8
+ * block quantization with incoherent processing; the pages give no formulas,
+ * the definitions taken are these).  Format: FP8 E4M3 (OCP E4M3FN: bias 7,
+ * largest finite 448, no infinities), the format the gfx950 matrix cores read.
+ *
+ * fa_fp8_quantize: x bf16 [B][H][N][d] -> codes uint8 [B][H][N][d] and block
+ * exponents exps int8 [B][H][ceil(N/FA_FP8_BLOCK)].  Each (b, h) slice is cut
+ * into blocks of FA_FP8_BLOCK rows; with signs (device float[d] of +-1, or
+ * NULL) every row first goes through the incoherent map x -> H (signs o x), H
+ * the Sylvester Hadamard matrix of order d, times 1/d when k_side = 1 (use
+ * k_side = 0 for Q, 1 for K, the same signs for both and NULL for V: then
+ * Q' K'^T = Q K^T).  A block gets the smallest e with max|x| / 2^e <= 448
+ * (e = 0 for an all-zero block, clamped to [-127, 127]) and codes = the nearest
+ * E4M3 value of x / 2^e, ties to even.  Deterministic and exact (the map is
+ * computed in fp64, where these sums are exact).
+ *
+ * fa_fwd_fp8: exact-attention forward of the dequantized tensors
+ * (code * 2^exp), with both matrix products on the FP8 matrix cores: S = Q K^T
+ * from the codes (block exponents applied by the instruction), P rounded to
+ * E4M3 (as 2^8 P, P <= 1) for P V; o bf16 [B][H][N][d] and lse float [B][H][N]
+ * as fa_fwd.  causal 0 or 1; no block mask or window.  The result differs from
+ * exact attention of the dequantized tensors by the rounding of P.
+ * Limits as fa_fwd; codes 16-byte aligned.
+ */
+#define FA_FP8_BLOCK 64
+int fa_fp8_quantize(const void* x, uint8_t* codes, int8_t* exps, int B, int H, int N, int d, const float* signs,
+                    int k_side, void* stream);
+int fa_fwd_fp8(const uint8_t* q, const int8_t* q_exps, const uint8_t* k, const int8_t* k_exps, const uint8_t* v,
+               const int8_t* v_exps, void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+               void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* fa_status_string(int status);

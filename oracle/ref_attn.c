@@ -493,7 +493,8 @@ int ref_attn_paged_fwd(const double* q, const double* k_cache, const double* v_c
  *   blocks      each (b, h) slice of Q, K and V is cut into blocks of `block`
  *               rows (the last may be short); a block gets the power-of-two
  *               scale 2^e, e = the smallest integer with amax / 2^e <= 448
- *               (e = 0 for an all-zero block), and codes = E4M3(x / 2^e);
+ *               (e = 0 for an all-zero block; e kept within [-127, 127], the
+ *               range of an E8M0 scale), and codes = E4M3(x / 2^e);
  *   incoherent  Q and K are first multiplied along the head dimension by the
  *               same random orthogonal map: x -> H (sigma o x), H the Sylvester
  *               Hadamard matrix of order d and sigma a vector of random signs,
@@ -565,6 +566,8 @@ static void ref_quant_blocks(const double* x, long rows, long d, long block, uin
             while (ldexp(amax, -e) > 448.0) e++;      /* guard the log2 rounding */
             while (ldexp(amax, -(e - 1)) <= 448.0) e--;
         }
+        if (e < -127) e = -127;  /* the range of an E8M0 block scale */
+        if (e > 127) e = 127;
         exps[bi] = (int8_t)e;
         for (long i = b0 * d; i < b1 * d; i++) codes[i] = (uint8_t)ref_e4m3_code(ldexp(x[i], -e));
     }

@@ -34,13 +34,14 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_bwd_workspace_size",
-                          "fa_status_string", "fa_version", "fa_decode_paged", "fa_decode_workspace_size"}
+                          "fa_status_string", "fa_version", "fa_decode_paged", "fa_decode_workspace_size",
+                          "fa_fp8_quantize", "fa_fwd_fp8"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status(lib):
-    assert fa.fa_version() == fa.ABI_VERSION == 3
+    assert fa.fa_version() == fa.ABI_VERSION == 4
     for s in range(5):
         assert fa.fa_status_string(s)
     assert fa.fa_status_string(99) == "unknown status"
@@ -196,3 +197,33 @@ def test_decode_validation(lib):
     assert _dec(lib, o=P1) == E                  # o aliases q
     assert _dec(lib, ws=P1 + BIG) == E           # workspace inside the K cache
     assert _dec(lib, max_pages=1 << 26, page_size=64) == E  # capacity >= 2^31
+
+
+def test_fp8_validation(lib):
+    E, U = 1, 2
+    q8, k8, v8 = P1, P1 + BIG, P1 + 2 * BIG
+    qe, ke, ve = P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG
+    o, lse = P1 + 6 * BIG, P1 + 7 * BIG
+
+    def fwd(**kw):
+        a = dict(q=q8, qe=qe, k=k8, ke=ke, v=v8, ve=ve, o=o, lse=lse, B=1, H=2, N=300, d=128, scale=0.1, causal=1)
+        a.update(kw)
+        return lib.fa_fwd_fp8(a["q"], a["qe"], a["k"], a["ke"], a["v"], a["ve"], a["o"], a["lse"], a["B"], a["H"],
+                              a["N"], a["d"], ctypes.c_float(a["scale"]), a["causal"], None)
+    assert fwd(q=0) == E and fwd(ve=0) == E and fwd(lse=0) == E
+    assert fwd(d=96) == U and fwd(N=0) == E and fwd(causal=3) == E
+    assert fwd(scale=float("inf")) == E
+    assert fwd(q=P1 + 4) == E               # codes must be 16-byte aligned
+    assert fwd(o=P1 + 8) == E               # o misaligned
+    assert fwd(o=q8) == E                   # o aliases the Q codes
+    assert fwd(lse=ke) == E                 # lse aliases K's exponents
+
+    def quant(**kw):
+        a = dict(x=P1, codes=P1 + BIG, exps=P1 + 2 * BIG, B=1, H=1, N=100, d=64, signs=None, k_side=0)
+        a.update(kw)
+        return lib.fa_fp8_quantize(a["x"], a["codes"], a["exps"], a["B"], a["H"], a["N"], a["d"], a["signs"],
+                                   a["k_side"], None)
+    assert quant(x=0) == E and quant(codes=0) == E and quant(exps=0) == E
+    assert quant(d=32) == U and quant(k_side=2) == E
+    assert quant(codes=P1 + 100) == E       # codes overlap x
+    assert quant(signs=P1 + 2 * BIG + 1) == E  # signs misaligned

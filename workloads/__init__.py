@@ -37,6 +37,7 @@ class Workload:
     backward: bool = False       # the workload also runs the recompute backward
     window: Optional[Tuple[int, int]] = None  # local window (left, right); negative = unbounded
     alibi: bool = False          # add the per-head ALiBi bias with alibi_slopes(H)
+    precision: str = "bf16"      # "fp8": the inputs are block-quantized to E4M3 for the FP8 forward
     description: str = ""
 
     @property
@@ -71,6 +72,9 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("bf16_blocksparse_fwd_b1h8n65536d64", 1, 8, 65536, 64, "bf16",
                  mask="band2_random", density=1.0 / 8,
                  description="bf16 block-sparse forward at 64K, 128x128 blocks, density 1/8"),
+        Workload("fp8_causal_fwd_b2h16n4096d128", 2, 16, 4096, 128, "bf16", causal=True, precision="fp8",
+                 description="FP8 causal forward (E4M3, 64-row block scales, incoherent map on Q and K) "
+                             "of the benchmarked step's shape"),
         Workload("bf16_window_alibi_fwdbwd_b2h16n4096d128", 2, 16, 4096, 128, "bf16", causal=True,
                  backward=True, window=(1023, -1), alibi=True,
                  description="bf16 causal sliding window of 1024 keys with ALiBi, forward + backward"),
@@ -78,8 +82,13 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 # Seed offsets per tensor (base seed s): q=s, k=s+1, v=s+2, do=s+3, mask=s+4, rows=s+5,
-# page table=s+6, sequence lengths=s+7.
-SEED_Q, SEED_K, SEED_V, SEED_DO, SEED_MASK, SEED_ROWS, SEED_PAGES, SEED_LENS = range(8)
+# page table=s+6, sequence lengths=s+7, incoherent-map signs=s+8.
+SEED_Q, SEED_K, SEED_V, SEED_DO, SEED_MASK, SEED_ROWS, SEED_PAGES, SEED_LENS, SEED_SIGNS = range(9)
+
+
+def fp8_signs(d: int, seed: int = 0) -> np.ndarray:
+    """The random sign vector of the incoherent map (float32 +-1, length d)."""
+    return np.random.default_rng(seed + SEED_SIGNS).choice([-1.0, 1.0], size=d).astype(np.float32)
 
 
 @dataclass(frozen=True)
