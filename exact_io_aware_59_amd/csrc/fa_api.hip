@@ -254,7 +254,7 @@ int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, c
 // per range; kpp is a multiple of the 32-key tile.
 static void decode_plan(int B, int H, int H_kv, int Nq, int page_size, int max_pages, int& n_parts, int& kpp) {
     const long long cap = (long long)max_pages * page_size;
-    const long long groups = (long long)B * H_kv * (((long long)(H / H_kv) * Nq + 31) / 32);
+    const long long groups = (long long)B * H_kv * (((long long)(H / H_kv) * Nq + 15) / 16);
     const long long want = (2048 + groups - 1) / groups;
     const long long most = (cap + 255) / 256;
     long long parts = want < 1 ? 1 : want;

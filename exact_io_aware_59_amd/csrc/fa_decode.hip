@@ -10,18 +10,20 @@
 //
 // Split along the keys ("FlashAttention 深度解析" section 二: partial results
 // over disjoint key ranges merge exactly with the running max / sum rule):
-//   1. decode_kernel: one wave per (sequence, KV head, group of 32 query rows,
+//   1. decode_kernel: one wave per (sequence, KV head, group of 16 query rows,
 //      key range).  The query rows of a KV head (its grouped query heads times
-//      the new positions) are the 32 columns of S^T = K Q^T; per 32-key tile
-//      the wave computes S^T on the matrix cores, folds it into its running
-//      max and sum and accumulates O^T += V^T P^T, like the forward kernel.
-//      K tiles go from HBM straight into registers (their rows are the MFMA A
-//      operand); V tiles go HBM -> LDS by buffer_load ... lds into a swizzled
-//      per-wave ring of two and are read transposed; the next tile is in
-//      flight while one is computed, and two workgroups (eight waves) share a
-//      CU.  The wave writes (O unnormalized, max,
-//      sum) for its key range, or the final O and lse when one range covers
-//      the sequence.
+//      the new positions) are the 16 columns of S^T = K Q^T on 16x16x32
+//      products: with a handful of useful rows, the narrow shape halves the
+//      matrix and softmax work per K/V byte against 32-wide products.  Per
+//      32-key tile the wave computes S^T, folds it into its running max and
+//      sum and accumulates O^T += V^T P^T.  K rows go from HBM straight into
+//      registers (their rows are the A operand, 64 contiguous bytes per row
+//      and load); V rows go HBM -> LDS by buffer_load ... lds into padded rows
+//      and are read transposed in the key order of the S^T results, so P
+//      never leaves registers.  The next tile is in flight while one is
+//      computed; a workgroup is eight waves (one per CU).  The wave
+//      writes (O unnormalized, max, sum) for its key range, or the final O
+//      and lse when one range covers the sequence.
 //   2. decode_merge_kernel: per query row (one wave), O = sum_p w_p O_p /
 //      sum_p w_p l_p with w_p = 2^(m_p - max_p m_p), lse = ln 2 (max + log2 sum).
 // Rows past a sequence's length and pages outside the cache read as zero
@@ -34,35 +36,41 @@
 namespace fa {
 namespace {
 
-// Transposing pair read (A operand of O^T += V^T P^T) at two byte offsets of a swizzled tile.
-__device__ __forceinline__ bf16x8 lds_tr_pair_v(const bf16* base, uint32_t lo_off, uint32_t hi_off) {
-    const bf16x4 lo = lds_read_tr4(base, lo_off / 2);
-    const bf16x4 hi = lds_read_tr4(base, hi_off / 2);
-    bf16x8 r;
-    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-    return r;
-}
-
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecBC = 32;     // keys per tile
+constexpr int kDecBC = 32;     // keys per tile (two 16-key blocks)
+constexpr int kDecRows = 16;   // query rows per wave (the N of the 16x16x32 products)
 constexpr int kDecStages = 2;  // per-wave ring: the tile being computed and the next in flight
 constexpr float kDecRescale = 8.0f;
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
 template <int D>
 struct DecCfg {
-    static constexpr int NKK = D / 16;          // k-steps of S^T over the head dimension
-    static constexpr int NDM = D / 32;          // 32-dim blocks of O^T
-    static constexpr int RB = 2 * D;            // bytes per V tile row (unpadded, swizzled)
-    static constexpr int VTILE = kDecBC * D;    // elements of a V tile
-    static constexpr int VSEGS = VTILE / 512;   // 1 KB copies per V tile
-    static constexpr int CPR = D / 8;           // 16-byte chunks per row
-    static_assert(VSEGS * 512 == VTILE, "a V tile must be whole 1 KB copies");
+    static constexpr int NK = D / 32;           // k-steps of S^T (32 dims each)
+    static constexpr int NDB = D / 16;          // 16-dim blocks of O^T
+    static constexpr int VS = 2 * D + 32;       // bytes per V tile row in LDS (32 mod 256: transposing reads)
+    static constexpr int VTILE = kDecBC * VS;   // bytes of a V tile
+    static constexpr int VSEGS = VTILE / 1024;  // 1 KB copies per V tile
+    static_assert(VSEGS * 1024 == VTILE, "a V tile must be whole 1 KB copies");
 };
 
+__device__ __forceinline__ f32x4v mfma16(bf16x8 a, bf16x8 b, f32x4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Max / sum over the four lanes that hold the same query (l, l^16, l^32, l^48).
+__device__ __forceinline__ float xquad_max(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return xhalf_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float xquad_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return xhalf_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(
+__global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ Kc, const bf16* __restrict__ Vc,
     const int* __restrict__ block_table, const int* __restrict__ seqlens, bf16* __restrict__ O,
     float* __restrict__ LSE, float* __restrict__ ws_o, float* __restrict__ ws_ml, int H, int Hkv, int Nq,
@@ -72,28 +80,30 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(
     // the two V slots are separate arrays so the compiler can tell the copy
     // in flight into one from the reads of another (it then waits for exactly
     // the copies a tile needs)
-    __shared__ __attribute__((aligned(1024))) bf16 vring0[kDecWaves][C::VTILE];
-    __shared__ __attribute__((aligned(1024))) bf16 vring1[kDecWaves][C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t vring0[kDecWaves][C::VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t vring1[kDecWaves][C::VTILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = lane >> 5, l32 = lane & 31;
+    const int gq = lane >> 4, l16 = lane & 15;  // k group of the operands / row group of the results
     const int item = blockIdx.x * kDecWaves + wave;
     if (item >= n_items) return;
-    // item -> (sequence b, KV head hk, query group qg, key range part), part fastest
-    const int part = item % n_parts;
-    int rest = item / n_parts;
+    // item -> (sequence b, query group qg, key range part, KV head hk), KV head
+    // fastest: the waves of a workgroup read the same cache rows' other heads
+    // at the same time, which keeps the HBM accesses close together
+    const int hk = item % Hkv;
+    int rest = item / Hkv;
+    const int part = rest % n_parts;
+    rest /= n_parts;
     const int qg = rest % nqg;
-    rest /= nqg;
-    const int hk = rest % Hkv;
-    const int b = rest / Hkv;
+    const int b = rest / nqg;
     const int G = H / Hkv;
     const int L = max(0, min(seqlens[b], max_pages * page_size));
     const int k_begin = part * kpp;
     const int k_end = min(L, k_begin + kpp);
 
-    // ---- this lane's query row: (grouped head g, new position qi) ----
-    const int R = qg * 32 + l32;
+    // ---- this lane's query row (the 16 columns; four lanes share each) ----
+    const int R = qg * kDecRows + l16;
     const bool row_ok = R < G * Nq;
     const int g = row_ok ? R / Nq : 0, qi = row_ok ? R % Nq : 0;
     const size_t row_id = ((size_t)b * H + (size_t)hk * G + g) * Nq + qi;
@@ -102,19 +112,19 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(
         // written directly gets O = 0 and lse = -inf
         if (n_parts == 1 && row_ok) {
             bf16* orow = O + row_id * D;
-            for (int c0 = 4 * h; c0 < D; c0 += 8) *reinterpret_cast<u32x2*>(orow + c0) = u32x2{0u, 0u};
-            if (h == 0) LSE[row_id] = -INFINITY;
+            for (int c0 = 4 * gq; c0 < D; c0 += 16) *reinterpret_cast<u32x2*>(orow + c0) = u32x2{0u, 0u};
+            if (gq == 0) LSE[row_id] = -INFINITY;
         }
         return;
     }
     const int nt = (k_end - k_begin + kDecBC - 1) / kDecBC;
     const int last_key = CAUSAL ? L - Nq + qi : L - 1;  // keys 0 .. last_key are allowed (and < k_end here)
-    bf16x8 qf[C::NKK];  // B operand of S^T = K Q^T (k = head dim, n = query)
+    bf16x8 qf[C::NK];  // B operand of S^T = K Q^T: query l16, dims 32 kk + 8 gq .. + 7
     {
-        const u32x4* qrow = reinterpret_cast<const u32x4*>(Q + row_id * D + 8 * h);
+        const u32x4* qrow = reinterpret_cast<const u32x4*>(Q + row_id * D + 8 * gq);
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; kk++) {
-            u32x4 raw = row_ok ? qrow[2 * kk] : u32x4{0u, 0u, 0u, 0u};
+        for (int kk = 0; kk < C::NK; kk++) {
+            u32x4 raw = row_ok ? qrow[4 * kk] : u32x4{0u, 0u, 0u, 0u};
             qf[kk] = __builtin_bit_cast(bf16x8, raw ^ qsign);
         }
     }
@@ -137,17 +147,21 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(
     };
     const uint32_t row_stride = (uint32_t)Hkv * D * 2;  // bytes between consecutive keys of one head
 
-    // K rows as MFMA A operands: lane l holds key l32, columns 16 kk + 8h .. + 7
-    bf16x8 kreg[kDecStages][C::NKK];
-    // V copy: segment i of a tile, lane -> (row, logical chunk (lane % CPR) ^ sigma(row))
+    // K rows as A operands of the 16x16x32 products: block mb holds keys 16 mb + l16,
+    // dims 32 kk + 8 gq .. + 7 (each load: 16 rows x 64 contiguous bytes)
+    bf16x8 kreg[kDecStages][2][C::NK];
+    const uint32_t k_off = (uint32_t)l16 * row_stride + 16u * gq;
+    // V copy into padded rows: segment i, lane -> (row, byte column); padding lanes re-read column 0
     uint32_t v_off[C::VSEGS];
 #pragma unroll
     for (int i = 0; i < C::VSEGS; i++) {
-        const int row = i * (512 / D) + lane / C::CPR;
-        const int chunk = (lane % C::CPR) ^ swz_sigma<D>(row & 15);
-        v_off[i] = (uint32_t)row * row_stride + (uint32_t)chunk * 16;
+        const int el = i * 1024 + lane * 16;
+        const int row = el / C::VS;
+        int col = el - row * C::VS;
+        col = col < 2 * D ? col : 0;
+        v_off[i] = (uint32_t)row * row_stride + (uint32_t)col;
     }
-    auto slot_of = [&](auto sc) -> bf16* {
+    auto slot_of = [&](auto sc) -> uint8_t* {
         constexpr int s = decltype(sc)::value;
         return s == 0 ? &vring0[wave][0] : &vring1[wave][0];
     };
@@ -155,34 +169,26 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(
         constexpr int s = decltype(sc)::value;
         const TileSrc src = tile_src(t);
         const rsrc_t rk = make_rsrc(src.kbase, src.bytes);
-        const uint32_t koff = (uint32_t)l32 * row_stride + 16u * h;
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; kk++) kreg[s][kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, koff + 32u * kk));
+        for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+            for (int kk = 0; kk < C::NK; kk++)
+                kreg[s][mb][kk] =
+                    __builtin_bit_cast(bf16x8, buf_load16(rk, k_off + 16u * row_stride * mb + 64u * kk));
         const rsrc_t rv = make_rsrc(src.vbase, src.bytes);
-        bf16* dst = slot_of(sc);
+        uint8_t* dst = slot_of(sc);
 #pragma unroll
-        for (int i = 0; i < C::VSEGS; i++) buf_load16_lds(rv, dst + 512 * i, v_off[i]);
+        for (int i = 0; i < C::VSEGS; i++) buf_load16_lds(rv, dst + 1024 * i, v_off[i]);
     };
+    // V^T as the A operand of O^T += V^T P^T, dims 16 db + l16: the transposing read of
+    // block mb gives keys 16 mb + 4 gq + j (j = 0..3), the key order of the S^T results
+    const uint32_t v_tr = (uint32_t)(4 * gq + (l16 >> 2)) * C::VS + 8u * (l16 & 3);
 
-    // transposing-read offsets of V^T as the A operand of O^T += V^T P^T
-    uint32_t tr_lo[C::NDM], tr_hi[C::NDM];
-    {
-        const int sl = lane & 15, j = sl >> 2, q = sl & 3, gq = (lane >> 4) & 1;
-        const int r = 4 * h + j;
-        const int slo = swz_sigma<D>(r), shi = swz_sigma<D>(r + 8);
+    f32x4v oacc[C::NDB];
 #pragma unroll
-        for (int dm = 0; dm < C::NDM; dm++) {
-            const int cc = 4 * dm + 2 * gq + (q >> 1);
-            tr_lo[dm] = r * C::RB + ((cc ^ slo) << 4) + (q & 1) * 8;
-            tr_hi[dm] = (r + 8) * C::RB + ((cc ^ shi) << 4) + (q & 1) * 8;
-        }
-    }
-
-    f32x16 oacc[C::NDM];
-#pragma unroll
-    for (int dm = 0; dm < C::NDM; dm++) oacc[dm] = f32x16{};
+    for (int db = 0; db < C::NDB; db++) oacc[db] = f32x4v{};
     float m_ref = -INFINITY;  // reference max of raw scores (moves lazily)
-    float l_part = 0.f;       // this lane's half of the running sum
+    float l_part = 0.f;       // this lane's quarter of the running sum
 
     // One tile from ring slot s (the compiler waits for exactly its loads; the
     // next tile stays in flight), then refill the slot with tile t + 2.  A tile
@@ -191,20 +197,26 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(
     auto tile = [&](auto sc, int t) {
         constexpr int s = decltype(sc)::value;
         const int t0 = k_begin + kDecBC * t;
-        f32x16 sv = f32x16{};
+        f32x4v sv[2];
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; kk++) sv = mfma32(kreg[s][kk], qf[kk], sv);
+        for (int mb = 0; mb < 2; mb++) {
+            sv[mb] = f32x4v{};
+#pragma unroll
+            for (int kk = 0; kk < C::NK; kk++) sv[mb] = mfma16(kreg[s][mb][kk], qf[kk], sv[mb]);
+        }
+        // result (mb, r): key t0 + 16 mb + 4 gq + r, query l16
         if (t0 + kDecBC > k_end || (CAUSAL && t0 + kDecBC - 1 > L - Nq)) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int key = t0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                sv[r] = (key > last_key || key >= k_end) ? -INFINITY : sv[r];
-            }
-        }
-        float mx = sv[0];
+            for (int mb = 0; mb < 2; mb++)
 #pragma unroll
-        for (int r = 1; r < 16; r++) mx = fmaxf(mx, sv[r]);
-        mx = xhalf_max(mx);
+                for (int r = 0; r < 4; r++) {
+                    const int key = t0 + 16 * mb + 4 * gq + r;
+                    sv[mb][r] = (key > last_key || key >= k_end) ? -INFINITY : sv[mb][r];
+                }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                         fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+        mx = xquad_max(mx);
         const float m_new = fmaxf(m_ref, mx);
         const bool bump = m_new != -INFINITY && (m_ref == -INFINITY || (m_new - m_ref) * c > kDecRescale);
         if (__builtin_expect(__ballot(bump) != 0, 0)) {
@@ -212,27 +224,27 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(
             if (bump) m_ref = m_new;
             l_part *= alpha;
 #pragma unroll
-            for (int dm = 0; dm < C::NDM; dm++) oacc[dm] *= alpha;
+            for (int db = 0; db < C::NDB; db++) oacc[db] *= alpha;
         }
         const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
-        u32x4 pb[2];
-        float ls[2] = {0.f, 0.f};
+        u32x4 pb;  // P^T as the B operand: element 4 mb + r is key 16 mb + 4 gq + r
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            const float p0 = exp2f_hw(__builtin_fmaf(sv[r], c, -mc));
-            const float p1 = exp2f_hw(__builtin_fmaf(sv[r + 1], c, -mc));
-            ls[0] += p0;
-            ls[1] += p1;
-            pb[r / 8][(r % 8) / 2] = cvt_pk_bf16(p0, p1);
+        for (int mb = 0; mb < 2; mb++) {
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) p[r] = exp2f_hw(__builtin_fmaf(sv[mb][r], c, -mc));
+            l_part += (p[0] + p[1]) + (p[2] + p[3]);
+            pb[2 * mb] = cvt_pk_bf16(p[0], p[1]);
+            pb[2 * mb + 1] = cvt_pk_bf16(p[2], p[3]);
         }
-        l_part += ls[0] + ls[1];
-        const bf16* vt = slot_of(sc);
+        const uint8_t* vt = slot_of(sc);
 #pragma unroll
-        for (int k16 = 0; k16 < 2; k16++)
-#pragma unroll
-            for (int dm = 0; dm < C::NDM; dm++)
-                oacc[dm] = mfma32(lds_tr_pair_v(vt, tr_lo[dm] + 16u * k16 * C::RB, tr_hi[dm] + 16u * k16 * C::RB),
-                                  __builtin_bit_cast(bf16x8, pb[k16]), oacc[dm]);
+        for (int db = 0; db < C::NDB; db++) {
+            const bf16x4 lo = lds_read_tr4(reinterpret_cast<const bf16*>(vt), (v_tr + 32u * db) / 2);
+            const bf16x4 hi = lds_read_tr4(reinterpret_cast<const bf16*>(vt), (v_tr + 16u * C::VS + 32u * db) / 2);
+            const bf16x8 va = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            oacc[db] = mfma16(va, __builtin_bit_cast(bf16x8, pb), oacc[db]);
+        }
         issue(sc, t + kDecStages);
     };
 
@@ -244,32 +256,27 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(
     }
     wait_vmem();  // copies past the last tile fetch nothing but must retire before the wave ends
 
-    // ---- epilogue ----
-    const float l = xhalf_sum(l_part);
+    // ---- epilogue: result (db, r) is dim 16 db + 4 gq + r of query l16 ----
+    const float l = xquad_sum(l_part);
     if (n_parts == 1) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         if (row_ok) {
             bf16* orow = O + row_id * D;
 #pragma unroll
-            for (int dm = 0; dm < C::NDM; dm++)
+            for (int db = 0; db < C::NDB; db++) {
+                bf16x4 v4;
 #pragma unroll
-                for (int gq = 0; gq < 4; gq++) {
-                    bf16x4 v4;
-#pragma unroll
-                    for (int e = 0; e < 4; e++) v4[e] = (bf16)(oacc[dm][4 * gq + e] * inv);
-                    *reinterpret_cast<bf16x4*>(orow + 32 * dm + 8 * gq + 4 * h) = v4;
-                }
-            if (h == 0) LSE[row_id] = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
+                for (int e = 0; e < 4; e++) v4[e] = (bf16)(oacc[db][e] * inv);
+                *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * gq) = v4;
+            }
+            if (gq == 0) LSE[row_id] = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
         }
     } else if (row_ok) {
         float* wo = ws_o + (row_id * n_parts + part) * D;
 #pragma unroll
-        for (int dm = 0; dm < C::NDM; dm++)
-#pragma unroll
-            for (int gq = 0; gq < 4; gq++)
-                *reinterpret_cast<f32x4*>(wo + 32 * dm + 8 * gq + 4 * h) =
-                    f32x4{oacc[dm][4 * gq], oacc[dm][4 * gq + 1], oacc[dm][4 * gq + 2], oacc[dm][4 * gq + 3]};
-        if (h == 0) {
+        for (int db = 0; db < C::NDB; db++)
+            *reinterpret_cast<f32x4*>(wo + 16 * db + 4 * gq) = f32x4{oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]};
+        if (gq == 0) {
             float* ml = ws_ml + (row_id * n_parts + part) * 2;
             ml[0] = m_ref == -INFINITY ? -INFINITY : m_ref * c;  // log2 units
             ml[1] = l;
@@ -337,7 +344,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 template <int D, bool CAUSAL>
 hipError_t launch_decode_d(const DecArgs& a) {
     const int G = a.H / a.Hkv;
-    const int nqg = (G * a.Nq + 31) / 32;
+    const int nqg = (G * a.Nq + kDecRows - 1) / kDecRows;
     const int n_items = a.B * a.Hkv * nqg * a.n_parts;
     const int blocks = (n_items + kDecWaves - 1) / kDecWaves;
     hipLaunchKernelGGL((decode_kernel<D, CAUSAL>), dim3(blocks), dim3(kDecThreads), 0, a.stream,
