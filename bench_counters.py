@@ -40,12 +40,20 @@ from workloads import accounting as A  # noqa: E402
 
 COPY_KIB = 262144.0
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["fa_common.h", "fa_fwd.hip", "fa_bwd.hip"]
+def kernel_sources(w) -> list:
+    """The kernel sources a workload's counted launches are built from."""
+    if getattr(w, "kind", "attn") == "decode":
+        return ["fa_common.h", "fa_decode.hip"]
+    if getattr(w, "precision", "bf16") == "fp8":
+        return ["fa_common.h", "fa_fp8.hip"]
+    return ["fa_common.h", "fa_fwd.hip", "fa_bwd.hip"]
 
 # kernel-name substring -> entry point that launches it
 ENTRY = [("fwd_bf16_kernel", "fa_fwd"), ("rowdot_kernel", "fa_bwd_prep"),
-         ("bwd_bf16_kernel", "fa_bwd_main"), ("bwd_dq_kernel", "fa_bwd_dq")]
-ORDER = [e for _, e in ENTRY]
+         ("bwd_bf16_kernel", "fa_bwd_main"), ("bwd_dq_kernel", "fa_bwd_dq"),
+         ("decode_kernel", "fa_decode_paged"), ("decode_merge_kernel", "fa_decode_paged"),
+         ("fp8_quant_kernel", "fa_fp8_quantize"), ("fwd_fp8_kernel", "fa_fwd_fp8")]
+ORDER = list(dict.fromkeys(e for _, e in ENTRY))
 
 
 def entry_of(kernel: str):
@@ -68,6 +76,8 @@ def read_counters(path: str):
 
 
 def workload_title(w) -> str:
+    if getattr(w, "kind", "attn") == "decode":
+        return w.description
     parts = [f"B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}", "causal" if w.causal else "non-causal"]
     if w.window is not None:
         parts.append(f"window {tuple(w.window)}")
@@ -75,6 +85,8 @@ def workload_title(w) -> str:
         parts.append("ALiBi")
     if w.mask:
         parts.append(f"block mask {w.mask}")
+    if getattr(w, "precision", "bf16") == "fp8":
+        parts.append("FP8 E4M3")
     return ", ".join(parts) + (" (forward + backward step)" if w.backward else " (forward)")
 
 
@@ -89,21 +101,28 @@ def traffic(args) -> None:
     copy_w = [k for (k, c) in wr if is_copy(k) and c == "WRITE_SIZE"]
     if not copy or not copy_w:
         raise SystemExit("no calibration copy in the profile: run bench.py with --copy-calib")
-    f_copy = statistics.mean(f[(copy[0], "FETCH_SIZE")])
-    w_copy = statistics.mean(wr[(copy_w[0], "WRITE_SIZE")])
+    # the 256 MiB calibration copy is the largest copy dispatch (input uploads are copies too)
+    f_copy = max(f[(copy[0], "FETCH_SIZE")])
+    w_copy = max(wr[(copy_w[0], "WRITE_SIZE")])
     fs, ws = COPY_KIB / f_copy, COPY_KIB / w_copy
-    alg = A.launch_bytes(w, W.workload_mask(w, seed=0))
+    if getattr(w, "kind", "attn") == "decode":
+        alg = {"fa_decode_paged": A.decode_bytes(w, W.decode_inputs(w, seed=0)["seqlens"])}
+    else:
+        alg = A.launch_bytes(w, W.workload_mask(w, seed=0))
     per = {}
     rows = []
     for (k, c), vals in f.items():
         api = entry_of(k)
-        if api is None or c != "FETCH_SIZE":
+        if api is None or c != "FETCH_SIZE" or api not in alg:
             continue
         fk = statistics.mean(vals)
         wk = statistics.mean(wr[(k, "WRITE_SIZE")])
         rb, wb = fk * fs * 1024, wk * ws * 1024
-        per[api] = {"read_bytes": round(rb), "write_bytes": round(wb), "traffic_bytes": round(rb + wb),
-                    "algorithmic_bytes": alg[api]}
+        # an entry point that launches several kernels sums their traffic per call
+        e = per.setdefault(api, {"read_bytes": 0, "write_bytes": 0, "traffic_bytes": 0, "algorithmic_bytes": alg[api]})
+        e["read_bytes"] += round(rb)
+        e["write_bytes"] += round(wb)
+        e["traffic_bytes"] += round(rb + wb)
         rows.append((ORDER.index(api), f"| {api} | `{k[:60]}` | {len(vals)} | {fk:.1f} | {wk:.1f} | {rb / 1e6:.1f} | "
                                        f"{wb / 1e6:.1f} | {(rb + wb) / 1e6:.1f} | {alg[api] / 1e6:.1f} | "
                                        f"{(rb + wb) / alg[api]:.2f} |"))
@@ -114,7 +133,7 @@ def traffic(args) -> None:
     except (OSError, ValueError):
         allw = {"workloads": {}}
     allw["workloads"][w.name] = {
-        "kernel_source_sha256": bench.kernel_source_digest(KERNEL_SOURCES), "sources": KERNEL_SOURCES,
+        "kernel_source_sha256": bench.kernel_source_digest(kernel_sources(w)), "sources": kernel_sources(w),
         "fetch_scale": fs, "write_scale": ws, "per_launch": per}
     with open(TRAFFIC_JSON, "w") as fh:
         json.dump(allw, fh, indent=1, sort_keys=True)
@@ -172,32 +191,36 @@ def trace(args) -> None:
     line = [json.loads(x) for x in open(args.bench_line) if x.startswith('{"metric"')][-1]
     steps, warm = line["steps"], line["warmup"]
     per = collections.defaultdict(list)
-    names = {}
     for r in csv.DictReader(open(args.csv)):
         api = entry_of(r["Kernel_Name"])
         if api is None:
             continue
-        per[api].append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
-        names[api] = r["Kernel_Name"]
+        per[(api, r["Kernel_Name"])].append(
+            (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
     ev = {"fa_fwd": line.get("fwd_ms"), "fa_bwd_prep": line.get("bwd_prep_ms"),
-          "fa_bwd_main": line.get("bwd_main_ms"), "fa_bwd_dq": line.get("bwd_dq_ms")}
-    lines = [f"# Kernel trace: {workload_title(w)}", ""]
+          "fa_bwd_main": line.get("bwd_main_ms"), "fa_bwd_dq": line.get("bwd_dq_ms"),
+          "fa_fwd_fp8": line.get("fwd_ms") if "fwd_pct_peak_fp8" in line else None,
+          "fa_decode_paged": line["call_us"]["median"] / 1e3 if "call_us" in line else None}
+    if "fwd_pct_peak_fp8" in line:
+        ev["fa_fwd"] = None
+    lines = [f"# Kernel trace: {workload_title(w) if getattr(w, 'kind', 'attn') == 'attn' else w.description}", ""]
     lines += commands_block(args.command)
     lines += [f"{warm} warm-up steps, then {steps} timed steps.  The last column is the median of the HIP-event "
-              f"times bench.py measured on the launch stream for the same timed steps.", "",
+              f"times bench.py measured on the launch stream for the same timed steps (per entry point: the "
+              f"sum of its kernels).", "",
               "| entry point | kernel | calls | avg µs (all) | avg µs (timed) | min µs | max µs | bench.py event median µs |",
               "|---|---|---|---|---|---|---|---|"]
-    for api in ORDER:
-        if api not in per:
-            continue
-        d = [x for _, x in sorted(per[api])]
+    shown = set()
+    for (api, name) in sorted(per, key=lambda x: (ORDER.index(x[0]), x[1])):
+        d = [x for _, x in sorted(per[(api, name)])]
         timed = d[-steps:]
-        e = ev.get(api)
-        lines.append(f"| {api} | `{names[api][:60]}` | {len(d)} | {statistics.mean(d):.1f} | "
+        e = ev.get(api) if api not in shown else None
+        shown.add(api)
+        lines.append(f"| {api} | `{name[:60]}` | {len(d)} | {statistics.mean(d):.1f} | "
                      f"{statistics.mean(timed):.1f} | {min(d):.1f} | {max(d):.1f} | "
                      f"{'' if e is None else f'{e * 1e3:.1f}'} |")
     keep = {k: line[k] for k in ("metric", "value", "unit", "ms_per_step", "fwd_ms", "bwd_ms", "bwd_prep_ms",
-                                 "bwd_main_ms", "bwd_dq_ms") if k in line}
+                                 "bwd_main_ms", "bwd_dq_ms", "call_us") if k in line}
     lines += ["", "bench.py line printed by the profiled run (abridged):", "", "```", json.dumps(keep), "```"]
     out = os.path.join(ROOT, "profiles", f"{args.workload}_kernel_trace.md")
     open(out, "w").write("\n".join(lines) + "\n")

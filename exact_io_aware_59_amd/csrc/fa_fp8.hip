@@ -3,10 +3,11 @@
 // FlashAttention-3 adds FP8 block quantization with incoherent processing).
 //
 //  1. fp8_quant_kernel: one workgroup per 64-row block of one (b, h) slice of
-//     Q, K or V.  Rows are widened to fp64 in LDS; with a sign vector the
-//     incoherent map x -> H (sigma o x) (Sylvester Hadamard matrix, a fast
-//     Walsh-Hadamard transform in log2(d) butterfly stages; times 1/d for K) is
-//     applied exactly (sums of bf16 values fit fp64).  The block gets the
+//     Q, K or V, a row per wave at a time in fp64 registers; with a sign
+//     vector the incoherent map x -> H (sigma o x) (Sylvester Hadamard matrix,
+//     a fast Walsh-Hadamard transform in log2(d) butterfly stages across the
+//     lanes; times 1/d for K) is applied exactly (sums of bf16 values fit
+//     fp64).  The block gets the
 //     smallest power-of-two scale 2^e with amax / 2^e <= 448, and every value
 //     becomes the nearest FP8 E4M3 code of x / 2^e (ties to even, computed in
 //     fp64 with round-to-nearest-even).  Power-of-two scales are exactly the
@@ -61,51 +62,66 @@ __device__ __forceinline__ uint32_t e4m3_rne(double x) {
     return sign | code;
 }
 
+// One workgroup per 64-row block (4 waves x 16 rows).  A wave keeps a row in
+// registers, EPL = D/64 consecutive elements per lane (element c = EPL lane +
+// j), so the butterfly stages of the map with stride < EPL stay in a lane and
+// the others exchange fp64 values with the lane at distance stride / EPL.
 template <int D>
 __global__ __launch_bounds__(256) void fp8_quant_kernel(const bf16* __restrict__ X, uint8_t* __restrict__ codes,
                                                         int8_t* __restrict__ exps, int N, int nblk,
                                                         const float* __restrict__ signs, int k_side) {
-    __shared__ double t[kF8Block][D];
-    __shared__ double red[256];
-    const int tid = threadIdx.x;
+    constexpr int EPL = D / 64;
+    constexpr int RPW = kF8Block / 4;  // rows per wave
+    __shared__ double wmax[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
-    const int r0 = blk * kF8Block;
-    const int rows = min(kF8Block, N - r0);
+    const int r0 = blk * kF8Block + wave * RPW;
+    const int rows = max(0, min(RPW, N - r0));
     const bf16* xh = X + ((size_t)bh * N + r0) * D;
-    // widen (and multiply by the signs)
-    for (int i = tid; i < kF8Block * D; i += 256) {
-        const int r = i / D, c = i % D;
-        double v = r < rows ? (double)(float)xh[i] : 0.0;
-        if (signs) v *= (double)signs[c];
-        t[r][c] = v;
-    }
-    __syncthreads();
-    if (signs) {
-        // fast Walsh-Hadamard transform of every row: (u, v) -> (u + v, u - v)
-        for (int len = 1; len < D; len <<= 1) {
-            for (int p = tid; p < kF8Block * D / 2; p += 256) {
-                const int r = p / (D / 2), pr = p % (D / 2);
-                const int i = (pr / len) * 2 * len + (pr % len), j = i + len;
-                const double u = t[r][i], v = t[r][j];
-                t[r][i] = u + v;
-                t[r][j] = u - v;
-            }
-            __syncthreads();
-        }
-        if (k_side)
-            for (int i = tid; i < kF8Block * D; i += 256) t[i / D][i % D] *= 1.0 / D;  // exact: D a power of two
-        __syncthreads();
-    }
-    // block amax
+    double sg[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; j++) sg[j] = signs ? (double)signs[EPL * lane + j] : 1.0;
+    double v[RPW][EPL];
     double m = 0.0;
-    for (int i = tid; i < rows * D; i += 256) m = fmax(m, fabs(t[i / D][i % D]));
-    red[tid] = m;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) red[tid] = fmax(red[tid], red[tid + s]);
-        __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RPW; r++) {
+#pragma unroll
+        for (int j = 0; j < EPL; j++) v[r][j] = r < rows ? (double)(float)xh[(size_t)r * D + EPL * lane + j] * sg[j] : 0.0;
+        if (signs) {
+            // fast Walsh-Hadamard transform of the row: (u, w) -> (u + w, u - w) for pairs at distance len
+#pragma unroll
+            for (int len = 1; len < D; len <<= 1) {
+                if (len < EPL) {
+#pragma unroll
+                    for (int j = 0; j < EPL; j++)
+                        if (!(j & len)) {
+                            const double u = v[r][j], w = v[r][j + len];
+                            v[r][j] = u + w;
+                            v[r][j + len] = u - w;
+                        }
+                } else {
+                    const int xl = len / EPL;
+                    const bool upper = lane & xl;
+#pragma unroll
+                    for (int j = 0; j < EPL; j++) {
+                        const double o = __shfl_xor(v[r][j], xl);
+                        v[r][j] = upper ? o - v[r][j] : v[r][j] + o;
+                    }
+                }
+            }
+            if (k_side)
+#pragma unroll
+                for (int j = 0; j < EPL; j++) v[r][j] *= 1.0 / D;  // exact: D a power of two
+        }
+#pragma unroll
+        for (int j = 0; j < EPL; j++) m = fmax(m, fabs(v[r][j]));
     }
-    const double amax = red[0];
+    // block amax: wave, then workgroup
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+    if (lane == 0) wmax[wave] = m;
+    __syncthreads();
+    const double amax = fmax(fmax(wmax[0], wmax[1]), fmax(wmax[2], wmax[3]));
     // smallest e with amax / 2^e <= 448, within the E8M0 range
     int e = 0;
     if (amax > 0.0) {
@@ -117,13 +133,17 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(const bf16* __restrict__
     }
     e = max(-127, min(127, e));
     if (tid == 0) exps[(size_t)bh * nblk + blk] = (int8_t)e;
-    // codes, four per 32-bit store
+    // codes: EPL consecutive bytes per lane and row
     uint8_t* ch = codes + ((size_t)bh * N + r0) * D;
-    for (int i = 4 * tid; i < rows * D; i += 4 * 256) {
-        uint32_t w = 0;
 #pragma unroll
-        for (int j = 0; j < 4; j++) w |= e4m3_rne(ldexp(t[(i + j) / D][(i + j) % D], -e)) << (8 * j);
-        *reinterpret_cast<uint32_t*>(ch + i) = w;
+    for (int r = 0; r < RPW; r++) {
+        if (r >= rows) break;
+        if constexpr (EPL == 2) {
+            const uint32_t w = e4m3_rne(ldexp(v[r][0], -e)) | (e4m3_rne(ldexp(v[r][1], -e)) << 8);
+            *reinterpret_cast<uint16_t*>(ch + (size_t)r * D + 2 * lane) = (uint16_t)w;
+        } else {
+            ch[(size_t)r * D + lane] = (uint8_t)e4m3_rne(ldexp(v[r][0], -e));
+        }
     }
 }
 

@@ -144,6 +144,12 @@ def launch_bytes(w: Workload, mask: Optional[np.ndarray] = None) -> dict:
     t = w.B * w.H * w.N * w.d * e
     r = w.B * w.H * w.N * F32_BYTES
     m = 0 if mask is None else int(mask.size)
+    if getattr(w, "precision", "bf16") == "fp8":
+        # fa_fwd_fp8 reads one-byte codes of q, k, v and their block exponents, writes bf16 o and lse
+        codes = w.B * w.H * w.N * w.d
+        exps = w.B * w.H * (-(-w.N // 64))
+        return {"fa_fwd_fp8": 3 * codes + 3 * exps + t + r,
+                "fa_fp8_quantize": 3 * (t + codes + exps)}
     out = {"fa_fwd": 4 * t + r + m}
     if w.backward:
         out.update({"fa_bwd_prep": 2 * t + 3 * r,
