@@ -658,6 +658,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             bf16x8 sb[2][2];
             auto probs = [&](int kb) {  // P = 2^(c s - lse2), dS = P (dP - D)
                 const float mlk = LIN ? __builtin_fmaf(var.slope2, (float)(kv0 + 32 * kb + 4 * h - my_q), ml2) : ml2;
+                // exponentials, then the element mask under one branch (a select per
+                // element inside the loop became a branch per element), then dS
+                float p[16];
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -665,11 +668,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                     if constexpr (LIN) z = __builtin_fmaf(s[kb][r], c, __builtin_fmaf(var.slope2, (float)row_in_block(r), mlk));
                     else z = __builtin_fmaf(s[kb][r], c, ml2);
                     if constexpr (GEN) z += var.bias2(my_q, key);
-                    float p = exp2f_hw(z);
-                    if (need_mask)
-                        p = ((CAUSAL && key > my_q) || key >= N || (VAR && var.dead(my_q, key))) ? 0.f : p;
-                    dp[kb][r] = p * (dp[kb][r] - dd);
+                    p[r] = exp2f_hw(z);
                 }
+                if (need_mask) {
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        p[r] = ((CAUSAL && key > my_q) || key >= N || (VAR && var.dead(my_q, key))) ? 0.f : p[r];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; r++) dp[kb][r] = p[r] * (dp[kb][r] - dd);
                 sb[kb][0] = pack8<0>(dp[kb]);
                 sb[kb][1] = pack8<8>(dp[kb]);
             };
