@@ -43,6 +43,12 @@ __device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp
 // log2(x) (v_log_f32); log2(0) = -inf.
 __device__ __forceinline__ float log2f_hw(float x) { return __builtin_amdgcn_logf(x); }
 
+// Computes x at this point of the program: an empty asm that "modifies" x.
+// Scheduling fences bind only the machine scheduler; without this, earlier
+// passes sink a running sum or max that is read only after a fenced loop down
+// to that read, out of the slots it was placed in.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 // Value of x in the other half-wave (lane l <-> lane l^32).
 __device__ __forceinline__ float xhalf_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

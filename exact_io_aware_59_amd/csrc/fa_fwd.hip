@@ -58,7 +58,17 @@ struct FwdCfg {
     static constexpr int VSEGS = VTILE / 512;
     static_assert(KSEGS * 512 == KTILE && VSEGS * 512 == VTILE, "tiles must be whole 1 KB segments");
     static_assert(kMaskBlock % BC == 0, "a mask block must hold whole tiles");
+    // one pipelined step = a fixed schedule of NSLOT matrix products
+    static constexpr int NS = NKK * NKB;     // S^T products of a tile
+    static constexpr int NP = NT * NDM;      // O^T products of a tile
+    static constexpr int NSLOT = NS + NP;
+    static constexpr int PD = 2;             // slots between an LDS operand read and its product
+    static constexpr int NDMA = (KSEGS + VSEGS + kWaves - 1) / kWaves;  // 1 KB copies per wave per step
 };
+
+// Items [spread<E, S>(j), spread<E, S>(j + 1)) of E items dealt evenly over S slots.
+template <int E, int S>
+constexpr int spread(int j) { return (j * E + S - 1) / S; }
 
 // Which K/V tiles a query block visits.
 struct TileList {
@@ -246,6 +256,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const rsrc_t rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
     Variant var{wl, wr, 0.f};
     if (VAR && slopes != nullptr) var.slope2 = slopes[bh % H] * kLog2e;
+    // the pipelined steps' copies: descriptors and, for copy i of this wave,
+    // the byte offset of its lane's 16 bytes from the tile's first row (a lane
+    // whose bytes fall in row padding re-reads the row's first chunk)
+    const int32x4_t srd_k = make_srd(K + head_off, head_bytes);
+    const int32x4_t srd_v = make_srd(V + head_off, head_bytes);
+    uint32_t dma_rel[C::NDMA];
+#pragma unroll
+    for (int i = 0; i < C::NDMA; i++) {
+        const int g = i * kWaves + wave;
+        const bool isk = g < C::KSEGS;
+        const int seg = isk ? g : min(g - C::KSEGS, C::VSEGS - 1);  // past the V tile: its last segment again
+        const int stride = isk ? C::KS : C::VS;
+        const int el = seg * 512 + lane * 8;
+        const int row = el / stride;
+        int col = el - row * stride;
+        col = col < D ? col : 0;
+        dma_rel[i] = (uint32_t)(row * D + col) * 2;
+    }
 
     for (int bi = 0; bi < nblk; bi++) {
         const int qb = qblk[bi];
@@ -336,6 +364,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         // One pipelined step: tile `it` (scores in sc, max mx_cur) is exponentiated
         // and multiplied into O while the scores of tile it+1 land in sn.
         // P = parity of `it`: tile it lives in kbuf<P>/vbuf<P>, tile it+1 in the other pair.
+        // The step is a fixed schedule of NSLOT matrix products, each slot closed
+        // by a scheduling fence: slots [0, NS) compute S(it+1) while the vector
+        // ALUs take the exponentials of tile it and pack them to bf16; slots
+        // [NS, NSLOT) compute O += V(it)^T P(it)^T while the vector ALUs take the
+        // row max of S(it+1).  Every slot issues the LDS operand read of slot
+        // j + PD, so no product waits on a read it has just issued, and a share of
+        // the step's HBM -> LDS copies (K of tile it+2, V of tile it+1; their
+        // buffers were last read before the previous barrier).  Scores of tile
+        // it+1 that need a mask or a bias (the few tiles at the diagonal, an edge
+        // of the window or N; every tile of a variant) are finished after the
+        // schedule, and their max is taken again.  (One instantiation of the
+        // schedule: a branch between a masked and a plain copy of it made the
+        // register allocator spill.)
         auto step = [&](auto parity, int it, f32x16 (&sc)[C::NKB], f32x16 (&sn)[C::NKB]) {
             constexpr int P = decltype(parity)::value;
             bf16* k_this = P ? kbuf1 : kbuf0;   // K(it), then K(it+2)
@@ -343,10 +384,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             bf16* v_this = P ? vbuf1 : vbuf0;   // V(it)
             bf16* v_next = P ? vbuf0 : vbuf1;   // V(it+1)
             const bool has_next = it + 1 < tl.n;
-            const int kv1 = has_next ? tl.kv0(it + 1) : 0;
-            // HBM -> LDS: K of tile it+2 and V of tile it+1 (their buffers were last read before the barrier)
-            if (it + 2 < tl.n) load_tile<D, C::KS, C::KSEGS>(rk, k_this, tl.kv0(it + 2), wave, lane);
-            if (has_next) load_tile<D, C::VS, C::VSEGS>(rv, v_next, kv1, wave, lane);
+            // tiles past the end are copied from rows >= N, which read as zero
+            const int kv1 = has_next ? tl.kv0(it + 1) : N;
+            const int kv2 = it + 2 < tl.n ? tl.kv0(it + 2) : N;
 
             // ---- reference-max update for tile it (rare O rescale) ----
             {
@@ -363,38 +403,71 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             }
             const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
 
-            // ---- phase A: S(it+1) on the matrix cores, 2^(c s - c m) of tile it on the VALU ----
-            // (a tile past the end computes S on stale LDS data; its result is never used)
+            const bf16* kl = k_next + k_lane;
+            const bf16* vl = v_this + v_lane;
+            const uint32_t k_dst = lds_addr_of(k_this), v_dst = lds_addr_of(v_next);
+            const uint32_t k_src = (uint32_t)kv2 * (D * 2), v_src = (uint32_t)kv1 * (D * 2);
+            bf16x8 opnd[C::NSLOT];
             bf16x8 pb[C::NT];
-            {
-                const bf16* kl = k_next + k_lane;
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; kb++) sn[kb] = f32x16{};
-                float ls[4] = {0.f, 0.f, 0.f, 0.f};   // independent partial sums (short dependency chains)
-                constexpr int NM = C::NKK * C::NKB;   // MFMAs in this phase
-                constexpr int EPM = 16 * C::NKB / NM; // exponentials per MFMA (d=128: 2, d=64: 4)
-#pragma unroll
-                for (int i = 0; i < NM; i++) {
-                    const int kk = i / C::NKB, kb = i % C::NKB;
-                    sn[kb] = mfma32(lds_read8(kl, 32 * kb * C::KS + 16 * kk), qf[kk], sn[kb]);
-#pragma unroll
-                    for (int e = 0; e < EPM; e++) {
-                        const int idx = i * EPM + e;           // 0 .. 16*NKB-1
-                        const int skb = idx / 16, r = idx % 16;
-                        const float p = exp2f_hw(__builtin_fmaf(sc[skb][r], c, -mc));
-                        sc[skb][r] = p;
+            float ls[4] = {0.f, 0.f, 0.f, 0.f};   // independent partial sums (short dependency chains)
+            float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            auto read_operand = [&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if constexpr (j < C::NS)
+                    opnd[j] = lds_read8(kl, 32 * (j % C::NKB) * C::KS + 16 * (j / C::NKB));
+                else
+                    opnd[j] = lds_tr_operand_pad<C::VS>(vl, 16 * ((j - C::NS) / C::NDM), 32 * ((j - C::NS) % C::NDM));
+            };
+            // copy i of this wave: 1 KB segment i*kWaves + wave of the K tile, then of the V tile
+            auto dma_op = [&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                const int g = i * kWaves + wave;
+                const bool isk = g < C::KSEGS;
+                const int seg = isk ? g : min(g - C::KSEGS, C::VSEGS - 1);
+                dma16_untracked(isk ? srd_k : srd_v, (isk ? k_dst : v_dst) + (uint32_t)seg * 1024u,
+                                dma_rel[i] + (isk ? k_src : v_src));
+            };
+            static_for<C::PD>([&](auto jc) { read_operand(jc); });
+            static_for<C::NSLOT>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if constexpr (j + C::PD < C::NSLOT) read_operand(std::integral_constant<int, j + C::PD>{});
+                if constexpr (j < C::NS) {
+                    // ---- S(it+1) product; exponentials of tile it ----
+                    constexpr int kk = j / C::NKB, kb = j % C::NKB;
+                    if constexpr (kk == 0) sn[kb] = mfma32(opnd[j], qf[0], f32x16{});
+                    else sn[kb] = mfma32(opnd[j], qf[kk], sn[kb]);
+                    static_for<spread<16 * C::NKB, C::NS>(j + 1) - spread<16 * C::NKB, C::NS>(j)>([&](auto ec) {
+                        constexpr int idx = spread<16 * C::NKB, C::NS>(j) + decltype(ec)::value;
+                        const float p = exp2f_hw(__builtin_fmaf(sc[idx / 16][idx % 16], c, -mc));
+                        sc[idx / 16][idx % 16] = p;
                         ls[idx & 3] += p;
-                    }
-                    if ((i * EPM + EPM) % 8 == 0) {
-                        const int t = (i * EPM + EPM) / 8 - 1;   // 8 probabilities complete
-                        pb[t] = (t & 1) ? pack8<8>(sc[t >> 1]) : pack8<0>(sc[t >> 1]);
+                        pin(ls[idx & 3]);
+                        if constexpr (idx % 8 == 7) pb[idx / 8] = pack8<((idx / 8) & 1) * 8>(sc[idx / 16]);
+                    });
+                } else {
+                    // ---- O += V(it)^T P(it)^T product; row max of S(it+1) ----
+                    constexpr int jp = j - C::NS, t = jp / C::NDM, dm = jp % C::NDM;
+                    oacc[dm] = mfma32(opnd[j], pb[t], oacc[dm]);
+                    if constexpr (VK == 0) {
+                        static_for<spread<8 * C::NKB, C::NP>(jp + 1) - spread<8 * C::NKB, C::NP>(jp)>([&](auto ec) {
+                            constexpr int pr = spread<8 * C::NKB, C::NP>(jp) + decltype(ec)::value;
+                            constexpr int kb = (2 * pr) / 16, r = (2 * pr) % 16;
+                            mp[pr & 3] = fmaxf(mp[pr & 3], fmaxf(sn[kb][r], sn[kb][r + 1]));
+                            pin(mp[pr & 3]);
+                        });
                     }
                 }
-                l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+                static_for<spread<C::NDMA, C::NSLOT>(j + 1) - spread<C::NDMA, C::NSLOT>(j)>([&](auto ic) {
+                    dma_op(std::integral_constant<int, spread<C::NDMA, C::NSLOT>(j) + decltype(ic)::value>{});
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+            if (VK != 0 || (has_next && needs_mask(kv1))) {
+                if (has_next) mx_cur = finish_scores(sn, kv1);
+            } else {
+                mx_cur = xhalf_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
             }
-            // ---- phase B: O^T += V^T P^T for tile it; mask and max of tile it+1 ----
-            tile_pv<D>(v_this + v_lane, pb, oacc);
-            if (has_next) mx_cur = finish_scores(sn, kv1);
             wait_vmem();
             __syncthreads();
         };
