@@ -64,11 +64,13 @@ struct FwdCfg {
     static constexpr int NSLOT = NS + NP;
     static constexpr int PD = 2;             // slots between an LDS operand read and its product
     static constexpr int NDMA = (KSEGS + VSEGS + kWaves - 1) / kWaves;  // 1 KB copies per wave per step
+    static constexpr int DMA_SLOTS = NSLOT;  // the copies are spread over the whole step
 };
 
-// Items [spread<E, S>(j), spread<E, S>(j + 1)) of E items dealt evenly over S slots.
+// Items [spread<E, S>(j), spread<E, S>(j + 1)) of E items dealt evenly over
+// slots 0 .. S-1 (none to later slots).
 template <int E, int S>
-constexpr int spread(int j) { return (j * E + S - 1) / S; }
+constexpr int spread(int j) { return ((j < S ? j : S) * E + S - 1) / S; }
 
 // Which K/V tiles a query block visits.
 struct TileList {
@@ -427,23 +429,47 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                 dma16_untracked(isk ? srd_k : srd_v, (isk ? k_dst : v_dst) + (uint32_t)seg * 1024u,
                                 dma_rel[i] + (isk ? k_src : v_src));
             };
+            // The probabilities of tile it go through three stages, each in its own
+            // slot so that no slot waits on a result it has just issued: z = c s - c m
+            // (slot j-1), p = 2^z (slot j), row sum and bf16 packing (slot j+1).
+            constexpr int NE = 16 * C::NKB;  // scores per lane per tile
+            auto for_items = [&](auto jc, auto&& fn) {   // the scores whose exponential is in slot j
+                constexpr int j = decltype(jc)::value;
+                if constexpr (j >= 0 && j < C::NS)
+                    static_for<spread<NE, C::NS>(j + 1) - spread<NE, C::NS>(j)>(
+                        [&](auto ec) { fn(std::integral_constant<int, spread<NE, C::NS>(j) + decltype(ec)::value>{}); });
+            };
+            auto z_stage = [&](auto ic) {
+                constexpr int idx = decltype(ic)::value;
+                float z = __builtin_fmaf(sc[idx / 16][idx % 16], c, -mc);
+                pin(z);
+                sc[idx / 16][idx % 16] = z;
+            };
+            auto p_stage = [&](auto ic) {
+                constexpr int idx = decltype(ic)::value;
+                float p = exp2f_hw(sc[idx / 16][idx % 16]);
+                pin(p);
+                sc[idx / 16][idx % 16] = p;
+            };
+            auto sum_stage = [&](auto ic) {
+                constexpr int idx = decltype(ic)::value;
+                ls[idx & 3] += sc[idx / 16][idx % 16];
+                pin(ls[idx & 3]);
+                if constexpr (idx % 8 == 7) pb[idx / 8] = pack8<((idx / 8) & 1) * 8>(sc[idx / 16]);
+            };
             static_for<C::PD>([&](auto jc) { read_operand(jc); });
+            for_items(std::integral_constant<int, 0>{}, z_stage);
             static_for<C::NSLOT>([&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 if constexpr (j + C::PD < C::NSLOT) read_operand(std::integral_constant<int, j + C::PD>{});
+                for_items(std::integral_constant<int, j + 1>{}, z_stage);
+                for_items(std::integral_constant<int, j>{}, p_stage);
+                for_items(std::integral_constant<int, j - 1>{}, sum_stage);
                 if constexpr (j < C::NS) {
                     // ---- S(it+1) product; exponentials of tile it ----
                     constexpr int kk = j / C::NKB, kb = j % C::NKB;
                     if constexpr (kk == 0) sn[kb] = mfma32(opnd[j], qf[0], f32x16{});
                     else sn[kb] = mfma32(opnd[j], qf[kk], sn[kb]);
-                    static_for<spread<16 * C::NKB, C::NS>(j + 1) - spread<16 * C::NKB, C::NS>(j)>([&](auto ec) {
-                        constexpr int idx = spread<16 * C::NKB, C::NS>(j) + decltype(ec)::value;
-                        const float p = exp2f_hw(__builtin_fmaf(sc[idx / 16][idx % 16], c, -mc));
-                        sc[idx / 16][idx % 16] = p;
-                        ls[idx & 3] += p;
-                        pin(ls[idx & 3]);
-                        if constexpr (idx % 8 == 7) pb[idx / 8] = pack8<((idx / 8) & 1) * 8>(sc[idx / 16]);
-                    });
                 } else {
                     // ---- O += V(it)^T P(it)^T product; row max of S(it+1) ----
                     constexpr int jp = j - C::NS, t = jp / C::NDM, dm = jp % C::NDM;
@@ -457,8 +483,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                         });
                     }
                 }
-                static_for<spread<C::NDMA, C::NSLOT>(j + 1) - spread<C::NDMA, C::NSLOT>(j)>([&](auto ic) {
-                    dma_op(std::integral_constant<int, spread<C::NDMA, C::NSLOT>(j) + decltype(ic)::value>{});
+                static_for<spread<C::NDMA, C::DMA_SLOTS>(j + 1) - spread<C::NDMA, C::DMA_SLOTS>(j)>([&](auto ic) {
+                    dma_op(std::integral_constant<int, spread<C::NDMA, C::DMA_SLOTS>(j) + decltype(ic)::value>{});
                 });
                 __builtin_amdgcn_sched_barrier(0);
             });
