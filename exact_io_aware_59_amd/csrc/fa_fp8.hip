@@ -315,8 +315,10 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
 #pragma unroll
                 for (int dm = 0; dm < C::NDM; dm++) oacc[dm] *= alpha;
             }
-            const float mc = m_ref == -INFINITY ? 0.f : m_ref * c;
-            // P (times 2^8) to E4M3, in the accumulator's key order: byte 16 kb + r
+            // 2^8 P = 2^(c s - c m + 8): the factor rides in the exponent's addend, and
+            // the running sum is of 2^8 P (divided out, exactly, at the end)
+            const float mc8 = (m_ref == -INFINITY ? 0.f : m_ref * c) - (float)kPExp;
+            // 2^8 P to E4M3, in the accumulator's key order: byte 16 kb + r
             i32x8 pb;
             float ls = 0.f;
 #pragma unroll
@@ -326,11 +328,11 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
                     float p[4];
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        p[e] = exp2f_hw(__builtin_fmaf(s[kb][4 * w + e], c, -mc));
+                        p[e] = exp2f_hw(__builtin_fmaf(s[kb][4 * w + e], c, -mc8));
                         ls += p[e];
                     }
-                    int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * 256.f, p[1] * 256.f, 0, false);
-                    word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * 256.f, p[3] * 256.f, word, true);
+                    int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                    word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
                     pb[4 * kb + w] = word;
                 }
             l_part += ls;
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
         if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
 
         // epilogue: one division per row, bf16 output, lse (rows >= N dropped)
-        const float l = xhalf_sum(l_part);
+        const float l = xhalf_sum(l_part) * (1.f / (float)(1 << kPExp));
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const rsrc_t ro = make_rsrc(O + head_off, head_bytes * 2);
 #pragma unroll
