@@ -210,25 +210,42 @@ __device__ __forceinline__ void tile_pv(const bf16* vl, const bf16x8 (&pb)[FwdCf
 // live pair (causal, or no slopes): two FMAs per score (linear_bias_scores),
 // and only tiles that reach an edge of the window, the diagonal or N are
 // masked; 2 handles any window and slopes (variant_scores on every tile).
-template <int D, bool CAUSAL, bool MASK, int VK>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+//
+// KS = 2 (launches with fewer than two workgroups per CU, e.g. 8 heads of a
+// causal N = 8192): eight waves in two groups of four share the 128 query rows
+// and split the block's K/V tiles, group g taking tiles g, g+2, ...; each
+// group has its own tile buffers and copies.  This doubles the waves per SIMD
+// and halves the longest chain of tiles.  At the end group 1 hands its running
+// (reference max, row sum, O) to group 0 through LDS, which merges them with
+// the online-softmax rescale ("FlashAttention 深度解析" section 二) and writes
+// the block.
+template <int D, bool CAUSAL, bool MASK, int VK, int KS>
+__global__ __launch_bounds__(64 * kWaves * KS, 2 / KS) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, float c, uint32_t qsign,
     const uint8_t* __restrict__ mask, int nb, int nqb, int n_items, int H, int wl, int wr,
     const float* __restrict__ slopes, float cs) {
     using C = FwdCfg<D>;
     constexpr bool VAR = VK != 0, LIN = VK == 1, GEN = VK == 2;
+    constexpr int NW = kWaves * KS;  // waves per workgroup
     // four separate arrays (not one 2-D array) so that alias analysis can tell
-    // the tile being read from the tile the DMA is filling
-    __shared__ __attribute__((aligned(1024))) bf16 kbuf0[C::KTILE];
-    __shared__ __attribute__((aligned(1024))) bf16 kbuf1[C::KTILE];
-    __shared__ __attribute__((aligned(1024))) bf16 vbuf0[C::VTILE];
-    __shared__ __attribute__((aligned(1024))) bf16 vbuf1[C::VTILE];
-    __shared__ int wave_cnt[kWaves];
+    // the tile being read from the tile the DMA is filling; group g uses
+    // [g * TILE, (g + 1) * TILE) of each
+    __shared__ __attribute__((aligned(1024))) bf16 kbuf0s[KS * C::KTILE];
+    __shared__ __attribute__((aligned(1024))) bf16 kbuf1s[KS * C::KTILE];
+    __shared__ __attribute__((aligned(1024))) bf16 vbuf0s[KS * C::VTILE];
+    __shared__ __attribute__((aligned(1024))) bf16 vbuf1s[KS * C::VTILE];
+    __shared__ int wave_cnt[NW];
     extern __shared__ uint16_t mask_cols[];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
+    const int group = KS == 1 ? 0 : wave_id / kWaves;             // tile group
+    const int wave = KS == 1 ? wave_id : wave_id % kWaves;        // wave within the group (its 32 queries)
+    bf16* const kbuf0 = kbuf0s + group * C::KTILE;
+    bf16* const kbuf1 = kbuf1s + group * C::KTILE;
+    bf16* const vbuf0 = vbuf0s + group * C::VTILE;
+    bf16* const vbuf1 = vbuf1s + group * C::VTILE;
     const int h = lane >> 5, l32 = lane & 31;
     const int k_lane = l32 * C::KS + 8 * h;            // this lane's K operand offset in a tile
     const int v_lane = lane_tr_offset<C::VS>(lane);    // this lane's transposing-read offset
@@ -301,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             const int lo_col = kv_lo / kMaskBlock;
             const int max_col = kv_hi > kv_lo ? (kv_hi - 1) / kMaskBlock : lo_col - 1;
             const int cnt = max_col >= lo_col
-                                ? build_block_list<kWaves>(mask + (size_t)qb * nb, 1, lo_col, max_col, mask_cols,
+                                ? build_block_list<NW>(mask + (size_t)qb * nb, 1, lo_col, max_col, mask_cols,
                                                            wave_cnt)
                                 : 0;
             tl.cols = mask_cols;
@@ -347,19 +364,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             }
         };
 
+        // this group's m-th tile and the number of steps (the same for every
+        // group, so that all waves pass the same barriers); a group's tiles past
+        // the list start at row N: they read as zero and are masked out
+        const int n_steps = (tl.n + KS - 1) / KS;
+        auto kvg = [&](int m) -> int {
+            const int t = KS * m + group;
+            return t < tl.n ? tl.kv0(t) : N;
+        };
+
         // ---- prologue: K0, V0, K1 in flight; S(0) and its max ----
         f32x16 sa[C::NKB], sb[C::NKB];
         float mx_cur = -INFINITY;
-        if (tl.n > 0) {
-            load_tile<D, C::KS, C::KSEGS>(rk, kbuf0, tl.kv0(0), wave, lane);
-            load_tile<D, C::VS, C::VSEGS>(rv, vbuf0, tl.kv0(0), wave, lane);
-            if (tl.n > 1) load_tile<D, C::KS, C::KSEGS>(rk, kbuf1, tl.kv0(1), wave, lane);
+        if (n_steps > 0) {
+            load_tile<D, C::KS, C::KSEGS>(rk, kbuf0, kvg(0), wave, lane);
+            load_tile<D, C::VS, C::VSEGS>(rv, vbuf0, kvg(0), wave, lane);
+            if (n_steps > 1) load_tile<D, C::KS, C::KSEGS>(rk, kbuf1, kvg(1), wave, lane);
             wait_vmem();
         }
         __syncthreads();
-        if (tl.n > 0) {
+        if (n_steps > 0) {
             tile_scores<D>(kbuf0 + k_lane, qf, sa);
-            mx_cur = finish_scores(sa, tl.kv0(0));
+            mx_cur = finish_scores(sa, kvg(0));
         }
         __syncthreads();  // every wave is done with kbuf0 before K2 overwrites it
 
@@ -385,10 +411,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             bf16* k_next = P ? kbuf0 : kbuf1;   // K(it+1)
             bf16* v_this = P ? vbuf1 : vbuf0;   // V(it)
             bf16* v_next = P ? vbuf0 : vbuf1;   // V(it+1)
-            const bool has_next = it + 1 < tl.n;
+            const bool has_next = it + 1 < n_steps;
             // tiles past the end are copied from rows >= N, which read as zero
-            const int kv1 = has_next ? tl.kv0(it + 1) : N;
-            const int kv2 = it + 2 < tl.n ? tl.kv0(it + 2) : N;
+            const int kv1 = kvg(it + 1);
+            const int kv2 = kvg(it + 2);
 
             // ---- reference-max update for tile it (rare O rescale) ----
             {
@@ -506,13 +532,47 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         };
 
         int it = 0;
-        for (; it + 1 < tl.n; it += 2) {
+        for (; it + 1 < n_steps; it += 2) {
             step(std::integral_constant<int, 0>{}, it, sa, sb);
             step(std::integral_constant<int, 1>{}, it + 1, sb, sa);
         }
-        if (it < tl.n) step(std::integral_constant<int, 0>{}, it, sa, sb);
+        if (it < n_steps) step(std::integral_constant<int, 0>{}, it, sa, sb);
+
+        if constexpr (KS == 2) {
+            // ---- group 1 hands (m_ref, l, O) of its rows to group 0 through LDS
+            // (the V buffers hold O, lane-contiguous; kbuf0s the max and sum) ----
+            float* xml = reinterpret_cast<float*>(kbuf0s);
+            auto xo = [&](int dm, int r) -> float* {
+                float* base = reinterpret_cast<float*>((dm & 1) ? vbuf1s : vbuf0s);
+                return base + (((dm >> 1) * kWaves + wave) * 16 + r) * 64 + lane;
+            };
+            static_assert((C::NDM + 1) / 2 * kWaves * 16 * 64 * 4 <= 2 * C::VTILE * 2, "O exchange must fit");
+            if (group == 1) {
+#pragma unroll
+                for (int dm = 0; dm < C::NDM; dm++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) *xo(dm, r) = oacc[dm][r];
+                xml[wave * 64 + lane] = m_ref;
+                xml[(kWaves + wave) * 64 + lane] = l_part;
+            }
+            __syncthreads();
+            if (group == 0) {
+                const float m1 = xml[wave * 64 + lane], l1 = xml[(kWaves + wave) * 64 + lane];
+                const float mm = fmaxf(m_ref, m1);
+                const float f0 = m_ref == -INFINITY ? 0.f : exp2f_hw((m_ref - mm) * c);
+                const float f1 = m1 == -INFINITY ? 0.f : exp2f_hw((m1 - mm) * c);
+#pragma unroll
+                for (int dm = 0; dm < C::NDM; dm++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) oacc[dm][r] = oacc[dm][r] * f0 + *xo(dm, r) * f1;
+                l_part = l_part * f0 + l1 * f1;
+                m_ref = mm;
+            }
+            __syncthreads();  // the exchange buffers are the next block's tiles
+        }
 
         // ---- epilogue: one division per row, bf16 output, lse (buffer stores drop rows >= N) ----
+        if (KS == 2 && group != 0) continue;
         const float l = xhalf_sum(l_part);
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
@@ -532,13 +592,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
 }
 
-template <int D, bool CAUSAL, bool MASK, int VK>
-hipError_t launch(const FwdArgs& a) {
-    const int nqb = (a.N + kBr - 1) / kBr;
-    const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
-    const int n_items = a.BH * per_head;
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int D, bool CAUSAL, bool MASK, int VK, int KS>
+hipError_t launch_ks(const FwdArgs& a, int nqb, int n_items) {
     const size_t dyn = MASK ? (size_t)a.nb * sizeof(uint16_t) : 0;
-    auto kern = fwd_bf16_kernel<D, CAUSAL, MASK, VK>;
+    auto kern = fwd_bf16_kernel<D, CAUSAL, MASK, VK, KS>;
     if (dyn > 0) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
@@ -546,10 +616,21 @@ hipError_t launch(const FwdArgs& a) {
     // c = 0 (scale 0) would turn -inf * 0 into NaN; any c below 1e-30 gives the
     // same fp32 probabilities (2^(s*c) == 1 for every finite score s).
     const float c = a.c < 1e-30f ? 1e-30f : a.c;
-    hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads), dyn, a.stream,
+    hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads * KS), dyn, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.N,
                        VK != 0 ? 1.0f : c, a.qsign, a.mask, a.nb, nqb, n_items, a.H, a.wl, a.wr, a.slopes, c);
     return hipGetLastError();
+}
+
+// Two workgroups of four waves fit on a CU; with fewer work items than that
+// the tile-split eight-wave workgroup keeps two waves on every SIMD.
+template <int D, bool CAUSAL, bool MASK, int VK>
+hipError_t launch(const FwdArgs& a) {
+    const int nqb = (a.N + kBr - 1) / kBr;
+    const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
+    const int n_items = a.BH * per_head;
+    if (n_items < 2 * cu_count()) return launch_ks<D, CAUSAL, MASK, VK, 2>(a, nqb, n_items);
+    return launch_ks<D, CAUSAL, MASK, VK, 1>(a, nqb, n_items);
 }
 
 }  // namespace
