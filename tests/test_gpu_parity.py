@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import workloads as W
-from tests.gpu_cases import TOL_BF16, TOL_F32, check, say, to_device, to_host64
+from tests.gpu_cases import TOL_BF16, TOL_F32, check, check_bf16_out, say, to_device, to_host64
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -66,6 +66,18 @@ FWD_BF16 = [
 ]
 
 
+# Launches with fewer work items than two workgroups per CU take the
+# eight-wave, tile-split forward (most small cases above); these shapes have at
+# least 512 items, which on the 256-CU MI355X keeps the four-wave launch, with
+# ragged tails, a causal diagonal, a block mask and a negative scale.
+FWD_BF16_FOUR_WAVE = [
+    (1, 520, 200, 128, True, None, None),
+    (1, 180, 300, 64, False, "rand", None),
+    (1, 520, 130, 128, True, None, -0.09),
+]
+FWD_BF16 = FWD_BF16 + FWD_BF16_FOUR_WAVE
+
+
 @pytest.mark.parametrize("case", FWD_BF16, ids=lambda c: "B{}H{}N{}d{}{}{}{}".format(
     *c[:4], "c" if c[4] else "", "-" + c[5] if c[5] else "", "" if c[6] is None else f"-s{c[6]}"))
 def test_fwd_bf16_small(case):
@@ -78,7 +90,7 @@ def test_fwd_bf16_small(case):
     o, lse = fa.forward(q, k, v, scale, causal, _dev_mask(m))
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attn_fwd(x["q"].values, x["k"].values, x["v"].values, scale, causal, m)
-    check("O", to_host64(o), o_ref, TOL_BF16["o"])
+    check_bf16_out("O", to_host64(o), o_ref, TOL_BF16["o"])
     check("lse", to_host64(lse), lse_ref, TOL_BF16["lse"])
 
 
@@ -108,6 +120,38 @@ def test_bwd_bf16_small(case):
     dq, dk, dv = fa.backward(q, k, v, o, do, lse, scale, causal, dm)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attn_bwd(x["q"].values, x["k"].values, x["v"].values, x["do"].values, scale, causal, m)
+    check("dQ", to_host64(dq), rq, TOL_BF16["dq"])
+    check("dK", to_host64(dk), rk, TOL_BF16["dk"])
+    check("dV", to_host64(dv), rv, TOL_BF16["dv"])
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_bwd_very_negative_scores_ragged(causal):
+    """Every score of every row near -150 (scale 1, Q near +u and K near -u with
+    |u|^2 = 150) and N = 200, not a multiple of the 64-key tile: lse2 is about
+    -210 in log2 units, so 2^(c s - lse2) at the zero score of a K row past N
+    would overflow fp32.  The gradients must stay finite and match the oracle
+    (which shifts by the exact row maximum).  dO is scaled by 0.1 so that every
+    gradient stays below 2, where bf16 output rounding is inside the tolerance."""
+    B, H, N, d = 1, 2, 200, 64
+    scale = 1.0
+    say(f"[bwd bf16 negative scores] B={B} H={H} N={N} d={d} causal={causal}")
+    u = np.full(d, math.sqrt(150.0 / d), dtype=np.float32)
+    noise = 0.05 * W.normal((B, H, N, d), 91)
+    def tens(x):
+        bits = W.f32_to_bf16_bits(x.astype(np.float32))
+        return W.Tensor(W.bf16_bits_to_f32(bits), bits, "bf16")
+    x = {"q": tens(u + noise), "k": tens(-u + 0.05 * W.normal((B, H, N, d), 92)),
+         "v": tens(W.normal((B, H, N, d), 93)), "do": tens(0.1 * W.normal((B, H, N, d), 94))}
+    q, k, v, do = (to_device(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, scale, causal)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, scale, causal)
+    torch.cuda.synchronize()
+    rq, rk, rv, ro, rl, _ = oracle.attn_bwd(x["q"].values, x["k"].values, x["v"].values, x["do"].values,
+                                            scale, causal, None, return_fwd=True)
+    assert float(np.max(rl)) < -100.0  # the construction really has very negative rows
+    check("O", to_host64(o), ro, TOL_BF16["o"])
+    check("lse", to_host64(lse), rl, TOL_BF16["lse"])
     check("dQ", to_host64(dq), rq, TOL_BF16["dq"])
     check("dK", to_host64(dk), rk, TOL_BF16["dk"])
     check("dV", to_host64(dv), rv, TOL_BF16["dv"])
