@@ -158,7 +158,17 @@ struct F8Cfg {
     static constexpr int NKK = D / 64;                 // k-steps of S^T (64 dims each)
     static constexpr int NDM = D / 32;                 // 32-dim blocks of O^T
     static_assert(SEGS * 1024 == TILE, "tiles must be whole 1 KB copies");
+    // one pipelined step = a fixed schedule of NSLOT matrix products
+    static constexpr int NS = 2 * NKK;                 // S^T products of a tile (two 32-key blocks)
+    static constexpr int NSLOT = NS + NDM;             // then the O^T products
+    static constexpr int PD = 2;                       // slots between an LDS operand read and its product
+    static constexpr int NDMA = (2 * SEGS + kF8Waves - 1) / kF8Waves;  // 1 KB copies per wave per step
 };
+
+// Items [spread<E, S>(j), spread<E, S>(j + 1)) of E items dealt evenly over
+// slots 0 .. S-1 (none to later slots).
+template <int E, int S>
+constexpr int f8_spread(int j) { return ((j < S ? j : S) * E + S - 1) / S; }
 
 template <int D>
 __device__ __forceinline__ void f8_load_tile(rsrc_t r, uint8_t* tile, int kv0, int wave, int lane) {
@@ -240,6 +250,25 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
         v_lane = key * C::RS + 16 * (G & 1) + 8 * half;            // + 32 dm per 32-dim block
     }
 
+    // copies of the pipelined steps: descriptors and, for copy i of this wave,
+    // its lane's byte offset from the tile's first row (1 KB segment
+    // i*kF8Waves + wave of the K tile, then of the V tile; past the V tile its
+    // last segment again; a lane whose bytes fall in row padding re-reads the
+    // row's first chunk)
+    const int32x4_t srd_k = make_srd(K + head_off, head_bytes);
+    const int32x4_t srd_v = make_srd(V + head_off, head_bytes);
+    uint32_t dma_rel[C::NDMA];
+#pragma unroll
+    for (int i = 0; i < C::NDMA; i++) {
+        const int g = i * kF8Waves + wave;
+        const int seg = g < C::SEGS ? g : min(g - C::SEGS, C::SEGS - 1);
+        const int el = seg * 1024 + lane * 16;
+        const int row = el / C::RS;
+        int col = el - row * C::RS;
+        col = col < D ? col : 0;
+        dma_rel[i] = (uint32_t)(row * D + col);
+    }
+
     for (int bi = 0; bi < nb; bi++) {
         const int q0 = qblk[bi] * kF8Br;
         const int qw = q0 + wave * 32;
@@ -266,97 +295,167 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
         for (int dm = 0; dm < C::NDM; dm++) oacc[dm] = f32x16{};
         float m_ref = -INFINITY, l_part = 0.f;
 
-        if (ntiles > 0) {
-            f8_load_tile<D>(rk, kbuf0, 0, wave, lane);
-            f8_load_tile<D>(rv, vbuf0, 0, wave, lane);
-        }
-        wait_vmem();
-        __syncthreads();
-
-        auto step = [&](auto parity, int it) {
-            constexpr int P = decltype(parity)::value;
-            const uint8_t* kt = P ? kbuf1 : kbuf0;
-            const uint8_t* vt = P ? vbuf1 : vbuf0;
-            const int kv0 = it * kF8Block;
-            if (it + 1 < ntiles) {
-                f8_load_tile<D>(rk, P ? kbuf0 : kbuf1, kv0 + kF8Block, wave, lane);
-                f8_load_tile<D>(rv, P ? vbuf0 : vbuf1, kv0 + kF8Block, wave, lane);
-            }
-            const int sk = 127 + ke[it], sv_ = 127 + ve[it];
-            // S^T for 64 keys: two 32-key blocks
-            f32x16 s[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; kb++) {
-                s[kb] = f32x16{};
-#pragma unroll
-                for (int kk = 0; kk < C::NKK; kk++)
-                    s[kb] = mfma_f8(lds_read32(kt + k_lane + kb * 32 * C::RS + 64 * kk), qf[kk], s[kb], sk, sq);
-            }
-            if ((CAUSAL && kv0 + kF8Block - 1 > qw) || kv0 + kF8Block > N) {
+        // tiles past the last one start at row N: they read as zero and are masked out
+        auto kv_of = [&](int t) -> int { return t < ntiles ? t * kF8Block : N; };
+        auto needs_mask = [&](int kv0) { return (CAUSAL && kv0 + kF8Block - 1 > qw) || kv0 + kF8Block > N; };
+        // scores of a tile at kv0: keys past the diagonal or N to -inf, then the row max
+        auto finish = [&](f32x16 (&sv)[2], int kv0) -> float {
+            if (needs_mask(kv0)) {
 #pragma unroll
                 for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                     for (int r = 0; r < 16; r++) {
                         const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        s[kb][r] = ((CAUSAL && key > my_q) || key >= N) ? -INFINITY : s[kb][r];
+                        sv[kb][r] = ((CAUSAL && key > my_q) || key >= N) ? -INFINITY : sv[kb][r];
                     }
             }
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[kb][r]);
-            mx = xhalf_max(mx);
-            // the reference follows the exact running max, so p <= 1
-            if (mx > m_ref) {
-                const float alpha = m_ref == -INFINITY ? 0.f : exp2f_hw((m_ref - mx) * c);
-                m_ref = mx;
-                l_part *= alpha;
+                for (int r = 0; r < 16; r++) mx = fmaxf(mx, sv[kb][r]);
+            return xhalf_max(mx);
+        };
+        auto kscale = [&](int t) -> int { return 127 + ke[min(t, nblk - 1)]; };
+
+        // ---- prologue: K0, V0, K1 in flight; S(0) and its max ----
+        f32x16 sa[2], sb[2];
+        float mx_cur = -INFINITY;
+        if (ntiles > 0) {
+            f8_load_tile<D>(rk, kbuf0, 0, wave, lane);
+            f8_load_tile<D>(rv, vbuf0, 0, wave, lane);
+            if (ntiles > 1) f8_load_tile<D>(rk, kbuf1, kF8Block, wave, lane);
+        }
+        wait_vmem();
+        __syncthreads();
+        if (ntiles > 0) {
+            const int sk = kscale(0);
 #pragma unroll
-                for (int dm = 0; dm < C::NDM; dm++) oacc[dm] *= alpha;
+            for (int kb = 0; kb < 2; kb++) {
+                sa[kb] = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < C::NKK; kk++)
+                    sa[kb] = mfma_f8(lds_read32(kbuf0 + k_lane + kb * 32 * C::RS + 64 * kk), qf[kk], sa[kb], sk, sq);
+            }
+            mx_cur = finish(sa, 0);
+        }
+        __syncthreads();  // every wave is done with kbuf0 before K2 overwrites it
+
+        // One pipelined step, a fixed schedule of NSLOT matrix products closed by
+        // scheduling fences (as in the bf16 forward): slots [0, NS) compute S of
+        // tile it+1 while the vector ALUs take 2^8 P of tile it and pack it to
+        // E4M3; slots [NS, NSLOT) compute O^T += V^T P^T of tile it while they
+        // take the row max of tile it+1.  Every slot issues the LDS operand read
+        // of slot j + PD and a share of the copies (K of tile it+2, V of tile
+        // it+1, into the buffers tiles it and it-1 left before the last barrier).
+        // The reference max follows the exact running max (P <= 1, so 2^8 P fits
+        // E4M3); scores of tile it+1 that need a mask are finished after the
+        // schedule and their max taken again.
+        auto step = [&](auto parity, int it, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+            constexpr int P = decltype(parity)::value;
+            uint8_t* k_this = P ? kbuf1 : kbuf0;  // K(it), then K(it+2)
+            const uint8_t* k_next = P ? kbuf0 : kbuf1;
+            const uint8_t* v_this = P ? vbuf1 : vbuf0;
+            uint8_t* v_next = P ? vbuf0 : vbuf1;
+            const bool has_next = it + 1 < ntiles;
+            const int kv1 = kv_of(it + 1), kv2 = kv_of(it + 2);
+            const int sk1 = kscale(it + 1), sv0 = 127 + ve[it];
+            // ---- reference-max update for tile it ----
+            {
+                const bool bump = mx_cur > m_ref;
+                if (__ballot(bump) != 0) {
+                    const float alpha = bump ? (m_ref == -INFINITY ? 0.f : exp2f_hw((m_ref - mx_cur) * c)) : 1.f;
+                    if (bump) m_ref = mx_cur;
+                    l_part *= alpha;
+#pragma unroll
+                    for (int dm = 0; dm < C::NDM; dm++) oacc[dm] *= alpha;
+                }
             }
             // 2^8 P = 2^(c s - c m + 8): the factor rides in the exponent's addend, and
             // the running sum is of 2^8 P (divided out, exactly, at the end)
             const float mc8 = (m_ref == -INFINITY ? 0.f : m_ref * c) - (float)kPExp;
-            // 2^8 P to E4M3, in the accumulator's key order: byte 16 kb + r
+            const uint32_t k_dst = lds_addr_of(k_this), v_dst = lds_addr_of(v_next);
+            const uint32_t k_src = (uint32_t)kv2 * D, v_src = (uint32_t)kv1 * D;
+            i32x8 opnd[C::NSLOT];
             i32x8 pb;
-            float ls = 0.f;
+            float ls[4] = {0.f, 0.f, 0.f, 0.f};
+            float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            float pw[4];
+            auto read_operand = [&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if constexpr (j < C::NS) {
+                    constexpr int kk = j / 2, kb = j % 2;
+                    opnd[j] = lds_read32(k_next + k_lane + kb * 32 * C::RS + 64 * kk);
+                } else {
+                    constexpr int dm = j - C::NS;
 #pragma unroll
-            for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-                for (int w = 0; w < 4; w++) {
-                    float p[4];
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        p[e] = exp2f_hw(__builtin_fmaf(s[kb][4 * w + e], c, -mc8));
-                        ls += p[e];
+                    for (int r8 = 0; r8 < 4; r8++) {
+                        const i32x2 t2 = lds_tr8(v_this + v_lane + r8 * 16 * C::RS + 32 * dm);
+                        opnd[j][2 * r8] = t2[0];
+                        opnd[j][2 * r8 + 1] = t2[1];
                     }
-                    int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-                    word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-                    pb[4 * kb + w] = word;
                 }
-            l_part += ls;
-            // O^T += V^T P^T: A = V^T from four transposing reads (8 keys each)
-#pragma unroll
-            for (int dm = 0; dm < C::NDM; dm++) {
-                i32x8 va;
-#pragma unroll
-                for (int r8 = 0; r8 < 4; r8++) {
-                    const i32x2 t2 = lds_tr8(vt + v_lane + r8 * 16 * C::RS + 32 * dm);
-                    va[2 * r8] = t2[0];
-                    va[2 * r8 + 1] = t2[1];
+            };
+            auto dma_op = [&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                const int g = i * kF8Waves + wave;
+                const bool isk = g < C::SEGS;
+                const int seg = isk ? g : min(g - C::SEGS, C::SEGS - 1);
+                dma16_untracked(isk ? srd_k : srd_v, (isk ? k_dst : v_dst) + (uint32_t)seg * 1024u,
+                                dma_rel[i] + (isk ? k_src : v_src));
+            };
+            static_for<C::PD>([&](auto jc) { read_operand(jc); });
+            static_for<C::NSLOT>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if constexpr (j == 0) __builtin_amdgcn_s_setprio(1);
+                if constexpr (j == C::NS) __builtin_amdgcn_s_setprio(0);
+                if constexpr (j + C::PD < C::NSLOT) read_operand(std::integral_constant<int, j + C::PD>{});
+                if constexpr (j < C::NS) {
+                    // ---- S(it+1) product; 2^8 P of tile it to E4M3 ----
+                    constexpr int kk = j / 2, kb = j % 2;
+                    if constexpr (kk == 0) sn[kb] = mfma_f8(opnd[j], qf[0], f32x16{}, sk1, sq);
+                    else sn[kb] = mfma_f8(opnd[j], qf[kk], sn[kb], sk1, sq);
+                    static_for<f8_spread<32, C::NS>(j + 1) - f8_spread<32, C::NS>(j)>([&](auto ec) {
+                        constexpr int idx = f8_spread<32, C::NS>(j) + decltype(ec)::value;  // 16 kb + r
+                        float p = exp2f_hw(__builtin_fmaf(sc[idx / 16][idx % 16], c, -mc8));
+                        pin(p);
+                        pw[idx % 4] = p;
+                        ls[idx % 4] += p;
+                        pin(ls[idx % 4]);
+                        if constexpr (idx % 4 == 3) {
+                            int word = __builtin_amdgcn_cvt_pk_fp8_f32(pw[0], pw[1], 0, false);
+                            word = __builtin_amdgcn_cvt_pk_fp8_f32(pw[2], pw[3], word, true);
+                            pb[idx / 4] = word;
+                        }
+                    });
+                } else {
+                    // ---- O^T += V^T P^T of tile it; row max of S(it+1) ----
+                    constexpr int dm = j - C::NS;
+                    oacc[dm] = mfma_f8(opnd[j], pb, oacc[dm], sv0, 127 - kPExp);
+                    static_for<f8_spread<16, C::NDM>(dm + 1) - f8_spread<16, C::NDM>(dm)>([&](auto ec) {
+                        constexpr int pr = f8_spread<16, C::NDM>(dm) + decltype(ec)::value;
+                        constexpr int kb = (2 * pr) / 16, r = (2 * pr) % 16;
+                        mp[pr & 3] = fmaxf(mp[pr & 3], fmaxf(sn[kb][r], sn[kb][r + 1]));
+                        pin(mp[pr & 3]);
+                    });
                 }
-                oacc[dm] = mfma_f8(va, pb, oacc[dm], sv_, 127 - kPExp);
-            }
+                static_for<f8_spread<C::NDMA, C::NSLOT>(j + 1) - f8_spread<C::NDMA, C::NSLOT>(j)>([&](auto ic) {
+                    dma_op(std::integral_constant<int, f8_spread<C::NDMA, C::NSLOT>(j) + decltype(ic)::value>{});
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+            if (has_next && needs_mask(kv1)) mx_cur = finish(sn, kv1);
+            else mx_cur = xhalf_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
             wait_vmem();
             __syncthreads();
         };
         int it = 0;
         for (; it + 1 < ntiles; it += 2) {
-            step(std::integral_constant<int, 0>{}, it);
-            step(std::integral_constant<int, 1>{}, it + 1);
+            step(std::integral_constant<int, 0>{}, it, sa, sb);
+            step(std::integral_constant<int, 1>{}, it + 1, sb, sa);
         }
-        if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
+        if (it < ntiles) step(std::integral_constant<int, 0>{}, it, sa, sb);
 
         // epilogue: one division per row, bf16 output, lse (rows >= N dropped)
         const float l = xhalf_sum(l_part) * (1.f / (float)(1 << kPExp));
