@@ -419,8 +419,14 @@ __global__ __launch_bounds__(64 * kWaves * KS, 2 / KS) void fwd_bf16_kernel(
             // ---- reference-max update for tile it (rare O rescale) ----
             {
                 const float m_new = fmaxf(m_ref, mx_cur);
+                // the local window / ALiBi kernels follow the exact running max: there
+                // one key often dominates a row, and a reference that trails the max
+                // leaves that key's weight 2^(m - m_ref) off a power of two, so its bf16
+                // rounding (up to 2^-9 of the dominant term) reaches the output; the
+                // plain kernels keep the lazy reference (about 7 % faster)
+                constexpr float thr = VK != 0 ? 0.f : kRescaleThreshold;
                 const bool bump = m_new != -INFINITY &&
-                                  (m_ref == -INFINITY || (m_new - m_ref) * c > kRescaleThreshold);
+                                  (m_ref == -INFINITY || (m_new - m_ref) * c > thr);
                 if (__builtin_expect(__ballot(bump) != 0, 0)) {
                     const float alpha = bump ? (m_ref == -INFINITY ? 0.f : exp2f_hw((m_ref - m_new) * c)) : 1.f;
                     if (bump) m_ref = m_new;
