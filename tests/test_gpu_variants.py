@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import workloads as W
-from tests.gpu_cases import TOL_BF16, TOL_F32, check, say, to_device, to_host64
+from tests.gpu_cases import TOL_BF16, TOL_F32, check, check_bf16_out, say, to_device, to_host64
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -97,6 +97,14 @@ FWD = [
     (1, 1, 300, 128, True, None, None, True, 0.0),
     (2, 2, 1100, 128, True, None, (400, None), True, None),
 ]
+# At least 512 work items (the four-wave launch on a 256-CU MI355X; the cases
+# above take the eight-wave tile-split one): non-causal window + ALiBi (the
+# per-element path) and causal window + ALiBi (the linear-bias path).
+FWD_FOUR_WAVE = [
+    (1, 520, 130, 128, False, None, (50, 20), True, None),
+    (1, 520, 130, 128, True, None, (40, None), True, None),
+]
+FWD = FWD + FWD_FOUR_WAVE
 
 
 @pytest.mark.parametrize("case", FWD, ids=_id)
@@ -113,7 +121,7 @@ def test_fwd_variant_bf16(case):
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attn_fwd(x["q"].values, x["k"].values, x["v"].values, scale, causal, m,
                                      window=_win(win), slopes=None if sl is None else sl.astype(np.float64))
-    check("O", to_host64(o), o_ref, TOL_BF16["o"])
+    check_bf16_out("O", to_host64(o), o_ref, TOL_BF16["o"])
     check("lse", to_host64(lse), lse_ref, TOL_BF16["lse"])
 
 
