@@ -1,6 +1,7 @@
 // Fused exact-attention forward for bf16 on gfx950.
 //
-// One workgroup (4 waves) owns 128 query rows of one (batch, head) and sweeps
+// One workgroup (4 waves; 8 in two tile groups when the launch has fewer than
+// two workgroups per CU) owns 128 query rows of one (batch, head) and sweeps
 // the K/V tiles its mask allows: the Q-outer loop order of FlashAttention-2
 // with the grid spread over batch x heads x query blocks ("FlashAttention
 // 深度解析" section 四; "FlashAttention原理概览" section 3.1).  Per K/V tile
@@ -497,8 +498,9 @@ __global__ __launch_bounds__(64 * kWaves * KS, 2 / KS) void fwd_bf16_kernel(
                 for_items(std::integral_constant<int, j + 1>{}, z_stage);
                 for_items(std::integral_constant<int, j>{}, p_stage);
                 for_items(std::integral_constant<int, j - 1>{}, sum_stage);
-                // The two waves that share a SIMD come from different workgroups and
-                // drift in and out of phase: the wave in its exponential half is
+                // The two waves that share a SIMD (from two workgroups, or from the two
+                // tile groups of an eight-wave one) drift in and out of phase: the
+                // wave in its exponential half is
                 // given issue priority, so its vector work goes out while the other
                 // wave's O^T products keep the matrix core busy (measured: ~4 % on
                 // the causal d=128 forward; no effect at one wave per SIMD).
