@@ -60,22 +60,33 @@ def bf16_rounding(want: np.ndarray) -> np.ndarray:
     return out
 
 
-def check_bf16_out(name: str, got, want, tol: float):
-    """Max-abs check of a bf16 output net of its unavoidable rounding: the
-    error beyond |want - bf16(want)| must stay within tol.  Values of magnitude
-    >= 4 (e.g. O = V_0 on the first causal row) round by up to 2^-6 > 1e-2."""
+def check_bf16_out(name: str, got, want, tol: float, net_from: float = 2.0):
+    """Max-abs check of a bf16 output against the fp64 oracle.
+
+    Every element whose exact value has |want| < net_from must meet the raw
+    bound |got - want| <= tol.  An element with |want| >= net_from is held to
+    the same tol net of its own bf16 rounding |want - bf16(want)|: there the
+    output's half-ulp (2^-7 in [2, 4), 2^-6 in [4, 8)) plus the bf16 rounding
+    of the probabilities before the matrix product (up to 2^-9 |want|) can
+    exceed 1e-2 with nothing wrong (e.g. O = V_0 on the first causal rows).
+    Prints the raw maximum and how many elements took the net rule."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     err = max_abs_err(got, want)
-    if np.isfinite(err):
-        fin = np.isfinite(want)
-        net = np.abs(got - want) - bf16_rounding(want)
-        err_net = float(np.max(net[fin])) if fin.any() else 0.0
-    else:
-        err_net = err
-    say(f"    {name}: max|err| = {err:.3e}, net of bf16 output rounding {err_net:.3e} (tol {tol:.0e})")
-    assert err_net <= tol, f"{name}: max abs error net of output rounding {err_net:.3e} > {tol:.1e}"
-    return err_net
+    assert np.isfinite(err), f"{name}: non-finite pattern or infinite values differ"
+    fin = np.isfinite(want)
+    diff = np.abs(got - want)
+    big = fin & (np.abs(want) >= net_from)
+    small = fin & ~big
+    err_small = float(np.max(diff[small])) if small.any() else 0.0
+    err_net = float(np.max(diff[big] - bf16_rounding(want[big]))) if big.any() else 0.0
+    err_big_raw = float(np.max(diff[big])) if big.any() else 0.0
+    say(f"    {name}: max|err| = {err:.3e}; |want| < {net_from:g}: {err_small:.3e} raw (tol {tol:.0e}); "
+        f"{int(big.sum())} elements with |want| >= {net_from:g}: raw {err_big_raw:.3e}, "
+        f"net of bf16 output rounding {err_net:.3e} (tol {tol:.0e})")
+    assert err_small <= tol, f"{name}: max abs error {err_small:.3e} > {tol:.1e} where |want| < {net_from:g}"
+    assert err_net <= tol, f"{name}: error net of output rounding {err_net:.3e} > {tol:.1e} where |want| >= {net_from:g}"
+    return max(err_small, err_net)
 
 
 def check(name: str, got, want, tol: float, extra: str = ""):
