@@ -136,8 +136,9 @@ def _stream(stream) -> Optional[int]:
 
 
 def _dims(q) -> Tuple[int, int, int, int]:
-    if q.dim() != 4:
-        raise ValueError("expected [B, H, N, d]")
+    import torch
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("expected a [B, H, N, d] torch tensor")
     B, H, N, d = q.shape
     return int(B), int(H), int(N), int(d)
 
@@ -158,17 +159,92 @@ def _check(status: int, where: str):
 
 
 # ----------------------------------------------------------------------------
+# argument validation (the C ABI sees plain pointers and cannot check what a
+# buffer holds: a wrong dtype, shape or device would make a kernel read or
+# write past an allocation, so every mirror checks its tensors first and
+# raises ValueError before anything is enqueued)
+# ----------------------------------------------------------------------------
+
+def _dtype(name: str):
+    import torch
+    return {"bf16": torch.bfloat16, "f32": torch.float32, "u8": torch.uint8, "i8": torch.int8,
+            "i32": torch.int32, "bool": torch.bool}[name]
+
+
+def _tensors(where: str, specs, device=None):
+    """specs: (name, tensor or None, dtype name(s), shape or None, optional).  Checks dtype, then
+    shape, then that every tensor is a contiguous CUDA tensor on one device; returns that device."""
+    import torch
+    for name, t, dts, shape, optional in specs:
+        if t is None:
+            if optional:
+                continue
+            raise ValueError(f"{where}: {name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{where}: {name} must be a torch tensor")
+        allowed = [_dtype(x) for x in (dts if isinstance(dts, tuple) else (dts,))]
+        if t.dtype not in allowed:
+            raise ValueError(f"{where}: {name} has dtype {t.dtype}, expected "
+                             + " or ".join(str(a) for a in allowed))
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{where}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    for name, t, _, _, _ in specs:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{where}: {name} is on {t.device}, expected a CUDA (HIP) device")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{where}: {name} is on {t.device}, the other tensors on {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{where}: {name} must be contiguous")
+    return device
+
+
+def _attn_specs(dt: str, q, B, H, N, d, **named):
+    """Specs for tensors of the attention entry points: bf16/f32 [B,H,N,d] ones
+    (q, k, v, o, do, dq, dk, dv), lse float32 [B,H,N]."""
+    specs = [("q", q, dt, (B, H, N, d), False)] if q is not None else []
+    for name, t in named.items():
+        if name == "lse":
+            specs.append(("lse", t, "f32", (B, H, N), False))
+        else:
+            specs.append((name, t, dt, (B, H, N, d), False))
+    return specs
+
+
+def _mask_spec(blockmask, N):
+    """uint8 or bool [ceil(N/128)]^2 (both one byte per entry, nonzero = kept)."""
+    nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    return ("blockmask", blockmask, ("u8", "bool"), (nb, nb), True)
+
+
+def _variant_specs(H, window, alibi_slopes):
+    if window is not None:
+        if len(window) != 2 or any(w is not None and not isinstance(w, int) for w in window):
+            raise ValueError("window must be (left, right) with int or None bounds")
+    return [("alibi_slopes", alibi_slopes, "f32", (H,), True)]
+
+
+def _ws_spec(workspace):
+    return ("workspace", workspace, "u8", None, True)
+
+
+# ----------------------------------------------------------------------------
 # C ABI mirrors
 # ----------------------------------------------------------------------------
 
 def fa_fwd(q, k, v, o, lse, scale: float, causal: bool = False, blockmask=None, stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_fwd", _attn_specs("bf16", q, B, H, N, d, k=k, v=v, o=o, lse=lse) + [_mask_spec(blockmask, N)])
     _check(load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                          int(bool(causal)), _ptr(blockmask), _stream(stream)), "fa_fwd")
 
 
 def fa_fwd_f32(q, k, v, o, lse, scale: float, causal: bool = False, blockmask=None, stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_fwd_f32", _attn_specs("f32", q, B, H, N, d, k=k, v=v, o=o, lse=lse) + [_mask_spec(blockmask, N)])
     _check(load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                              int(bool(causal)), _ptr(blockmask), _stream(stream)), "fa_fwd_f32")
 
@@ -176,6 +252,8 @@ def fa_fwd_f32(q, k, v, o, lse, scale: float, causal: bool = False, blockmask=No
 def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, blockmask=None,
            workspace=None, stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_bwd", _attn_specs("bf16", q, B, H, N, d, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv)
+             + [_mask_spec(blockmask, N), _ws_spec(workspace)])
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                          _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(blockmask),
@@ -185,6 +263,8 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, 
 def fa_bwd_f32(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, blockmask=None,
                workspace=None, stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_bwd_f32", _attn_specs("f32", q, B, H, N, d, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv)
+             + [_mask_spec(blockmask, N), _ws_spec(workspace)])
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().fa_bwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                              _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
@@ -197,6 +277,7 @@ def _nbytes(t) -> int:
 
 def fa_bwd_prep(o, do, lse, workspace, stream=None):
     B, H, N, d = _dims(o)
+    _tensors("fa_bwd_prep", _attn_specs("bf16", None, B, H, N, d, o=o, do=do, lse=lse) + [_ws_spec(workspace)])
     _check(load().fa_bwd_prep(_ptr(o), _ptr(do), _ptr(lse), B, H, N, d, _ptr(workspace), _nbytes(workspace),
                               _stream(stream)), "fa_bwd_prep")
 
@@ -204,6 +285,8 @@ def fa_bwd_prep(o, do, lse, workspace, stream=None):
 def fa_bwd_main(q, k, v, do, dk, dv, scale: float, causal: bool = False, blockmask=None, workspace=None,
                 stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_bwd_main", _attn_specs("bf16", q, B, H, N, d, k=k, v=v, do=do, dk=dk, dv=dv)
+             + [_mask_spec(blockmask, N), _ws_spec(workspace)])
     _check(load().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv), B, H, N, d,
                               float(scale), int(bool(causal)), _ptr(blockmask), _ptr(workspace),
                               _nbytes(workspace), _stream(stream)), "fa_bwd_main")
@@ -211,6 +294,8 @@ def fa_bwd_main(q, k, v, do, dk, dv, scale: float, causal: bool = False, blockma
 
 def fa_bwd_dq(q, k, v, do, dq, scale: float, causal: bool = False, blockmask=None, workspace=None, stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_bwd_dq", _attn_specs("bf16", q, B, H, N, d, k=k, v=v, do=do, dq=dq)
+             + [_mask_spec(blockmask, N), _ws_spec(workspace)])
     _check(load().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), B, H, N, d, float(scale),
                             int(bool(causal)), _ptr(blockmask), _ptr(workspace), _nbytes(workspace),
                             _stream(stream)), "fa_bwd_dq")
@@ -219,6 +304,8 @@ def fa_bwd_dq(q, k, v, do, dq, scale: float, causal: bool = False, blockmask=Non
 def fa_fwd_ex(q, k, v, o, lse, scale: float, causal: bool = False, blockmask=None, window=None,
               alibi_slopes=None, stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_fwd_ex", _attn_specs("bf16", q, B, H, N, d, k=k, v=v, o=o, lse=lse) + [_mask_spec(blockmask, N)]
+             + _variant_specs(H, window, alibi_slopes))
     _check(load().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                             int(bool(causal)), _ptr(blockmask), _variant(window, alibi_slopes), _stream(stream)),
            "fa_fwd_ex")
@@ -227,6 +314,8 @@ def fa_fwd_ex(q, k, v, o, lse, scale: float, causal: bool = False, blockmask=Non
 def fa_fwd_f32_ex(q, k, v, o, lse, scale: float, causal: bool = False, blockmask=None, window=None,
                   alibi_slopes=None, stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_fwd_f32_ex", _attn_specs("f32", q, B, H, N, d, k=k, v=v, o=o, lse=lse)
+             + [_mask_spec(blockmask, N)] + _variant_specs(H, window, alibi_slopes))
     _check(load().fa_fwd_f32_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                                 int(bool(causal)), _ptr(blockmask), _variant(window, alibi_slopes),
                                 _stream(stream)), "fa_fwd_f32_ex")
@@ -235,6 +324,8 @@ def fa_fwd_f32_ex(q, k, v, o, lse, scale: float, causal: bool = False, blockmask
 def fa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, blockmask=None, window=None,
               alibi_slopes=None, workspace=None, stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_bwd_ex", _attn_specs("bf16", q, B, H, N, d, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv)
+             + [_mask_spec(blockmask, N), _ws_spec(workspace)] + _variant_specs(H, window, alibi_slopes))
     _check(load().fa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                             _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(blockmask),
                             _variant(window, alibi_slopes), _ptr(workspace), _nbytes(workspace),
@@ -244,6 +335,8 @@ def fa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = Fals
 def fa_bwd_f32_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, blockmask=None,
                   window=None, alibi_slopes=None, workspace=None, stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_bwd_f32_ex", _attn_specs("f32", q, B, H, N, d, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv)
+             + [_mask_spec(blockmask, N), _ws_spec(workspace)] + _variant_specs(H, window, alibi_slopes))
     _check(load().fa_bwd_f32_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                                 _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(blockmask),
                                 _variant(window, alibi_slopes), _ptr(workspace), _nbytes(workspace),
@@ -253,6 +346,8 @@ def fa_bwd_f32_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = 
 def fa_bwd_main_ex(q, k, v, do, dk, dv, scale: float, causal: bool = False, blockmask=None, window=None,
                    alibi_slopes=None, workspace=None, stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_bwd_main_ex", _attn_specs("bf16", q, B, H, N, d, k=k, v=v, do=do, dk=dk, dv=dv)
+             + [_mask_spec(blockmask, N), _ws_spec(workspace)] + _variant_specs(H, window, alibi_slopes))
     _check(load().fa_bwd_main_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv), B, H, N, d,
                                  float(scale), int(bool(causal)), _ptr(blockmask), _variant(window, alibi_slopes),
                                  _ptr(workspace), _nbytes(workspace), _stream(stream)), "fa_bwd_main_ex")
@@ -261,6 +356,8 @@ def fa_bwd_main_ex(q, k, v, do, dk, dv, scale: float, causal: bool = False, bloc
 def fa_bwd_dq_ex(q, k, v, do, dq, scale: float, causal: bool = False, blockmask=None, window=None,
                  alibi_slopes=None, workspace=None, stream=None):
     B, H, N, d = _dims(q)
+    _tensors("fa_bwd_dq_ex", _attn_specs("bf16", q, B, H, N, d, k=k, v=v, do=do, dq=dq)
+             + [_mask_spec(blockmask, N), _ws_spec(workspace)] + _variant_specs(H, window, alibi_slopes))
     _check(load().fa_bwd_dq_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), B, H, N, d, float(scale),
                                int(bool(causal)), _ptr(blockmask), _variant(window, alibi_slopes), _ptr(workspace),
                                _nbytes(workspace), _stream(stream)), "fa_bwd_dq_ex")
@@ -279,10 +376,22 @@ def fa_decode_paged(q, k_cache, v_cache, block_table, seqlens, o, lse, scale: fl
     """Decode over a paged KV cache (bf16): q [B,H,Nq,d]; caches [num_pages,page_size,H_kv,d];
     block_table int32 [B,max_pages]; seqlens int32 [B]; writes o [B,H,Nq,d] and lse [B,H,Nq]."""
     B, H, Nq, d = _dims(q)
-    num_pages, page_size, H_kv, dk = (int(x) for x in k_cache.shape)
-    if dk != d or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("k_cache and v_cache must be [num_pages, page_size, H_kv, d]")
+    import torch
+    if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 4 or int(k_cache.shape[3]) != d:
+        raise ValueError("fa_decode_paged: k_cache must be [num_pages, page_size, H_kv, d]")
+    num_pages, page_size, H_kv, _ = (int(x) for x in k_cache.shape)
+    if not isinstance(block_table, torch.Tensor) or block_table.dim() != 2 or int(block_table.shape[0]) != B:
+        raise ValueError("fa_decode_paged: block_table must be int32 [B, max_pages]")
     max_pages = int(block_table.shape[1])
+    _tensors("fa_decode_paged", [
+        ("q", q, "bf16", (B, H, Nq, d), False),
+        ("k_cache", k_cache, "bf16", (num_pages, page_size, H_kv, d), False),
+        ("v_cache", v_cache, "bf16", (num_pages, page_size, H_kv, d), False),
+        ("block_table", block_table, "i32", (B, max_pages), False),
+        ("seqlens", seqlens, "i32", (B,), False),
+        ("o", o, "bf16", (B, H, Nq, d), False),
+        ("lse", lse, "f32", (B, H, Nq), False),
+        _ws_spec(workspace)])
     _check(load().fa_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seqlens),
                                   _ptr(o), _ptr(lse), B, H, H_kv, Nq, d, num_pages, page_size, max_pages,
                                   float(scale), int(bool(causal)), _ptr(workspace), _nbytes(workspace),
@@ -319,12 +428,23 @@ def fa_fp8_quantize(x, codes, exps, signs=None, k_side: bool = False, stream=Non
     """Block-quantize bf16 x [B,H,N,d] to E4M3 codes (uint8, same shape) and int8
     block exponents [B,H,ceil(N/64)]; signs (float [d] of +-1) applies the incoherent map."""
     B, H, N, d = _dims(x)
+    _tensors("fa_fp8_quantize", [
+        ("x", x, "bf16", (B, H, N, d), False),
+        ("codes", codes, "u8", (B, H, N, d), False),
+        ("exps", exps, "i8", (B, H, (N + FP8_BLOCK - 1) // FP8_BLOCK), False),
+        ("signs", signs, "f32", (d,), True)])
     _check(load().fa_fp8_quantize(_ptr(x), _ptr(codes), _ptr(exps), B, H, N, d, _ptr(signs), int(bool(k_side)),
                                   _stream(stream)), "fa_fp8_quantize")
 
 
 def fa_fwd_fp8(q8, qe, k8, ke, v8, ve, o, lse, scale: float, causal: bool = False, stream=None):
     B, H, N, d = _dims(q8)
+    ne = (B, H, (N + FP8_BLOCK - 1) // FP8_BLOCK)
+    _tensors("fa_fwd_fp8", [
+        ("q8", q8, "u8", (B, H, N, d), False), ("qe", qe, "i8", ne, False),
+        ("k8", k8, "u8", (B, H, N, d), False), ("ke", ke, "i8", ne, False),
+        ("v8", v8, "u8", (B, H, N, d), False), ("ve", ve, "i8", ne, False),
+        ("o", o, "bf16", (B, H, N, d), False), ("lse", lse, "f32", (B, H, N), False)])
     _check(load().fa_fwd_fp8(_ptr(q8), _ptr(qe), _ptr(k8), _ptr(ke), _ptr(v8), _ptr(ve), _ptr(o), _ptr(lse), B, H,
                              N, d, float(scale), int(bool(causal)), _stream(stream)), "fa_fwd_fp8")
 
@@ -354,6 +474,15 @@ def forward_fp8(q, k, v, scale: Optional[float] = None, causal: bool = False, si
     return o, lse
 
 
+def _compute_dtype(q, where: str):
+    """forward / backward run bf16 tensors on the bf16 kernels and float32 ones
+    on the fp32 kernels; any other dtype is rejected (the entry points then
+    check every other tensor against q)."""
+    import torch
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"{where}: q has dtype {q.dtype}; bfloat16 and float32 are supported")
+
+
 def _default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
@@ -363,6 +492,7 @@ def forward(q, k, v, scale: Optional[float] = None, causal: bool = False, blockm
     """Returns (o, lse).  bf16 inputs use fa_fwd(_ex), float32 inputs fa_fwd_f32(_ex)."""
     import torch
     B, H, N, d = _dims(q)
+    _compute_dtype(q, "forward")
     scale = _default_scale(d) if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -386,8 +516,9 @@ def backward(q, k, v, o, do, lse, scale: Optional[float] = None, causal: bool = 
     """Returns (dq, dk, dv).  bf16 inputs use fa_bwd(_ex), float32 inputs fa_bwd_f32(_ex)."""
     import torch
     B, H, N, d = _dims(q)
+    _compute_dtype(q, "backward")
     scale = _default_scale(d) if scale is None else scale
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     if ws is None:
         ws = workspace(B, H, N, d, q.device)
     if window is None and alibi_slopes is None:

@@ -1,0 +1,143 @@
+"""The Python binding rejects tensors whose dtype, shape or device does not
+match what the C ABI will read, before anything is enqueued (CPU only: every
+case raises ValueError inside the binding, libfa.so is never called).
+
+The C ABI takes plain pointers, so it cannot see a buffer's size: a float16 q
+passed to the fp32 kernels, a lse of the wrong length, a block mask smaller
+than ceil(N/128)^2 or fewer ALiBi slopes than heads would make a kernel read
+or write past an allocation."""
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import exact_io_aware_59_amd as fa  # noqa: E402
+
+B, H, N, d = 1, 2, 200, 64
+NB = (N + 127) // 128
+
+
+def t(shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def attn(dtype=torch.bfloat16):
+    return {n: t((B, H, N, d), dtype) for n in ("q", "k", "v", "o", "do", "dq", "dk", "dv")}
+
+
+def lse():
+    return t((B, H, N), torch.float32)
+
+
+def raises(match, fn, *a, **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(*a, **kw)
+
+
+def test_fwd_rejects_wrong_dtype():
+    x = attn()
+    raises("k has dtype torch.float16", fa.fa_fwd, x["q"], t((B, H, N, d), torch.float16), x["v"], x["o"], lse(), 0.1)
+    raises("q has dtype torch.float32", fa.fa_fwd, t((B, H, N, d), torch.float32), x["k"], x["v"], x["o"], lse(), 0.1)
+    raises("lse has dtype torch.bfloat16", fa.fa_fwd, x["q"], x["k"], x["v"], x["o"], t((B, H, N)), 0.1)
+    y = attn(torch.float32)
+    raises("o has dtype torch.bfloat16", fa.fa_fwd_f32, y["q"], y["k"], y["v"], x["o"], lse(), 0.1)
+
+
+def test_fwd_rejects_wrong_shape():
+    x = attn()
+    raises(r"v has shape \(1, 2, 100, 64\)", fa.fa_fwd, x["q"], x["k"], t((B, H, 100, d)), x["o"], lse(), 0.1)
+    raises(r"lse has shape \(1, 2, 199\)", fa.fa_fwd, x["q"], x["k"], x["v"], x["o"], t((B, H, N - 1), torch.float32),
+           0.1)
+    raises("expected a \\[B, H, N, d\\]", fa.fa_fwd, t((H, N, d)), x["k"], x["v"], x["o"], lse(), 0.1)
+
+
+def test_mask_rejects_wrong_size_or_dtype():
+    x = attn()
+    raises(r"blockmask has shape \(1, 1\)", fa.fa_fwd, x["q"], x["k"], x["v"], x["o"], lse(), 0.1, False,
+           t((1, 1), torch.uint8))
+    raises("blockmask has dtype torch.int32", fa.fa_fwd, x["q"], x["k"], x["v"], x["o"], lse(), 0.1, False,
+           t((NB, NB), torch.int32))
+    # a correctly sized uint8 or bool mask passes the dtype/shape checks (then fails the device check)
+    for dt in (torch.uint8, torch.bool):
+        raises("expected a CUDA", fa.fa_fwd, x["q"], x["k"], x["v"], x["o"], lse(), 0.1, False, t((NB, NB), dt))
+
+
+def test_device_checks():
+    x = attn()
+    raises("q is on cpu, expected a CUDA", fa.fa_fwd, x["q"], x["k"], x["v"], x["o"], lse(), 0.1)
+    raises("must be a torch tensor", fa.fa_fwd, x["q"], [0.0] * 4, x["v"], x["o"], lse(), 0.1)
+
+
+def test_slopes_rejected():
+    x = attn()
+    raises(r"alibi_slopes has shape \(1,\)", fa.fa_fwd_ex, x["q"], x["k"], x["v"], x["o"], lse(), 0.1,
+           alibi_slopes=t((H - 1,), torch.float32))
+    raises("alibi_slopes has dtype torch.float64", fa.fa_fwd_ex, x["q"], x["k"], x["v"], x["o"], lse(), 0.1,
+           alibi_slopes=t((H,), torch.float64))
+    raises("window must be", fa.fa_fwd_ex, x["q"], x["k"], x["v"], x["o"], lse(), 0.1, window=(1, 2, 3))
+    raises("window must be", fa.fa_fwd_ex, x["q"], x["k"], x["v"], x["o"], lse(), 0.1, window=(1.5, None))
+
+
+def test_bwd_rejects():
+    x = attn()
+    ws = t((fa_ws_bytes(),), torch.uint8)
+    args = [x[n] for n in ("q", "k", "v", "o", "do")] + [lse()] + [x[n] for n in ("dq", "dk", "dv")]
+    bad = list(args)
+    bad[4] = t((B, H, N, d), torch.float16)  # dO
+    raises("do has dtype torch.float16", fa.fa_bwd, *bad, 0.1, False, None, ws)
+    bad = list(args)
+    bad[7] = t((B, H, N + 1, d))  # dk
+    raises("dk has shape", fa.fa_bwd, *bad, 0.1, False, None, ws)
+    raises("workspace has dtype torch.float32", fa.fa_bwd, *args, 0.1, False, None, t((16,), torch.float32))
+    raises("q is on cpu", fa.fa_bwd, *args, 0.1, False, None, ws)
+    raises("lse has shape", fa.fa_bwd_prep, x["o"], x["do"], t((B, H, 3), torch.float32), ws)
+    raises("dv has dtype", fa.fa_bwd_main, x["q"], x["k"], x["v"], x["do"], x["dk"], t((B, H, N, d), torch.float32),
+           0.1, False, None, ws)
+    raises("dq has shape", fa.fa_bwd_dq, x["q"], x["k"], x["v"], x["do"], t((B, H, N, 32)), 0.1, False, None, ws)
+    y = attn(torch.float32)
+    raises("dq has dtype torch.bfloat16", fa.fa_bwd_f32, *[y[n] for n in ("q", "k", "v", "o", "do")], lse(),
+           x["dq"], y["dk"], y["dv"], 0.1, False, None, ws)
+    raises("alibi_slopes has shape", fa.fa_bwd_ex, *args, 0.1, False, None, alibi_slopes=t((3,), torch.float32),
+           workspace=ws)
+
+
+def fa_ws_bytes():
+    return 2 * 256 * ((B * H * N * 4 + 255) // 256)
+
+
+def test_forward_backward_reject_other_dtypes():
+    for dt in (torch.float16, torch.float64, torch.int8):
+        q = t((B, H, N, d), dt)
+        raises("bfloat16 and float32 are supported", fa.forward, q, q, q, 0.1)
+        raises("bfloat16 and float32 are supported", fa.backward, q, q, q, q, q, lse(), 0.1)
+
+
+def test_decode_rejects():
+    Nq, Hkv, P, S, MP = 1, 1, 4, 32, 3
+    q = t((2, H, Nq, d))
+    kc = t((P, S, Hkv, d))
+    bt = t((2, MP), torch.int32)
+    sl = t((2,), torch.int32)
+    o = t((2, H, Nq, d))
+    ls = t((2, H, Nq), torch.float32)
+    raises("block_table has dtype torch.int64", fa.fa_decode_paged, q, kc, kc, t((2, MP), torch.int64), sl, o, ls, 0.1)
+    raises("seqlens has shape", fa.fa_decode_paged, q, kc, kc, bt, t((3,), torch.int32), o, ls, 0.1)
+    raises("v_cache has shape", fa.fa_decode_paged, q, kc, t((P, S, Hkv + 1, d)), bt, sl, o, ls, 0.1)
+    raises("lse has shape", fa.fa_decode_paged, q, kc, kc, bt, sl, o, t((2, H, 2), torch.float32), 0.1)
+    raises("k_cache must be", fa.fa_decode_paged, q, t((P, S, Hkv, 32)), kc, bt, sl, o, ls, 0.1)
+    raises("block_table must be", fa.fa_decode_paged, q, kc, kc, t((3, MP), torch.int32), sl, o, ls, 0.1)
+    raises("q is on cpu", fa.fa_decode_paged, q, kc, kc, bt, sl, o, ls, 0.1)
+
+
+def test_fp8_rejects():
+    x = t((B, H, N, d))
+    codes = t((B, H, N, d), torch.uint8)
+    exps = t((B, H, (N + 63) // 64), torch.int8)
+    raises("exps has shape", fa.fa_fp8_quantize, x, codes, t((B, H, 1), torch.int8))
+    raises("codes has dtype torch.int8", fa.fa_fp8_quantize, x, t((B, H, N, d), torch.int8), exps)
+    raises("signs has shape", fa.fa_fp8_quantize, x, codes, exps, t((d + 1,), torch.float32))
+    o = t((B, H, N, d))
+    raises("ve has dtype torch.uint8", fa.fa_fwd_fp8, codes, exps, codes, exps, codes, t(exps.shape, torch.uint8), o,
+           lse(), 0.1)
+    raises("o has dtype torch.float32", fa.fa_fwd_fp8, codes, exps, codes, exps, codes, exps,
+           t((B, H, N, d), torch.float32), lse(), 0.1)
+    raises("q8 is on cpu", fa.fa_fwd_fp8, codes, exps, codes, exps, codes, exps, o, lse(), 0.1)
