@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "fa.h"
 #include "fa_kernels.h"
 
@@ -16,6 +18,18 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// Whether the product of the (positive) factors is below `limit`, computed
+// without overflow: each partial product stays at most `limit`.
+bool prod_below(long long limit, std::initializer_list<long long> factors) {
+    long long t = 1;
+    for (long long x : factors) {
+        if (x <= 0) return false;
+        if (t > (limit - 1) / x) return false;
+        t *= x;
+    }
+    return t < limit;
+}
+
 // Half-open byte ranges [p, p+n) overlap?
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -25,8 +39,7 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 int check_sizes(int B, int H, int N, int d, float scale, const uint8_t* mask) {
     if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
-    const long long total = (long long)B * H * N * d;
-    if (total >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+    if (!prod_below(1LL << 31, {B, H, N, d})) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (mask && N > kMaxMaskN) return FA_ERR_UNSUPPORTED;
     // the bf16 kernels address one head with 32-bit byte offsets and may form
@@ -177,7 +190,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
-    if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+    if (B < 1 || H < 1 || N < 1 || d < 1 || !prod_below(1LL << 31, {B, H, N, d})) return 0;
     const size_t rows = (size_t)B * H * N;
     return 2 * align_up(rows * sizeof(float));
 }
@@ -268,11 +281,11 @@ static void decode_plan(int B, int H, int H_kv, int Nq, int page_size, int max_p
 static int decode_check(int B, int H, int H_kv, int Nq, int d, int page_size, int max_pages) {
     if (B < 1 || H < 1 || H_kv < 1 || Nq < 1 || d < 1 || page_size < 1 || max_pages < 1) return FA_ERR_INVALID_ARG;
     if (H % H_kv != 0) return FA_ERR_INVALID_ARG;
-    if ((long long)B * H * Nq * d >= (1LL << 31)) return FA_ERR_INVALID_ARG;
-    if ((long long)max_pages * page_size >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+    if (!prod_below(1LL << 31, {B, H, Nq, d})) return FA_ERR_INVALID_ARG;
+    if (!prod_below(1LL << 31, {max_pages, page_size})) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (page_size % 32 != 0) return FA_ERR_UNSUPPORTED;
-    if ((long long)page_size * H_kv * d * 2 >= (1LL << 32)) return FA_ERR_UNSUPPORTED;
+    if (!prod_below(1LL << 32, {page_size, H_kv, d, 2})) return FA_ERR_UNSUPPORTED;
     return FA_OK;
 }
 

@@ -35,8 +35,10 @@
  *           accumulation, fp32 softmax statistics, outputs rounded to bfloat16
  *           (round to nearest even).  fa_fwd_f32 / fa_bwd_f32: float tensors.
  * Memory    every pointer is device memory owned by the caller.  The library
- *           never allocates, frees or synchronizes, holds no global state and
- *           is re-entrant.  Outputs must not alias inputs.
+ *           never allocates, frees or synchronizes and is re-entrant; its only
+ *           host-side state is a per-device cache of the compute-unit count
+ *           (read once with hipDeviceGetAttribute, used to size launches).
+ *           Outputs must not alias inputs.
  * Streams   `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *           enqueue work and return; results are ready once the stream is
  *           synchronized.  Kernel faults surface at the caller's next sync.

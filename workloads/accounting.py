@@ -87,13 +87,12 @@ def bwd_bytes(B: int, H: int, N: int, d: int, dtype: str, nb_mask: int = 0) -> i
 
 
 def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
-    """Extra traffic of this implementation's backward beyond the floor.
-
-    D = rowsum(dO*O) is written once and read once (fp32 per row); the fp32 dQ
-    accumulator is cleared once and read once by the final conversion (the
-    atomic read-modify-writes into it are on-chip L2 traffic when they hit).
-    """
-    return 2 * F32_BYTES * B * H * N + 2 * F32_BYTES * B * H * N * d
+    """Extra traffic of this implementation's backward beyond the floor: two
+    fp32 row vectors (D = rowsum(dO*O) and lse in log2 units), each written once
+    by the preprocessing kernel and read by the key-outer and dQ kernels.  dQ
+    is accumulated in registers by the query-outer kernel, so there is no O(N d)
+    fp32 accumulator and no atomic traffic."""
+    return 2 * F32_BYTES * B * H * N * 3
 
 
 def naive_score_bytes(B: int, H: int, N: int, dtype_bytes: int) -> int:
