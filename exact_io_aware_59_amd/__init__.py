@@ -29,11 +29,12 @@ __all__ = [
     "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex", "fa_bwd_dq_ex", "Variant",
     "forward", "backward", "workspace", "fa_decode_workspace_size", "fa_decode_paged", "decode_workspace",
     "decode_paged", "fa_fp8_quantize", "fa_fwd_fp8", "quantize_fp8", "forward_fp8", "FP8_BLOCK",
-    "MASK_BLOCK", "ABI_VERSION",
+    "MASK_BLOCK", "ABI_VERSION", "fa_bwd_noalloc", "NOALLOC_MAX_ROWS",
 ]
 
 MASK_BLOCK = 128
-ABI_VERSION = 4  # FA_VERSION of the fa.h these argument lists follow
+ABI_VERSION = 5  # FA_VERSION of the fa.h these argument lists follow
+NOALLOC_MAX_ROWS = 2097152  # FA_NOALLOC_MAX_ROWS
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
 
@@ -76,11 +77,12 @@ def load():
     lib.fa_fwd_f32_ex.argtypes = lib.fa_fwd_ex.argtypes
     lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp, sz, vp]
     lib.fa_bwd_f32_ex.argtypes = lib.fa_bwd_ex.argtypes
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp]
     lib.fa_bwd_main_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp, sz, vp]
     lib.fa_bwd_dq_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp, sz, vp]
     for name in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq",
                  "fa_version", "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex",
-                 "fa_bwd_dq_ex", "fa_decode_paged", "fa_fp8_quantize", "fa_fwd_fp8"):
+                 "fa_bwd_dq_ex", "fa_decode_paged", "fa_fp8_quantize", "fa_fwd_fp8", "fa_bwd_noalloc"):
         getattr(lib, name).restype = i
     lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_decode_workspace_size.restype = sz
@@ -330,6 +332,19 @@ def fa_bwd_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = Fals
                             _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(blockmask),
                             _variant(window, alibi_slopes), _ptr(workspace), _nbytes(workspace),
                             _stream(stream)), "fa_bwd_ex")
+
+
+def fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, blockmask=None,
+                   window=None, alibi_slopes=None, stream=None):
+    """fa_bwd_ex without a workspace: the library's static device scratch holds
+    the backward's row vectors (B*H*N <= NOALLOC_MAX_ROWS; calls that overlap
+    in time on one GPU race)."""
+    B, H, N, d = _dims(q)
+    _tensors("fa_bwd_noalloc", _attn_specs("bf16", q, B, H, N, d, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv)
+             + [_mask_spec(blockmask, N)] + _variant_specs(H, window, alibi_slopes))
+    _check(load().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(blockmask),
+                                 _variant(window, alibi_slopes), _stream(stream)), "fa_bwd_noalloc")
 
 
 def fa_bwd_f32_ex(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool = False, blockmask=None,

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_kernels.h"
@@ -164,6 +165,37 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch of fa_bwd_noalloc: the two fp32 row vectors of the backward
+// (D and lse in log2 units) for at most FA_NOALLOC_MAX_ROWS rows, laid out as
+// the fa_bwd workspace.  `scratch` names the host-side stand-in of the device
+// array; the device address comes from hipGetSymbolAddress, once per device,
+// and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = 2 * (size_t)FA_NOALLOC_MAX_ROWS * sizeof(float);
+static __device__ __attribute__((aligned(256))) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch` (resolved on the
+// first call on that device, with it current).
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return FA_ERR_HIP;
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return FA_OK;
+}
+static_assert(2 * ((FA_NOALLOC_MAX_ROWS * sizeof(float) + kAlign - 1) / kAlign * kAlign) <= kScratchBytes,
+              "the scratch must hold the backward workspace of FA_NOALLOC_MAX_ROWS rows");
+
 }  // namespace
 
 extern "C" {
@@ -208,6 +240,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* workspace, size_t workspace_bytes, void* stream) {
     return fa_bwd_ex(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, blockmask, nullptr, workspace,
                      workspace_bytes, stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* blockmask, const fa_variant* variant, void* stream) {
+    if (B >= 1 && H >= 1 && N >= 1 && !prod_below((long long)FA_NOALLOC_MAX_ROWS + 1, {B, H, N}))
+        return FA_ERR_SCRATCH;
+    void* ws = nullptr;
+    const int st = scratch_address(&ws);
+    if (st != FA_OK) return st;
+    return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+                                (const uint16_t*)dO, lse, (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, B, H, N, d,
+                                scale, causal, blockmask, variant, ws, kScratchBytes, stream, true, kAll);
 }
 
 int fa_bwd_prep(const void* o, const void* dO, const float* lse, int B, int H, int N, int d, void* workspace,
@@ -401,6 +446,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_UNSUPPORTED: return "unsupported configuration";
         case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case FA_ERR_HIP: return "HIP runtime error while enqueueing";
+        case FA_ERR_SCRATCH: return "B*H*N exceeds the static scratch of fa_bwd_noalloc (FA_NOALLOC_MAX_ROWS rows)";
         default: return "unknown status";
     }
 }

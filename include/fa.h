@@ -67,11 +67,12 @@ typedef enum {
     FA_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, non-finite scale, aliasing, too large */
     FA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. head dimension not 64 or 128) */
     FA_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or smaller than the *_workspace_size() */
-    FA_ERR_HIP = 4          /* the HIP runtime reported an error while enqueueing */
+    FA_ERR_HIP = 4,         /* the HIP runtime reported an error while enqueueing */
+    FA_ERR_SCRATCH = 5      /* fa_bwd_noalloc: B*H*N exceeds FA_NOALLOC_MAX_ROWS */
 } fa_status;
 
 #define FA_MASK_BLOCK 128 /* block-mask granularity in rows and columns */
-#define FA_VERSION 4
+#define FA_VERSION 5
 
 /*
  * Local window and ALiBi, the two further built-in variants "FlashAttention
@@ -161,6 +162,27 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, voi
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void* dq, int B, int H,
               int N, int d, float scale, int causal, const uint8_t* blockmask, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_ex without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, semantics, kernels and results
+ * (bit for bit) as fa_bwd_ex, bfloat16 only.  The backward's two fp32 row
+ * vectors live in a static device array of the library (2 * FA_NOALLOC_MAX_ROWS
+ * floats, 16 MiB, held on every GPU the library runs on until the process
+ * ends); its address is resolved once per device with hipGetSymbolAddress on
+ * the first call, which must therefore run with the stream's device current.
+ * The call allocates and frees nothing.  Limit: B*H*N <= FA_NOALLOC_MAX_ROWS,
+ * else FA_ERR_SCRATCH and nothing is enqueued.  Every call on one GPU shares
+ * that array: calls that overlap in time on one GPU (on different streams,
+ * or on one stream from several host threads interleaving their stages)
+ * race and give wrong gradients; calls serialized on one stream do not.
+ * The array needs no clearing: each call writes every entry it reads.
+ */
+#define FA_NOALLOC_MAX_ROWS 2097152
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                   int causal, const uint8_t* blockmask, const fa_variant* variant, void* stream);
 
 /* Backward, float32 tensors; same semantics as fa_bwd (deterministic). */
 int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dO,

@@ -41,8 +41,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status(lib):
-    assert fa.fa_version() == fa.ABI_VERSION == 4
-    for s in range(5):
+    assert fa.fa_version() == fa.ABI_VERSION == 5
+    for s in range(6):
         assert fa.fa_status_string(s)
     assert fa.fa_status_string(99) == "unknown status"
 
@@ -227,3 +227,16 @@ def test_fp8_validation(lib):
     assert quant(d=32) == U and quant(k_side=2) == E
     assert quant(codes=P1 + 100) == E       # codes overlap x
     assert quant(signs=P1 + 2 * BIG + 1) == E  # signs misaligned
+
+
+def test_noalloc_validation(lib):
+    """fa_bwd_noalloc rejects B*H*N beyond its static scratch before touching the GPU."""
+    def call(B, H, N, d=64):
+        return lib.fa_bwd_noalloc(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG,
+                                  P1 + 6 * BIG, P1 + 7 * BIG, P1 + 8 * BIG, B, H, N, d, ctypes.c_float(0.125), 1,
+                                  None, None, None)
+    assert fa.NOALLOC_MAX_ROWS == 2097152
+    assert call(1, 1, fa.NOALLOC_MAX_ROWS + 1) == 5
+    assert call(2, 16, 65537) == 5
+    assert call(1 << 20, 1 << 10, 4096) == 5
+    assert "scratch" in fa.fa_status_string(5)
