@@ -498,15 +498,34 @@ struct DqCfg {
     static constexpr int BC = 64;               // keys per tile
     static constexpr int NKK = D / 16;
     static constexpr int NDM = D / 32;
-    static constexpr int KS = D + 40;           // K tile: 16-row b128 reads and 4-row transposing reads
+    static constexpr int RB = 2 * D;            // K tile: unpadded rows, 16-byte chunks swizzled (swz_sigma)
     static constexpr int VS = PadK<D>::STRIDE;  // V tile: 16-row b128 reads only
-    static constexpr int KTILE = BC * KS;
+    static constexpr int KTILE = BC * D;
     static constexpr int VTILE = BC * VS;
     static constexpr int KSEGS = KTILE / 512;
     static constexpr int VSEGS = VTILE / 512;
     static_assert(KSEGS * 512 == KTILE && VSEGS * 512 == VTILE, "tiles must be whole 1 KB segments");
 };
 constexpr int kDqBr = 128;  // queries per workgroup
+
+// The K tile is read both as rows (16 rows x 16 bytes per b128 operand read)
+// and as columns (4 rows x 64 bytes per half-wave transposing read); no row
+// padding keeps both free of bank conflicts, the chunk swizzle of swz<D> does.
+// Lane i of 1 KB segment s fills LDS chunk position i of its row and fetches
+// the logical chunk that position holds.
+template <int D, int SEGS>
+__device__ __forceinline__ void dq_load_tile_swz(rsrc_t r, bf16* tile, int kv0, int wave, int lane) {
+    constexpr int CPR = D / 8;  // chunks per row
+#pragma unroll
+    for (int i = 0; i < (SEGS + kWaves - 1) / kWaves; i++) {
+        const int s = i * kWaves + wave;
+        if (s < SEGS) {
+            const int row = s * (512 / D) + lane / CPR;
+            const int chunk = (lane % CPR) ^ swz_sigma<D>(row & 15);
+            buf_load16_lds(r, tile + s * 512, ((uint32_t)(kv0 + row) * D + 8 * chunk) * 2);
+        }
+    }
+}
 
 template <int D, int STRIDE, int SEGS>
 __device__ __forceinline__ void dq_load_tile(rsrc_t r, bf16* tile, int kv0, int wave, int lane) {
@@ -543,9 +562,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
-    const int k_lane = l32 * C::KS + 8 * h;           // K rows as the A operand of S^T
-    const int v_lane = l32 * C::VS + 8 * h;           // V rows as the A operand of dP^T
-    const int kt_lane = lane_tr_offset<C::KS>(lane);  // K^T via transposing reads (A operand of dQ^T)
+    const int v_lane = l32 * C::VS + 8 * h;  // V rows as the A operand of dP^T
+    // Byte offsets in the swizzled K tile (loop invariant, per lane; rows 16
+    // apart share a swizzle, so the 32-key block and 16-row half are immediates):
+    //   k_off[kk]: row l32, logical chunk 2kk + h (b128 read of the S^T A operand);
+    //   kt_lo/hi[dm]: rows 4h + j and 4h + j + 8, columns 32dm + 16g + 4q (the two
+    //   transposing reads of the dQ^T A operand, see lds_tr_operand_pad).
+    uint32_t k_off[C::NKK], kt_lo[C::NDM], kt_hi[C::NDM];
+    {
+        const int sig = swz_sigma<D>(l32 & 15);
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; kk++) k_off[kk] = l32 * C::RB + (((2 * kk + h) ^ sig) << 4);
+        const int sl = lane & 15, j = sl >> 2, q = sl & 3, g = (lane >> 4) & 1;
+        const int r = 4 * h + j;
+        const int slo = swz_sigma<D>(r), shi = swz_sigma<D>(r + 8);
+#pragma unroll
+        for (int dm = 0; dm < C::NDM; dm++) {
+            const int cc = 4 * dm + 2 * g + (q >> 1);
+            kt_lo[dm] = r * C::RB + ((cc ^ slo) << 4) + (q & 1) * 8;
+            kt_hi[dm] = (r + 8) * C::RB + ((cc ^ shi) << 4) + (q & 1) * 8;
+        }
+    }
 
     const int item = xcd_remap(blockIdx.x, n_items);
     int bh, qblk[2], nblk;
@@ -627,7 +664,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         for (int dm = 0; dm < C::NDM; dm++) acc[dm] = f32x16{};
 
         if (ntiles > 0) {
-            dq_load_tile<D, C::KS, C::KSEGS>(rk, kbuf0, kv0_of(0), wave, lane);
+            dq_load_tile_swz<D, C::KSEGS>(rk, kbuf0, kv0_of(0), wave, lane);
             dq_load_tile<D, C::VS, C::VSEGS>(rv, vbuf0, kv0_of(0), wave, lane);
         }
         wait_vmem();
@@ -639,7 +676,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             const bf16* vt = P ? vbuf1 : vbuf0;
             const int kv0 = kv0_of(it);
             if (it + 1 < ntiles) {
-                dq_load_tile<D, C::KS, C::KSEGS>(rk, P ? kbuf0 : kbuf1, kv0_of(it + 1), wave, lane);
+                dq_load_tile_swz<D, C::KSEGS>(rk, P ? kbuf0 : kbuf1, kv0_of(it + 1), wave, lane);
                 dq_load_tile<D, C::VS, C::VSEGS>(rv, P ? vbuf0 : vbuf1, kv0_of(it + 1), wave, lane);
             }
             const bool need_mask = GEN || (LIN ? block_has_dead<CAUSAL>(qw, 32, kv0, C::BC, N, var)
@@ -651,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                 dp[kb] = f32x16{};
 #pragma unroll
                 for (int kk = 0; kk < C::NKK; kk++) {
-                    s[kb] = mfma32(lds_read8(kt + k_lane, 32 * kb * C::KS + 16 * kk), qf[kk], s[kb]);
+                    s[kb] = mfma32(lds_read8_b(kt, k_off[kk] + 32 * kb * C::RB), qf[kk], s[kb]);
                     dp[kb] = mfma32(lds_read8(vt + v_lane, 32 * kb * C::VS + 16 * kk), of[kk], dp[kb]);
                 }
             };
@@ -687,7 +724,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                 for (int half = 0; half < 2; half++)
 #pragma unroll
                     for (int dm = 0; dm < C::NDM; dm++)
-                        acc[dm] = mfma32(lds_tr_operand_pad<C::KS>(kt + kt_lane, 32 * kb + 16 * half, 32 * dm),
+                        acc[dm] = mfma32(lds_tr_pair_b(kt, kt_lo[dm] + (32 * kb + 16 * half) * C::RB,
+                                                       kt_hi[dm] + (32 * kb + 16 * half) * C::RB),
                                          sb[kb][half], acc[dm]);
             };
             scores(0);
