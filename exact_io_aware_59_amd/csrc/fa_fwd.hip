@@ -342,7 +342,23 @@ __global__ __launch_bounds__(64 * kWaves * KS, 2 / KS) void fwd_bf16_kernel(
 #pragma unroll
         for (int dm = 0; dm < C::NDM; dm++) oacc[dm] = f32x16{};
         float m_ref = -INFINITY;  // reference max of raw scores (moves lazily)
+        float mc = 0.f;           // m_ref * c (0 while m_ref = -inf)
         float l_part = 0.f;       // this lane's half of the running sum
+        // The local window / ALiBi kernels follow the exact running max: there one
+        // key often dominates a row, and a reference that trails the max leaves
+        // that key's weight 2^(m - m_ref) off a power of two, so its bf16 rounding
+        // (up to 2^-9 of the dominant term) reaches the output; the plain kernels
+        // keep the lazy reference (about 7 % faster).
+        constexpr float thr = VK != 0 ? 0.f : kRescaleThreshold;
+        // Reference decision for the next tile to be exponentiated, taken as soon
+        // as that tile's row max is known: its candidate reference and whether
+        // this lane moves to it.
+        float m_nx = -INFINITY;
+        bool bump_nx = false;
+        auto decide = [&](float mx) {
+            m_nx = fmaxf(m_ref, mx);
+            bump_nx = m_nx != -INFINITY && (m_ref == -INFINITY || (m_nx - m_ref) * c > thr);
+        };
 
         auto needs_mask = [&](int kv0) {
             bool m = (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N);
@@ -387,6 +403,7 @@ __global__ __launch_bounds__(64 * kWaves * KS, 2 / KS) void fwd_bf16_kernel(
         if (n_steps > 0) {
             tile_scores<D>(kbuf0 + k_lane, qf, sa);
             mx_cur = finish_scores(sa, kvg(0));
+            decide(mx_cur);
         }
         __syncthreads();  // every wave is done with kbuf0 before K2 overwrites it
 
@@ -417,26 +434,18 @@ __global__ __launch_bounds__(64 * kWaves * KS, 2 / KS) void fwd_bf16_kernel(
             const int kv1 = kvg(it + 1);
             const int kv2 = kvg(it + 2);
 
-            // ---- reference-max update for tile it (rare O rescale) ----
-            {
-                const float m_new = fmaxf(m_ref, mx_cur);
-                // the local window / ALiBi kernels follow the exact running max: there
-                // one key often dominates a row, and a reference that trails the max
-                // leaves that key's weight 2^(m - m_ref) off a power of two, so its bf16
-                // rounding (up to 2^-9 of the dominant term) reaches the output; the
-                // plain kernels keep the lazy reference (about 7 % faster)
-                constexpr float thr = VK != 0 ? 0.f : kRescaleThreshold;
-                const bool bump = m_new != -INFINITY &&
-                                  (m_ref == -INFINITY || (m_new - m_ref) * c > thr);
-                if (__builtin_expect(__ballot(bump) != 0, 0)) {
-                    const float alpha = bump ? (m_ref == -INFINITY ? 0.f : exp2f_hw((m_ref - m_new) * c)) : 1.f;
-                    if (bump) m_ref = m_new;
-                    l_part *= alpha;
-#pragma unroll
-                    for (int dm = 0; dm < C::NDM; dm++) oacc[dm] *= alpha;
+            // ---- reference-max update for tile it (rare O rescale), decided when
+            // its row max became known ----
+            if (__builtin_expect(__ballot(bump_nx) != 0, 0)) {
+                const float alpha = bump_nx ? (m_ref == -INFINITY ? 0.f : exp2f_hw((m_ref - m_nx) * c)) : 1.f;
+                if (bump_nx) {
+                    m_ref = m_nx;
+                    mc = m_ref * c;
                 }
+                l_part *= alpha;
+#pragma unroll
+                for (int dm = 0; dm < C::NDM; dm++) oacc[dm] *= alpha;
             }
-            const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
 
             const bf16* kl = k_next + k_lane;
             const bf16* vl = v_this + v_lane;
@@ -516,12 +525,25 @@ __global__ __launch_bounds__(64 * kWaves * KS, 2 / KS) void fwd_bf16_kernel(
                     constexpr int jp = j - C::NS, t = jp / C::NDM, dm = jp % C::NDM;
                     oacc[dm] = mfma32(opnd[j], pb[t], oacc[dm]);
                     if constexpr (VK == 0) {
-                        static_for<spread<8 * C::NKB, C::NP>(jp + 1) - spread<8 * C::NKB, C::NP>(jp)>([&](auto ec) {
-                            constexpr int pr = spread<8 * C::NKB, C::NP>(jp) + decltype(ec)::value;
+                        // row max of S(it+1) in the first NP - 3 slots, then its
+                        // half-wave exchange and the reference decision, so the
+                        // next step starts without that dependency chain
+                        constexpr int NMX = C::NP - 3;
+                        static_for<spread<8 * C::NKB, NMX>(jp + 1) - spread<8 * C::NKB, NMX>(jp)>([&](auto ec) {
+                            constexpr int pr = spread<8 * C::NKB, NMX>(jp) + decltype(ec)::value;
                             constexpr int kb = (2 * pr) / 16, r = (2 * pr) % 16;
                             mp[pr & 3] = fmaxf(mp[pr & 3], fmaxf(sn[kb][r], sn[kb][r + 1]));
                             pin(mp[pr & 3]);
                         });
+                        if constexpr (jp == NMX) {
+                            mp[0] = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+                            pin(mp[0]);
+                        } else if constexpr (jp == NMX + 1) {
+                            mx_cur = xhalf_max(mp[0]);
+                            pin(mx_cur);
+                        } else if constexpr (jp == NMX + 2) {
+                            decide(mx_cur);
+                        }
                     }
                 }
                 static_for<spread<C::NDMA, C::DMA_SLOTS>(j + 1) - spread<C::NDMA, C::DMA_SLOTS>(j)>([&](auto ic) {
@@ -531,9 +553,10 @@ __global__ __launch_bounds__(64 * kWaves * KS, 2 / KS) void fwd_bf16_kernel(
             });
             l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
             if (VK != 0 || (has_next && needs_mask(kv1))) {
-                if (has_next) mx_cur = finish_scores(sn, kv1);
-            } else {
-                mx_cur = xhalf_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+                if (has_next) {
+                    mx_cur = finish_scores(sn, kv1);
+                    decide(mx_cur);
+                }
             }
             wait_vmem();
             __syncthreads();
