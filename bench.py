@@ -15,12 +15,19 @@ HIP events on the launch stream time every kernel call of every timed step;
 the five products) against the bf16 dense matrix-core peak.  `cpu_baseline` times the fp64 oracle on a
 bounded sample of the same workload (a few heads).
 
+Timing: W untimed warm-up steps, then untimed settle steps until --settle-s
+seconds (default 0.3) of sustained load have passed -- the GPU's shader clock
+ramps up over about a tenth of a second, so the K timed steps measure the
+steady state (their count is reported as `settle_steps`) -- then exactly K
+timed steps.  `call_us` gives the median, p10 and p90 of every entry point's
+per-call event time.
+
 Options: --steps K --warmup W (timed / untimed steps), --gpus N (only 1 is
 supported: the implementation runs on a single GPU), --workload NAME (another
 workload of workloads.WORKLOADS, forward only unless it has a backward; the
 paged decode workload reports GB/s against the HBM peak),
 --no-cpu-baseline, --copy-calib (run a plain device copy first, for the
-profiler's traffic calibration).
+profiler's traffic calibration), --settle-s S.
 """
 from __future__ import annotations
 
@@ -117,6 +124,7 @@ def cpu_baseline(w, x, mask_np, heads: int) -> dict:
             fl = A.fwd_flops(1, heads, w.N, w.d, w.causal, mask_np)
         if w.backward:
             fl *= 3.5
+        performed = A.oracle_flops(heads, w.N, w.d, A.allowed_pairs(w.N, w.causal, mask_np, window), w.backward)
         what = (f"{'forward+backward' if w.backward else 'forward'} of heads (b=0, h=0..{heads - 1}) of "
                 f"{w.B * w.H}")
     else:
@@ -130,6 +138,8 @@ def cpu_baseline(w, x, mask_np, heads: int) -> dict:
             fl = A.fwd_flops_window(1, 1, w.N, w.d, w.causal, window) * len(rows) / w.N
         else:
             fl = A.fwd_flops(1, 1, w.N, w.d, w.causal, mask_np) * len(rows) / w.N
+        # per sampled row: dense scores over all N keys, P V over its admitted keys
+        performed = len(rows) * 2.0 * w.N * w.d + fl / 2.0
         what = f"forward of 512 sampled rows of {w.B * w.H * w.N}"
     return {
         "value": fl / dt / 1e12,
@@ -137,10 +147,40 @@ def cpu_baseline(w, x, mask_np, heads: int) -> dict:
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": (f"{what} (N={w.N}, d={w.d}, {'causal' if w.causal else 'non-causal'}"
-                   f"{variant_label(w)}), fp64, {dt:.2f} s"),
+                   f"{variant_label(w)}), fp64, {dt:.2f} s; value credits the metric's FLOPs of the sample"),
         "seconds": round(dt, 3),
+        "metric_flops": fl,
+        # the oracle materializes the dense N x N matrices, so it does more arithmetic than the metric credits
+        "oracle_flops_performed": performed,
+        "oracle_gflops_performed": round(performed / dt / 1e9, 2),
         "host_cpu": host_cpu_model(),
     }
+
+
+def settle_until(step, t_start: float, settle_s: float) -> int:
+    """Run untimed steps until `settle_s` seconds have passed since `t_start`.
+
+    The GPU raises its shader clock over roughly a tenth of a second of
+    sustained load (measured on the MI355X: a matrix-core stream runs at
+    1.63 GHz after 0.6 ms and 1.97 GHz after 6 ms of load; the causal forward
+    at 1.32 GHz a few ms after a cold start and at 1.69 GHz after 0.2 s), so a
+    handful of warm-up steps leaves the timed steps on the ramp.  Returns the
+    number of extra steps run."""
+    import torch
+    n = 0
+    while settle_s > 0 and time.perf_counter() - t_start < settle_s:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+        n += 8
+    return n
+
+
+def percentiles_us(times_ms) -> dict:
+    """Median, p10 and p90 of per-call event times (ms in, us out)."""
+    t = sorted(times_ms)
+    return {"median": round(statistics.median(t) * 1e3, 2), "p10": round(t[len(t) // 10] * 1e3, 2),
+            "p90": round(t[(9 * len(t)) // 10] * 1e3, 2)}
 
 
 def variant_label(w) -> str:
@@ -185,9 +225,11 @@ def bench_decode(args, w) -> int:
     def step():
         fa.fa_decode_paged(q, kc, vc, bt, sl, o, lse, w.scale, w.causal, ws, stream)
 
+    t_warm = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    settle_steps = settle_until(step, t_warm, args.settle_s)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for a, b in ev:
@@ -211,6 +253,7 @@ def bench_decode(args, w) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -225,8 +268,7 @@ def bench_decode(args, w) -> int:
             "workspace_bytes": 0 if ws is None else int(ws.numel()),
         },
         "pct_peak": round(100 * value / PEAK_HBM_GBS, 2),
-        "call_us": {"median": round(med * 1e3, 2), "p10": round(times[len(times) // 10] * 1e3, 2),
-                    "p90": round(times[(9 * len(times)) // 10] * 1e3, 2)},
+        "call_us": percentiles_us(times),
         "tflops": round(flops / (med * 1e-3) / 1e12, 2),
         "roofline": {
             "bound": "hbm",
@@ -268,6 +310,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="after the warm-up steps, run further untimed steps until this many seconds of "
+                         "sustained load have passed (the GPU clock ramps up over ~0.1 s); 0 disables")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -354,9 +399,11 @@ def main() -> int:
             if evs is not None:
                 evs[4].record(stream)
 
+    t_warm = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    settle_steps = settle_until(step, t_warm, args.settle_s)
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -368,12 +415,15 @@ def main() -> int:
 
     t_fwd = [e[0].elapsed_time(e[1]) for e in events]
     res = {"fwd_ms": statistics.median(t_fwd)}
+    per_call = {"fa_fwd_fp8" if w.precision == "fp8" else "fa_fwd": t_fwd}
     if w.backward:
         t_prep = [e[1].elapsed_time(e[2]) for e in events]
         t_main = [e[2].elapsed_time(e[3]) for e in events]
         t_dq = [e[3].elapsed_time(e[4]) for e in events]
         res.update(bwd_prep_ms=statistics.median(t_prep), bwd_main_ms=statistics.median(t_main),
                    bwd_dq_ms=statistics.median(t_dq))
+        per_call.update(fa_bwd_prep=t_prep, fa_bwd_main=t_main, fa_bwd_dq=t_dq,
+                        fa_bwd=[a + b + c for a, b, c in zip(t_prep, t_main, t_dq)])
 
     quant_ms = None
     if fp8:
@@ -443,6 +493,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -463,6 +514,7 @@ def main() -> int:
         },
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         **extra,
+        "call_us": {name: percentiles_us(t) for name, t in per_call.items()},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

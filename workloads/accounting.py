@@ -74,6 +74,36 @@ def fwd_flops_window(B: int, H: int, N: int, d: int, causal: bool, window) -> fl
     return 4.0 * B * H * d * window_pairs(N, causal, window)
 
 
+def allowed_pairs(N: int, causal: bool, mask: Optional[np.ndarray] = None, window=None) -> int:
+    """Number of (query, key) pairs of one N x N head that the mask admits,
+    counted exactly (diagonal blocks of a causal block mask count their lower
+    triangle, ragged tail blocks their true size)."""
+    if window is not None:
+        return window_pairs(N, causal, window)
+    if mask is None:
+        return N * (N + 1) // 2 if causal else N * N
+    nb = mask.shape[0]
+    size = np.full(nb, MASK_BLOCK, dtype=np.int64)
+    size[-1] = N - MASK_BLOCK * (nb - 1)
+    full = np.outer(size, size)
+    if causal:
+        tri = size * (size + 1) // 2
+        full = np.tril(full, -1) + np.diag(tri)
+    return int((full * (mask != 0)).sum())
+
+
+def oracle_flops(heads: int, N: int, d: int, pairs: int, backward: bool) -> float:
+    """Floating-point work the fp64 oracle performs for `heads` heads with
+    `pairs` admitted pairs each: it materializes the dense N x N scores
+    (2 N^2 d) in the forward and again in the backward, the dense
+    dP = dO V^T (2 N^2 d), and skips zero probabilities in P V, dS K, P^T dO
+    and dS^T Q (2 d per admitted pair each).  Elementwise work is not counted."""
+    f = 2.0 * N * N * d + 2.0 * pairs * d
+    if backward:
+        f += 4.0 * N * N * d + 6.0 * pairs * d
+    return heads * f
+
+
 def fwd_bytes(B: int, H: int, N: int, d: int, dtype: str, nb_mask: int = 0) -> int:
     """Read q, k, v; write o (each B*H*N*d) and lse (fp32 per row); read the mask."""
     e = elem_bytes(dtype)
