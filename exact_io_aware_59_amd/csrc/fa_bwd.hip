@@ -468,24 +468,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     if constexpr (LIN)
         for (; st < nsteps; st++) step(std::true_type{}, st);
     wait_vmem();  // copies past the last tile fetch nothing, but must retire before exit
+    __syncthreads();  // every wave is done with the ring, which now stages the outputs
 
     // ---- epilogue: dK = -scale * acc, dV = acc, bf16 (rows >= N dropped) ----
-    const rsrc_t rdk = make_rsrc(dK + head_off, head_bytes);
-    const rsrc_t rdv = make_rsrc(dV + head_off, head_bytes);
-#pragma unroll
-    for (int dm = 0; dm < C::NDM; dm++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            bf16x4 a, b;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                a[e] = (bf16)(dkacc[dm][4 * g + e] * -scale);  // the accumulator holds -dK / scale
-                b[e] = (bf16)dvacc[dm][4 * g + e];
-            }
-            const uint32_t off = (uint32_t)(my_key * D + 32 * dm + 8 * g + 4 * h) * 2;
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, a), rdk, off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), rdv, off, 0, 0);
-        }
+    static_assert(kWaves * 2 * 32 * (D + 8) <= 3 * 2 * C::QTILE, "output staging must fit in the ring");
+    bf16* const stage = &ring[0][0][0] + wave * 2 * 32 * (D + 8);
+    const uint32_t rows_off = (uint32_t)(k0 + 32 * wave) * D * 2;
+    store_rows_staged<D>(dkacc, -scale, stage, make_rsrc(dK + head_off, head_bytes), rows_off, lane);
+    store_rows_staged<D>(dvacc, 1.0f, stage + 32 * (D + 8), make_rsrc(dV + head_off, head_bytes), rows_off, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -744,17 +734,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         }
         if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
 
-        // dQ = scale * acc -> bf16 (rows >= N dropped)
-#pragma unroll
-        for (int dm = 0; dm < C::NDM; dm++)
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                bf16x4 v4;
-#pragma unroll
-                for (int e = 0; e < 4; e++) v4[e] = (bf16)(acc[dm][4 * g + e] * scale);
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), rdq,
-                                                      (uint32_t)(my_q * D + 32 * dm + 8 * g + 4 * h) * 2, 0, 0);
-            }
+        // dQ = scale * acc -> bf16 (rows >= N dropped), staged in the V tiles, which
+        // every wave finished reading before the last step's barrier
+        static_assert(2 * 32 * (D + 8) <= C::VTILE, "output staging must fit in the V tiles");
+        bf16* const stage = (wave < 2 ? vbuf0 : vbuf1) + (wave & 1) * 32 * (D + 8);
+        store_rows_staged<D>(acc, scale, stage, rdq, (uint32_t)qw * D * 2, lane);
+        __syncthreads();  // the staging is read before the next block's tiles land there
     }
 }
 

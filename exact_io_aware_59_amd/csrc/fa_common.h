@@ -243,6 +243,42 @@ __device__ __forceinline__ uint32_t lds_addr_of(const T* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
 }
 
+// Store one wave's 32 x D block of a row-major bf16 tensor held in 32x32 MFMA
+// accumulator layout -- acc[dm][4g + e] is element (row l32, column
+// 32dm + 8g + 4h + e) -- scaled by `mul`.  Written straight from that layout
+// every lane stores 8 bytes into a different row, 64 partial cache lines per
+// instruction; instead the block goes through a wave-private LDS staging area
+// (32 rows of D + 8 elements: 16-byte aligned rows, at most two-way bank
+// conflicts on the 8-byte writes) and leaves with 16-byte stores, each
+// instruction covering 1 KB of consecutive rows.  `row0_off` is the byte
+// offset of the block's first row in the buffer; rows past the buffer's end
+// are dropped by its range check.  The caller must make sure no other wave
+// uses `stage` meanwhile.
+template <int D>
+__device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], float mul, bf16* stage, rsrc_t r,
+                                                  uint32_t row0_off, int lane) {
+    constexpr int SS = D + 8;
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int dm = 0; dm < D / 32; dm++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            bf16x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; e++) v4[e] = (bf16)(acc[dm][4 * g + e] * mul);
+            *reinterpret_cast<bf16x4*>(stage + l32 * SS + 32 * dm + 8 * g + 4 * h) = v4;
+        }
+    constexpr int CPR = D / 8;          // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;       // rows per store instruction
+    const int rr = lane / CPR, ch = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; i++) {
+        const int row = RPI * i + rr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * SS + 8 * ch);
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, row0_off + (uint32_t)(row * D + 8 * ch) * 2, 0, 0);
+    }
+}
+
 // Local window and ALiBi of one head ("FlashAttention 深度解析" section 五
 // names both as built-in variants beside the causal mask): key j is allowed
 // for query i iff i - wl <= j <= i + wr (a negative bound is unbounded), and

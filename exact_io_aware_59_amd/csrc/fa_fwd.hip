@@ -603,23 +603,21 @@ __global__ __launch_bounds__(64 * kWaves * KS, 2 / KS) void fwd_bf16_kernel(
         }
 
         // ---- epilogue: one division per row, bf16 output, lse (buffer stores drop rows >= N) ----
-        if (KS == 2 && group != 0) continue;
-        const float l = xhalf_sum(l_part);
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-        for (int dm = 0; dm < C::NDM; dm++)
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                bf16x4 v4;
-#pragma unroll
-                for (int e = 0; e < 4; e++) v4[e] = (bf16)(oacc[dm][4 * g + e] * inv);
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), ro,
-                                                      (uint32_t)(my_q * D + 32 * dm + 8 * g + 4 * h) * 2, 0, 0);
+        // O goes out through a staging area in the V buffers (every wave finished
+        // reading them before the last step's barrier); the barrier after it keeps
+        // the next block's first copies from landing there too early.
+        static_assert(2 * 32 * (D + 8) <= C::VTILE, "output staging must fit in the V buffers");
+        if (KS == 1 || group == 0) {
+            const float l = xhalf_sum(l_part);
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            bf16* const stage = (wave < 2 ? vbuf0s : vbuf1s) + (wave & 1) * 32 * (D + 8);
+            store_rows_staged<D>(oacc, inv, stage, ro, (uint32_t)qw * D * 2, lane);
+            if (h == 0) {
+                const float lse = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, (uint32_t)my_q * 4, 0, 0);
             }
-        if (h == 0) {
-            const float lse = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, (uint32_t)my_q * 4, 0, 0);
         }
+        if (bi + 1 < nblk) __syncthreads();
     }
 }
 
