@@ -33,7 +33,7 @@ __all__ = [
 ]
 
 MASK_BLOCK = 128
-ABI_VERSION = 5  # FA_VERSION of the fa.h these argument lists follow
+ABI_VERSION = 6  # FA_VERSION of the fa.h these argument lists follow
 NOALLOC_MAX_ROWS = 2097152  # FA_NOALLOC_MAX_ROWS
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None

@@ -14,6 +14,8 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMaxMaskN = 4194304;
 constexpr int kMaxMaskNBwd = 524288;  // the backward keeps its block-row list in LDS beside its tiles
+constexpr int kMaxHead = 128;         // head size limit of the backward and of the fp32 path
+constexpr int kMaxHeadFwd = 256;      // ... of the bf16 forward
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -37,11 +39,13 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-int check_sizes(int B, int H, int N, int d, float scale, const uint8_t* mask) {
+// Head sizes a path supports: a multiple of 16 up to `max_d`, or (max_d = 0)
+// exactly 64 or 128.
+int check_sizes(int B, int H, int N, int d, float scale, const uint8_t* mask, int max_d) {
     if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
     if (!prod_below(1LL << 31, {B, H, N, d})) return FA_ERR_INVALID_ARG;
-    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (max_d == 0 ? (d != 64 && d != 128) : (d % 16 != 0 || d > max_d)) return FA_ERR_UNSUPPORTED;
     if (mask && N > kMaxMaskN) return FA_ERR_UNSUPPORTED;
     // the bf16 kernels address one head with 32-bit byte offsets and may form
     // offsets up to a few hundred rows past N (reads there fall outside the
@@ -71,8 +75,10 @@ int fwd_common(const T* q, const T* k, const T* v, T* o, float* lse, int B, int 
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3))
         return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-    int st = check_sizes(B, H, N, d, scale, mask);
+    int st = check_sizes(B, H, N, d, scale, mask, bf16 ? kMaxHeadFwd : kMaxHead);
     if (st != FA_OK) return st;
+    // the 256-wide tiles leave room for a block-row list of at most 4096 entries
+    if (mask && d > kMaxHead && N > kMaxMaskNBwd) return FA_ERR_UNSUPPORTED;
     st = check_variant(var);
     if (st != FA_OK) return st;
     const size_t tb = (size_t)B * H * N * d * sizeof(T), lb = (size_t)B * H * N * sizeof(float);
@@ -119,7 +125,7 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
         if (p && !aligned16(p)) return FA_ERR_INVALID_ARG;
     if (lse && ((uintptr_t)lse & 3)) return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-    int st = check_sizes(B, H, N, d, scale, mask);
+    int st = check_sizes(B, H, N, d, scale, mask, kMaxHead);
     if (st != FA_OK) return st;
     st = check_variant(var);
     if (st != FA_OK) return st;
@@ -398,7 +404,7 @@ int fa_fp8_quantize(const void* x, uint8_t* codes, int8_t* exps, int B, int H, i
     if (!x || !codes || !exps) return FA_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(codes) || (signs && ((uintptr_t)signs & 3))) return FA_ERR_INVALID_ARG;
     if (k_side != 0 && k_side != 1) return FA_ERR_INVALID_ARG;
-    const int st = check_sizes(B, H, N, d, 1.0f, nullptr);
+    const int st = check_sizes(B, H, N, d, 1.0f, nullptr, 0);
     if (st != FA_OK) return st;
     const size_t xb = (size_t)B * H * N * d * 2, cb = (size_t)B * H * N * d;
     const size_t eb = (size_t)B * H * ((N + FA_FP8_BLOCK - 1) / FA_FP8_BLOCK);
@@ -420,7 +426,7 @@ int fa_fwd_fp8(const uint8_t* q, const int8_t* q_exps, const uint8_t* k, const i
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3))
         return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-    const int st = check_sizes(B, H, N, d, scale, nullptr);
+    const int st = check_sizes(B, H, N, d, scale, nullptr, 0);
     if (st != FA_OK) return st;
     const size_t cb = (size_t)B * H * N * d, ob = cb * 2, lb = (size_t)B * H * N * 4;
     const size_t eb = (size_t)B * H * ((N + FA_FP8_BLOCK - 1) / FA_FP8_BLOCK);

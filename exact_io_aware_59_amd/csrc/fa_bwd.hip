@@ -36,18 +36,19 @@ constexpr int kBrq = 64;   // queries per step
 // ---------------------------------------------------------------------------
 // 1. D = rowsum(dO * O); lse in log2 units.
 // ---------------------------------------------------------------------------
+// D (64 or 128) bounds the row length hd; chunks past hd contribute nothing.
 template <int D>
 __global__ __launch_bounds__(256) void rowdot_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
                                                      const float* __restrict__ LSE, float* __restrict__ Dv,
-                                                     float* __restrict__ lse2, long rows) {
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
+                                                     float* __restrict__ lse2, long rows, int hd) {
+    constexpr int CPR = D / 8;  // 16-byte chunks per row (at most)
     const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const long row = gid / CPR;
     const int ch = (int)(gid % CPR);
     float acc = 0.f;
-    if (row < rows) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * D + ch * 8);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * D + ch * 8);
+    if (row < rows && 8 * ch < hd) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * hd + ch * 8);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * hd + ch * 8);
         const bf16x8 x = __builtin_bit_cast(bf16x8, a), y = __builtin_bit_cast(bf16x8, b);
 #pragma unroll
         for (int i = 0; i < 8; i++) acc = __builtin_fmaf((float)x[i], (float)y[i], acc);
@@ -129,7 +130,7 @@ template <int D, bool CAUSAL, bool MASK, int VK>
 __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float c, float scale,
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int hd, float c, float scale,
     const uint8_t* __restrict__ mask, int nb, int nkb, int BH, int H, int wl, int wr,
     const float* __restrict__ slopes) {
     using C = BwdCfg<D>;
@@ -154,8 +155,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     const int bh = blockIdx.x % BH;
     const int k0 = kb * kBck;
     const int my_key = k0 + 32 * wave + l32;
-    const size_t head_off = (size_t)bh * N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const size_t head_off = (size_t)bh * N * hd;
+    const uint32_t head_bytes = (uint32_t)N * hd * 2;
     const int32x4_t sq = make_srd(Q + head_off, head_bytes);
     const int32x4_t sdo = make_srd(dO + head_off, head_bytes);
     // waves 0 and 2 copy lse2 rows, waves 1 and 3 the D rows (the second copy is
@@ -164,17 +165,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
                                       : make_srd(LSE2 + (size_t)bh * N, (uint32_t)N * 4);
     const uint32_t vec_lds0 = (wave & 1) ? lds_addr_of(&dvec[0][0]) : lds_addr_of(&lvec[0][0]);
 
-    // ---- this wave's K and V rows as MFMA B operands (k = head dim, n = key) ----
+    // ---- this wave's K and V rows as MFMA B operands (k = head dim, n = key);
+    // columns past hd are zero, so the padded columns of the query tiles never
+    // reach S or dP ----
     bf16x8 kf[C::NKK], vneg[C::NKK];
     {
         const rsrc_t rk = make_rsrc(K + head_off, head_bytes);
         const rsrc_t rv = make_rsrc(V + head_off, head_bytes);
-        const uint32_t off = (uint32_t)(my_key * D + 8 * h) * 2;
 #pragma unroll
         for (int kk = 0; kk < C::NKK; kk++) {
-            kf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, off + 32 * kk));
+            const int col = 16 * kk + 8 * h;
+            const uint32_t off = (uint32_t)(my_key * hd + (col < hd ? col : 0)) * 2;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            kf[kk] = __builtin_bit_cast(bf16x8, col < hd ? buf_load16(rk, off) : z);
             // -V (exact: a sign flip), so the R chain yields D - dP
-            vneg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off + 32 * kk) ^ 0x80008000u);
+            vneg[kk] = __builtin_bit_cast(bf16x8, col < hd ? (buf_load16(rv, off) ^ 0x80008000u) : z);
         }
     }
     // ---- the query tiles to visit: queries [q_lo, q_hi) can see this key block ----
@@ -215,19 +220,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     // Per-lane byte offsets of this wave's DMA segments relative to the tile's
     // first row.  Segments are dealt round-robin to the waves; lane i of a
     // segment fills LDS chunk position i, i.e. logical chunk i ^ sigma(row).
+    // A chunk past the row's hd elements re-reads the row's first chunk: those
+    // tile columns only meet the zero columns of K and V or produce dK / dV
+    // columns that are not stored.
     uint32_t seg_off[C::SEG_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < C::SEG_PER_WAVE; i++) {
         constexpr int CPR = D / 8;  // chunks per row
         const int seg = i * kWaves + wave;
         const int row = seg * (512 / D) + lane / CPR;
-        const int chunk = (lane % CPR) ^ swz_sigma<D>(row & 15);
-        seg_off[i] = (uint32_t)(row * D + 8 * chunk) * 2;
+        const int col = 8 * ((lane % CPR) ^ swz_sigma<D>(row & 15));
+        seg_off[i] = (uint32_t)(row * hd + (col < hd ? col : 0)) * 2;
     }
     // copy k (0 .. NDMA-1) of the tile starting at query q0 into ring slot `buf`
     auto dma_op = [&](auto kc, int q0, int buf) {
         constexpr int k = decltype(kc)::value;
-        const uint32_t rb = (uint32_t)q0 * D * 2;
+        const uint32_t rb = (uint32_t)q0 * hd * 2;
         if constexpr (k < 2 * C::SEG_PER_WAVE) {
             constexpr int i = k % C::SEG_PER_WAVE;
             constexpr int tensor = k / C::SEG_PER_WAVE;
@@ -473,9 +481,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     // ---- epilogue: dK = -scale * acc, dV = acc, bf16 (rows >= N dropped) ----
     static_assert(kWaves * 2 * 32 * (D + 8) <= 3 * 2 * C::QTILE, "output staging must fit in the ring");
     bf16* const stage = &ring[0][0][0] + wave * 2 * 32 * (D + 8);
-    const uint32_t rows_off = (uint32_t)(k0 + 32 * wave) * D * 2;
-    store_rows_staged<D>(dkacc, -scale, stage, make_rsrc(dK + head_off, head_bytes), rows_off, lane);
-    store_rows_staged<D>(dvacc, 1.0f, stage + 32 * (D + 8), make_rsrc(dV + head_off, head_bytes), rows_off, lane);
+    const uint32_t rows_off = (uint32_t)(k0 + 32 * wave) * hd * 2;
+    store_rows_staged<D>(dkacc, -scale, stage, make_rsrc(dK + head_off, head_bytes), rows_off, hd, lane);
+    store_rows_staged<D>(dvacc, 1.0f, stage + 32 * (D + 8), make_rsrc(dV + head_off, head_bytes), rows_off, hd,
+                         lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -503,22 +512,25 @@ constexpr int kDqBr = 128;  // queries per workgroup
 // padding keeps both free of bank conflicts, the chunk swizzle of swz<D> does.
 // Lane i of 1 KB segment s fills LDS chunk position i of its row and fetches
 // the logical chunk that position holds.
+// (Rows hold hd <= D elements; a chunk past hd re-reads the row's first one:
+// those tile columns only meet the zero columns of Q and dO or produce dQ
+// columns that are not stored.)
 template <int D, int SEGS>
-__device__ __forceinline__ void dq_load_tile_swz(rsrc_t r, bf16* tile, int kv0, int wave, int lane) {
+__device__ __forceinline__ void dq_load_tile_swz(rsrc_t r, bf16* tile, int kv0, int hd, int wave, int lane) {
     constexpr int CPR = D / 8;  // chunks per row
 #pragma unroll
     for (int i = 0; i < (SEGS + kWaves - 1) / kWaves; i++) {
         const int s = i * kWaves + wave;
         if (s < SEGS) {
             const int row = s * (512 / D) + lane / CPR;
-            const int chunk = (lane % CPR) ^ swz_sigma<D>(row & 15);
-            buf_load16_lds(r, tile + s * 512, ((uint32_t)(kv0 + row) * D + 8 * chunk) * 2);
+            const int col = 8 * ((lane % CPR) ^ swz_sigma<D>(row & 15));
+            buf_load16_lds(r, tile + s * 512, ((uint32_t)(kv0 + row) * hd + (col < hd ? col : 0)) * 2);
         }
     }
 }
 
 template <int D, int STRIDE, int SEGS>
-__device__ __forceinline__ void dq_load_tile(rsrc_t r, bf16* tile, int kv0, int wave, int lane) {
+__device__ __forceinline__ void dq_load_tile(rsrc_t r, bf16* tile, int kv0, int hd, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < (SEGS + kWaves - 1) / kWaves; i++) {
         const int s = i * kWaves + wave;
@@ -526,21 +538,24 @@ __device__ __forceinline__ void dq_load_tile(rsrc_t r, bf16* tile, int kv0, int 
             const int el = s * 512 + lane * 8;
             const int row = el / STRIDE;
             int col = el - row * STRIDE;
-            col = col < D ? col : 0;
-            buf_load16_lds(r, tile + s * 512, ((uint32_t)(kv0 + row) * D + col) * 2);
+            col = col < hd ? col : 0;
+            buf_load16_lds(r, tile + s * 512, ((uint32_t)(kv0 + row) * hd + col) * 2);
         }
     }
 }
 
 // VK as for the key-outer kernel; with VK = 1 the bias enters the exponent's
 // addend, slope2 (kv0 + 32 kb + 4h - q) per 32-key block plus slope2 r' per element.
-template <int D, bool CAUSAL, bool MASK, int VK>
+// PAD = false when the rows hold exactly D elements (the row length is then a
+// compile-time constant, as the runtime one costs registers here).
+template <int D, bool CAUSAL, bool MASK, int VK, bool PAD>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
-    bf16* __restrict__ dQ, int N, float c, float scale, const uint8_t* __restrict__ mask, int nb, int nqb,
-    int n_items, int H, int wl, int wr, const float* __restrict__ slopes) {
+    bf16* __restrict__ dQ, int N, int hd_arg, float c, float scale, const uint8_t* __restrict__ mask, int nb,
+    int nqb, int n_items, int H, int wl, int wr, const float* __restrict__ slopes) {
     using C = DqCfg<D>;
+    const int hd = PAD ? hd_arg : D;
     constexpr bool VAR = VK != 0, LIN = VK == 1, GEN = VK == 2;
     __shared__ __attribute__((aligned(1024))) bf16 kbuf0[C::KTILE];
     __shared__ __attribute__((aligned(1024))) bf16 kbuf1[C::KTILE];
@@ -589,8 +604,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         qblk[1] = -1;
         nblk = 1;
     }
-    const size_t head_off = (size_t)bh * N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const size_t head_off = (size_t)bh * N * hd;
+    const uint32_t head_bytes = (uint32_t)N * hd * 2;
     const rsrc_t rq = make_rsrc(Q + head_off, head_bytes);
     const rsrc_t rdo = make_rsrc(dO + head_off, head_bytes);
     const rsrc_t rk = make_rsrc(K + head_off, head_bytes);
@@ -636,14 +651,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         };
 
         // this lane's query: Q and dO fragments (B operands, k = head dim, n = query), lse2 and D
+        // (columns past hd are zero)
         bf16x8 qf[C::NKK], of[C::NKK];
-        {
-            const uint32_t off = (uint32_t)(my_q * D + 8 * h) * 2;
 #pragma unroll
-            for (int kk = 0; kk < C::NKK; kk++) {
-                qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, off + 32 * kk));
-                of[kk] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off + 32 * kk));
-            }
+        for (int kk = 0; kk < C::NKK; kk++) {
+            const int col = 16 * kk + 8 * h;
+            const uint32_t off = (uint32_t)(my_q * hd + (col < hd ? col : 0)) * 2;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qf[kk] = __builtin_bit_cast(bf16x8, col < hd ? buf_load16(rq, off) : z);
+            of[kk] = __builtin_bit_cast(bf16x8, col < hd ? buf_load16(rdo, off) : z);
         }
         const float l2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)my_q * 4, 0, 0));
         const float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)my_q * 4, 0, 0));
@@ -654,8 +670,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         for (int dm = 0; dm < C::NDM; dm++) acc[dm] = f32x16{};
 
         if (ntiles > 0) {
-            dq_load_tile_swz<D, C::KSEGS>(rk, kbuf0, kv0_of(0), wave, lane);
-            dq_load_tile<D, C::VS, C::VSEGS>(rv, vbuf0, kv0_of(0), wave, lane);
+            dq_load_tile_swz<D, C::KSEGS>(rk, kbuf0, kv0_of(0), hd, wave, lane);
+            dq_load_tile<D, C::VS, C::VSEGS>(rv, vbuf0, kv0_of(0), hd, wave, lane);
         }
         wait_vmem();
         __syncthreads();
@@ -666,8 +682,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             const bf16* vt = P ? vbuf1 : vbuf0;
             const int kv0 = kv0_of(it);
             if (it + 1 < ntiles) {
-                dq_load_tile_swz<D, C::KSEGS>(rk, P ? kbuf0 : kbuf1, kv0_of(it + 1), wave, lane);
-                dq_load_tile<D, C::VS, C::VSEGS>(rv, P ? vbuf0 : vbuf1, kv0_of(it + 1), wave, lane);
+                dq_load_tile_swz<D, C::KSEGS>(rk, P ? kbuf0 : kbuf1, kv0_of(it + 1), hd, wave, lane);
+                dq_load_tile<D, C::VS, C::VSEGS>(rv, P ? vbuf0 : vbuf1, kv0_of(it + 1), hd, wave, lane);
             }
             const bool need_mask = GEN || (LIN ? block_has_dead<CAUSAL>(qw, 32, kv0, C::BC, N, var)
                                                : (CAUSAL && kv0 + C::BC - 1 > qw) || (kv0 + C::BC > N));
@@ -738,26 +754,31 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         // every wave finished reading before the last step's barrier
         static_assert(2 * 32 * (D + 8) <= C::VTILE, "output staging must fit in the V tiles");
         bf16* const stage = (wave < 2 ? vbuf0 : vbuf1) + (wave & 1) * 32 * (D + 8);
-        store_rows_staged<D>(acc, scale, stage, rdq, (uint32_t)qw * D * 2, lane);
+        store_rows_staged<D>(acc, scale, stage, rdq, (uint32_t)qw * hd * 2, hd, lane);
         __syncthreads();  // the staging is read before the next block's tiles land there
     }
 }
 
-template <int D, bool CAUSAL, bool MASK, int VK>
-hipError_t launch_dq(const BwdArgs& a) {
+template <int D, bool CAUSAL, bool MASK, int VK, bool PAD>
+hipError_t launch_dq_pad(const BwdArgs& a) {
     const int nqb = (a.N + kDqBr - 1) / kDqBr;
     const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
     const int n_items = a.BH * per_head;
     const size_t dyn = MASK ? (size_t)a.nb * sizeof(uint16_t) : 0;
-    auto kern = bwd_dq_kernel<D, CAUSAL, MASK, VK>;
+    auto kern = bwd_dq_kernel<D, CAUSAL, MASK, VK, PAD>;
     if (dyn > 0) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads), dyn, a.stream, (const bf16*)a.q, (const bf16*)a.k,
-                       (const bf16*)a.v, (const bf16*)a.dO, a.ws_lse2, a.ws_D, (bf16*)a.dq, a.N,
+                       (const bf16*)a.v, (const bf16*)a.dO, a.ws_lse2, a.ws_D, (bf16*)a.dq, a.N, a.d,
                        a.scale * kLog2e, a.scale, a.mask, a.nb, nqb, n_items, a.H, a.wl, a.wr, a.slopes);
     return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool MASK, int VK>
+hipError_t launch_dq(const BwdArgs& a) {
+    return a.d == D ? launch_dq_pad<D, CAUSAL, MASK, VK, false>(a) : launch_dq_pad<D, CAUSAL, MASK, VK, true>(a);
 }
 
 template <int D, bool CAUSAL, bool MASK, int VK>
@@ -772,7 +793,7 @@ hipError_t launch_main(const BwdArgs& a) {
     }
     hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads), dyn, a.stream, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (const bf16*)a.dO, a.ws_lse2, a.ws_D, (bf16*)a.dk, (bf16*)a.dv,
-                       a.N, a.scale * kLog2e, a.scale, a.mask, a.nb, nkb, a.BH, a.H, a.wl, a.wr, a.slopes);
+                       a.N, a.d, a.scale * kLog2e, a.scale, a.mask, a.nb, nkb, a.BH, a.H, a.wl, a.wr, a.slopes);
     return hipGetLastError();
 }
 
@@ -781,7 +802,7 @@ hipError_t launch_prep(const BwdArgs& a) {
     const long rows = (long)a.BH * a.N;
     const long nthr = rows * (D / 8);
     hipLaunchKernelGGL(rowdot_kernel<D>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, a.stream,
-                       (const bf16*)a.o, (const bf16*)a.dO, a.lse, a.ws_D, a.ws_lse2, rows);
+                       (const bf16*)a.o, (const bf16*)a.dO, a.lse, a.ws_D, a.ws_lse2, rows, a.d);
     return hipGetLastError();
 }
 
@@ -811,22 +832,22 @@ int variant_kind(const BwdArgs& a, bool divides_by_c) {
 }  // namespace
 
 hipError_t launch_bwd_prep_bf16(const BwdArgs& a) {
-    return a.d == 128 ? launch_prep<128>(a) : launch_prep<64>(a);
+    return a.d > 64 ? launch_prep<128>(a) : launch_prep<64>(a);
 }
 
 hipError_t launch_bwd_main_bf16(const BwdArgs& a) {
     switch (variant_kind(a, true)) {
-        case 0: return a.d == 128 ? launch_main_all<128, 0>(a) : launch_main_all<64, 0>(a);
-        case 1: return a.d == 128 ? launch_main_all<128, 1>(a) : launch_main_all<64, 1>(a);
-        default: return a.d == 128 ? launch_main_all<128, 2>(a) : launch_main_all<64, 2>(a);
+        case 0: return a.d > 64 ? launch_main_all<128, 0>(a) : launch_main_all<64, 0>(a);
+        case 1: return a.d > 64 ? launch_main_all<128, 1>(a) : launch_main_all<64, 1>(a);
+        default: return a.d > 64 ? launch_main_all<128, 2>(a) : launch_main_all<64, 2>(a);
     }
 }
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
     switch (variant_kind(a, false)) {
-        case 0: return a.d == 128 ? launch_dq_all<128, 0>(a) : launch_dq_all<64, 0>(a);
-        case 1: return a.d == 128 ? launch_dq_all<128, 1>(a) : launch_dq_all<64, 1>(a);
-        default: return a.d == 128 ? launch_dq_all<128, 2>(a) : launch_dq_all<64, 2>(a);
+        case 0: return a.d > 64 ? launch_dq_all<128, 0>(a) : launch_dq_all<64, 0>(a);
+        case 1: return a.d > 64 ? launch_dq_all<128, 1>(a) : launch_dq_all<64, 1>(a);
+        default: return a.d > 64 ? launch_dq_all<128, 2>(a) : launch_dq_all<64, 2>(a);
     }
 }
 

@@ -250,13 +250,14 @@ __device__ __forceinline__ uint32_t lds_addr_of(const T* p) {
 // instruction; instead the block goes through a wave-private LDS staging area
 // (32 rows of D + 8 elements: 16-byte aligned rows, at most two-way bank
 // conflicts on the 8-byte writes) and leaves with 16-byte stores, each
-// instruction covering 1 KB of consecutive rows.  `row0_off` is the byte
-// offset of the block's first row in the buffer; rows past the buffer's end
-// are dropped by its range check.  The caller must make sure no other wave
-// uses `stage` meanwhile.
+// instruction covering up to 1 KB of consecutive rows.  The tensor's rows
+// hold `ld` <= D elements (a multiple of 8); columns from `ld` on are not
+// stored.  `row0_off` is the byte offset of the block's first row in the
+// buffer; rows past the buffer's end are dropped by its range check.  The
+// caller must make sure no other wave uses `stage` meanwhile.
 template <int D>
 __device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], float mul, bf16* stage, rsrc_t r,
-                                                  uint32_t row0_off, int lane) {
+                                                  uint32_t row0_off, int ld, int lane) {
     constexpr int SS = D + 8;
     const int h = lane >> 5, l32 = lane & 31;
 #pragma unroll
@@ -275,7 +276,7 @@ __device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], f
     for (int i = 0; i < 32 / RPI; i++) {
         const int row = RPI * i + rr;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * SS + 8 * ch);
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, row0_off + (uint32_t)(row * D + 8 * ch) * 2, 0, 0);
+        if (8 * ch < ld) __builtin_amdgcn_raw_buffer_store_b128(v, r, row0_off + (uint32_t)(row * ld + 8 * ch) * 2, 0, 0);
     }
 }
 

@@ -205,9 +205,34 @@ hipError_t bwd_f32(const BwdArgs& a) {
     return hipGetLastError();
 }
 
+// One instantiation per head size (a multiple of 16 up to 128): the per-row
+// register arrays need the size at compile time.
+template <template <int> class L, class Args>
+hipError_t by_head_dim(const Args& a) {
+    switch (a.d) {
+        case 16: return L<16>::run(a);
+        case 32: return L<32>::run(a);
+        case 48: return L<48>::run(a);
+        case 64: return L<64>::run(a);
+        case 80: return L<80>::run(a);
+        case 96: return L<96>::run(a);
+        case 112: return L<112>::run(a);
+        case 128: return L<128>::run(a);
+        default: return hipErrorInvalidValue;  // excluded by the argument checks
+    }
+}
+template <int D>
+struct FwdF32 {
+    static hipError_t run(const FwdArgs& a) { return fwd_f32<D>(a); }
+};
+template <int D>
+struct BwdF32 {
+    static hipError_t run(const BwdArgs& a) { return bwd_f32<D>(a); }
+};
+
 }  // namespace
 
-hipError_t launch_fwd_f32(const FwdArgs& a) { return a.d == 128 ? fwd_f32<128>(a) : fwd_f32<64>(a); }
-hipError_t launch_bwd_f32(const BwdArgs& a) { return a.d == 128 ? bwd_f32<128>(a) : bwd_f32<64>(a); }
+hipError_t launch_fwd_f32(const FwdArgs& a) { return by_head_dim<FwdF32>(a); }
+hipError_t launch_bwd_f32(const BwdArgs& a) { return by_head_dim<BwdF32>(a); }
 
 }  // namespace fa

@@ -42,11 +42,15 @@
  * Streams   `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *           enqueue work and return; results are ready once the stream is
  *           synchronized.  Kernel faults surface at the caller's next sync.
- * Limits    B, H, N >= 1; d in {64, 128} (the pages allow any multiple of 16 up
- *           to 256; other values return FA_ERR_UNSUPPORTED); B*H*N*d < 2^31;
- *           (N + 256) * d * 2 < 2^32 (else FA_ERR_UNSUPPORTED: the kernels
- *           address one head with 32-bit byte offsets); scale finite; with a
- *           blockmask, N <= 4194304 (forward) and N <= 524288 (backward).
+ * Limits    B, H, N >= 1; the head size d a multiple of 16 ("FlashAttention
+ *           原理概览" section 3.4) of at most 256 for the bf16 forward and at
+ *           most 128 for the backward and the fp32 entry points ("FlashAttention
+ *           深度解析" section 五 bounds it by 256; the key-outer backward's LDS
+ *           ring does not fit at 256); other values return FA_ERR_UNSUPPORTED;
+ *           B*H*N*d < 2^31; (N + 256) * d * 2 < 2^32 (else FA_ERR_UNSUPPORTED:
+ *           the kernels address one head with 32-bit byte offsets); scale
+ *           finite; with a blockmask, N <= 4194304 (forward, d <= 128),
+ *           N <= 524288 (forward with d > 128, and the backward).
  * Errors    arguments are validated before anything is enqueued; on any
  *           error nothing is enqueued and the outputs are untouched.
  *           FA_ERR_HIP reports a failed kernel launch (hipGetLastError).
@@ -65,14 +69,14 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, non-finite scale, aliasing, too large */
-    FA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. head dimension not 64 or 128) */
+    FA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. a head size that is not a multiple of 16) */
     FA_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or smaller than the *_workspace_size() */
     FA_ERR_HIP = 4,         /* the HIP runtime reported an error while enqueueing */
     FA_ERR_SCRATCH = 5      /* fa_bwd_noalloc: B*H*N exceeds FA_NOALLOC_MAX_ROWS */
 } fa_status;
 
 #define FA_MASK_BLOCK 128 /* block-mask granularity in rows and columns */
-#define FA_VERSION 5
+#define FA_VERSION 6
 
 /*
  * Local window and ALiBi, the two further built-in variants "FlashAttention
@@ -264,7 +268,7 @@ int fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, con
  * E4M3 (as 2^8 P, P <= 1) for P V; o bf16 [B][H][N][d] and lse float [B][H][N]
  * as fa_fwd.  causal 0 or 1; no block mask or window.  The result differs from
  * exact attention of the dequantized tensors by the rounding of P.
- * Limits as fa_fwd; codes 16-byte aligned.
+ * Limits as fa_fwd but d in {64, 128}; codes 16-byte aligned.
  */
 #define FA_FP8_BLOCK 64
 int fa_fp8_quantize(const void* x, uint8_t* codes, int8_t* exps, int B, int H, int N, int d, const float* signs,

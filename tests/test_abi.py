@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status(lib):
-    assert fa.fa_version() == fa.ABI_VERSION == 5
+    assert fa.fa_version() == fa.ABI_VERSION == 6
     for s in range(6):
         assert fa.fa_status_string(s)
     assert fa.fa_status_string(99) == "unknown status"
@@ -71,8 +71,10 @@ def test_fwd_validation(lib):
         assert _fwd(lib, scale=nan, f32=f32) == 1
         assert _fwd(lib, scale=float("inf"), f32=f32) == 1
         assert _fwd(lib, causal=2, f32=f32) == 1
-        assert _fwd(lib, d=96, f32=f32) == 2
-        assert _fwd(lib, d=256, f32=f32) == 2
+        assert _fwd(lib, d=72, f32=f32) == 2   # not a multiple of 16
+        assert _fwd(lib, d=272, f32=f32) == 2  # above 256
+        if f32:
+            assert _fwd(lib, d=144, f32=f32) == 2  # the fp32 path stops at 128
         assert _fwd(lib, B=1 << 20, H=1 << 10, N=4096, f32=f32) == 1  # more than 2^31 elements
         assert _fwd(lib, o=P1, f32=f32) == 1  # output aliases q
         assert _fwd(lib, lse=P1 + 3 * BIG + 100, f32=f32) == 1  # lse inside o
@@ -99,7 +101,8 @@ def test_bwd_validation(lib):
         assert _bwd(lib, dq=None, f32=f32) == 1
         assert _bwd(lib, dk=P1 + 6 * BIG, f32=f32) == 1  # dk aliases dq
         assert _bwd(lib, dv=P1, f32=f32) == 1  # dv aliases q
-        assert _bwd(lib, d=32, f32=f32) == 2
+        assert _bwd(lib, d=40, f32=f32) == 2   # not a multiple of 16
+        assert _bwd(lib, d=144, f32=f32) == 2  # the backward stops at 128
         assert _bwd(lib, scale=float("nan"), f32=f32) == 1
 
 
@@ -122,7 +125,7 @@ def test_stage_validation(lib):
     assert lib.fa_bwd_prep(None, P2, P3, 1, 1, 128, 64, ws, nbytes, None) == 1
     assert lib.fa_bwd_prep(P1, P1 + BIG, None, 1, 1, 128, 64, ws, nbytes, None) == 1
     assert lib.fa_bwd_prep(P1, P1 + BIG, P1 + 2 * BIG, 1, 1, 128, 64, ws, nbytes - 1, None) == 3
-    assert lib.fa_bwd_prep(P1, P1 + BIG, P1 + 2 * BIG, 1, 1, 128, 96, ws, nbytes, None) == 2
+    assert lib.fa_bwd_prep(P1, P1 + BIG, P1 + 2 * BIG, 1, 1, 128, 144, ws, nbytes, None) == 2
     assert lib.fa_bwd_dq(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, None, 1, 1, 128, 64, ctypes.c_float(0.1), 0,
                          None, ws, nbytes, None) == 1
     assert lib.fa_bwd_dq(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, 1, 1, 128, 64,
@@ -146,7 +149,7 @@ def test_variant_validation(lib):
         assert fn(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, 1, 1, 128, 64, s, 0, None, bad,
                   None) == 1
         # other errors are still reported with a valid variant
-        assert fn(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, 1, 1, 128, 96, s, 0, None, ok,
+        assert fn(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, 1, 1, 128, 72, s, 0, None, ok,
                   None) == 2
     for fn in (lib.fa_bwd_ex, lib.fa_bwd_f32_ex):
         assert fn(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG, P1 + 6 * BIG,

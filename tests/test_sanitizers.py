@@ -128,7 +128,10 @@ int main(void) {
            FA_ERR_INVALID_ARG);
     EXPECT(fa_fwd(P(1), P(2), P(3), P(4), (float*)P(5), 1, 1, 128, 64, NAN, 0, NULL, NULL), FA_ERR_INVALID_ARG);
     EXPECT(fa_fwd(P(1), P(1), P(3), P(1), (float*)P(5), 1, 1, 128, 64, 0.1f, 0, NULL, NULL), FA_ERR_INVALID_ARG);
-    EXPECT(fa_fwd(P(1), P(2), P(3), P(4), (float*)P(5), 1, 1, 128, 96, 0.1f, 0, NULL, NULL), FA_ERR_UNSUPPORTED);
+    EXPECT(fa_fwd(P(1), P(2), P(3), P(4), (float*)P(5), 1, 1, 128, 72, 0.1f, 0, NULL, NULL), FA_ERR_UNSUPPORTED);
+    EXPECT(fa_fwd(P(1), P(2), P(3), P(4), (float*)P(5), 1, 1, 128, 272, 0.1f, 0, NULL, NULL), FA_ERR_UNSUPPORTED);
+    EXPECT(fa_bwd(P(1), P(2), P(3), P(4), P(5), (float*)P(6), P(7), P(8), P(9), 1, 1, 128, 144, 0.1f, 0,
+                  NULL, P(10), ws, NULL), FA_ERR_UNSUPPORTED);
     EXPECT((int)fa_bwd_workspace_size(big, big, big, 128), 0);
     EXPECT(fa_bwd(P(1), P(2), P(3), P(4), P(5), (float*)P(6), P(7), P(8), P(9), 2, 16, 4096, 128, 0.088f, 1,
                   NULL, P(10), ws - 1, NULL), FA_ERR_WORKSPACE);

@@ -78,6 +78,12 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("bf16_window_alibi_fwdbwd_b2h16n4096d128", 2, 16, 4096, 128, "bf16", causal=True,
                  backward=True, window=(1023, -1), alibi=True,
                  description="bf16 causal sliding window of 1024 keys with ALiBi, forward + backward"),
+        Workload("bf16_causal_fwd_b1h8n8192d256", 1, 8, 8192, 256, "bf16", causal=True,
+                 description="bf16 causal forward at the largest head size the pages name (256), "
+                             "case-study sequence length"),
+        Workload("bf16_causal_fwdbwd_b2h16n4096d96", 2, 16, 4096, 96, "bf16", causal=True, backward=True,
+                 description="bf16 causal forward + backward at a head size that is a multiple of 16 "
+                             "but not of the tile width (rows padded to 128 in the tiles)"),
     ]
 }
 
