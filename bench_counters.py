@@ -14,11 +14,23 @@ Three summaries, each from the CSV files of one profiler run (or one pair):
             SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE.
   trace     per-kernel durations from a --kernel-trace run, beside the HIP
             event medians of the bench.py line that run printed.
+  dram      read / write requests the L2 sends to the memory controllers
+            (TCC_EA0_RDREQ_DRAM, TCC_EA0_WRREQ_DRAM) beside all L2 -> fabric
+            requests, from one run of `bench.py --copy-calib`, scaled to bytes
+            by the same counters of the 256 MiB copy.
+  mix       instruction mix per kernel (VALU, SALU, LDS, transcendental and
+            matrix instructions, LDS bank-conflict cycles, issue waits).
+
+The mfma summary also reports the matrix operations each kernel executes
+(SQ_INSTS_VALU_MFMA_MOPS_*, 512 FLOPs per unit) against the FLOPs the metric
+credits to it.
 
 Usage:
   python bench_counters.py traffic --workload NAME --fetch F.csv --write W.csv --command "..." [--command "..."]
   python bench_counters.py mfma --workload NAME --csv M.csv --command "..."
   python bench_counters.py trace --workload NAME --csv KT_kernel_trace.csv --bench-line B.json --command "..."
+  python bench_counters.py dram --workload NAME --csv D.csv --command "..."
+  python bench_counters.py mix --workload NAME --csv X.csv --command "..."
 """
 from __future__ import annotations
 
@@ -46,7 +58,8 @@ def kernel_sources(w) -> list:
         return ["fa_common.h", "fa_decode.hip"]
     if getattr(w, "precision", "bf16") == "fp8":
         return ["fa_common.h", "fa_fp8.hip"]
-    return ["fa_common.h", "fa_fwd.hip", "fa_bwd.hip"]
+    return ["fa_common.h", "fa_fwd.h", "fa_fwd.hip", "fa_fwd_64.hip", "fa_fwd_128.hip", "fa_fwd_256.hip",
+            "fa_bwd.hip"]
 
 # kernel-name substring -> entry point that launches it
 ENTRY = [("fwd_bf16_kernel", "fa_fwd"), ("rowdot_kernel", "fa_bwd_prep"),
@@ -164,10 +177,17 @@ def mfma(args) -> None:
             dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
     lines = [f"# Matrix-core busy fraction and clock: {workload_title(w)}", ""]
     lines += commands_block(args.command)
+    credited = metric_flops_per_launch(w)
+    mops_names = [c for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+                              "SQ_INSTS_VALU_MFMA_MOPS_F6F4") if any(c == n for _, n in m)]
     lines += ["GRBM_GUI_ACTIVE is summed over the 8 XCDs; busy per SIMD = SQ_VALU_MFMA_BUSY_CYCLES / "
-              "(1024 SIMDs x GRBM_GUI_ACTIVE / 8); clock = (GRBM_GUI_ACTIVE / 8) / dispatch duration.", "",
-              "| entry point | dispatches | GRBM_GUI_ACTIVE | SQ_VALU_MFMA_BUSY_CYCLES | MFMA busy per SIMD | clock GHz |",
-              "|---|---|---|---|---|---|"]
+              "(1024 SIMDs x GRBM_GUI_ACTIVE / 8); clock = (GRBM_GUI_ACTIVE / 8) / dispatch duration.  "
+              "Executed matrix FLOPs = " + " + ".join(mops_names or ["(no MOPS counter)"]) + " x 512 per "
+              "dispatch (the SQ counters read per dispatch: the forward's SQ_INSTS_MFMA equals its product "
+              "count computed from the tiling); credited = the FLOPs the metric gives that entry point.", "",
+              "| entry point | dispatches | GRBM_GUI_ACTIVE | SQ_VALU_MFMA_BUSY_CYCLES | MFMA busy per SIMD | clock GHz "
+              "| SQ_INSTS_MFMA | executed GFLOP | credited GFLOP | executed / credited |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
     rows = []
     for k in sorted({k for k, _ in m}):
         api = entry_of(k)
@@ -176,12 +196,107 @@ def mfma(args) -> None:
         g = statistics.mean(m[(k, "GRBM_GUI_ACTIVE")])
         b = statistics.mean(m[(k, "SQ_VALU_MFMA_BUSY_CYCLES")])
         d = statistics.mean(dur[k])
+        ni = statistics.mean(m[(k, "SQ_INSTS_MFMA")]) if (k, "SQ_INSTS_MFMA") in m else None
+        ex = sum(statistics.mean(m[(k, c)]) for c in mops_names if (k, c) in m) * 512 if mops_names else None
+        cr = credited.get(api)
         rows.append((ORDER.index(api), f"| {api} | {len(dur[k])} | {g:.4g} | {b:.4g} | {b / (1024 * g / 8):.3f} | "
-                                       f"{g / 8 / d / 1e9:.2f} |"))
+                                       f"{g / 8 / d / 1e9:.2f} | {'' if ni is None else f'{ni:.4g}'} | "
+                                       f"{'' if ex is None else f'{ex / 1e9:.1f}'} | "
+                                       f"{'' if cr is None else f'{cr / 1e9:.1f}'} | "
+                                       f"{'' if (ex is None or not cr) else f'{ex / cr:.3f}'} |"))
     lines += [r for _, r in sorted(rows)]
     lines += ["", "The published peaks assume 2.4 GHz; a dispatch too short for the estimate (the rowdot stage) "
               "reads a clock dominated by launch overhead."]
     out = os.path.join(ROOT, "profiles", f"{args.workload}_mfma_busy.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def metric_flops_per_launch(w) -> dict:
+    """FLOPs the metric credits to each entry point of one step: the forward's
+    two products, and of the backward's five, four to the key-outer kernel
+    (S, dP, dV, dK) and one to the dQ kernel."""
+    if getattr(w, "kind", "attn") == "decode":
+        return {"fa_decode_paged": A.decode_flops(w, W.decode_inputs(w, seed=0)["seqlens"])}
+    f = A.workload_flops(w, W.workload_mask(w, seed=0))
+    out = {"fa_fwd_fp8" if getattr(w, "precision", "bf16") == "fp8" else "fa_fwd": f["fwd"]}
+    if "bwd" in f:
+        out.update({"fa_bwd_prep": 0.0, "fa_bwd_main": f["bwd"] * 4 / 5, "fa_bwd_dq": f["bwd"] / 5})
+    return out
+
+
+def dram(args) -> None:
+    w = W.WORKLOADS[args.workload]
+    m = read_counters(args.csv)
+    copy = [k for (k, c) in m if is_copy(k) and c == "TCC_EA0_RDREQ_DRAM_sum"]
+    if not copy:
+        raise SystemExit("no calibration copy in the profile: run bench.py with --copy-calib")
+    rd_copy = max(m[(copy[0], "TCC_EA0_RDREQ_DRAM_sum")])
+    wr_copy = max(m[(copy[0], "TCC_EA0_WRREQ_DRAM_sum")])
+    rb_req, wb_req = COPY_KIB * 1024 / rd_copy, COPY_KIB * 1024 / wr_copy
+    if getattr(w, "kind", "attn") == "decode":
+        alg = {"fa_decode_paged": A.decode_bytes(w, W.decode_inputs(w, seed=0)["seqlens"])}
+    else:
+        alg = A.launch_bytes(w, W.workload_mask(w, seed=0))
+    lines = [f"# Memory-controller traffic per launch: {workload_title(w)}", ""]
+    lines += commands_block(args.command)
+    lines += [f"Calibration: the 256 MiB device copy reads TCC_EA0_RDREQ_DRAM_sum = {rd_copy:.4g} and "
+              f"TCC_EA0_WRREQ_DRAM_sum = {wr_copy:.4g} requests per dispatch, i.e. {rb_req:.1f} and "
+              f"{wb_req:.1f} bytes per request; the kernels' counts are scaled by the same factors.  "
+              "All-request columns (TCC_EA0_RDREQ_sum / TCC_EA0_WRREQ_sum) count every L2 -> fabric request.", "",
+              "| entry point | kernel | dispatches | RDREQ (all) | RDREQ_DRAM | WRREQ (all) | WRREQ_DRAM | "
+              "DRAM read MB | DRAM write MB | algorithmic MB | DRAM / algorithmic |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
+    rows, per = [], collections.defaultdict(lambda: [0.0, 0.0, 0.0, 0.0])
+    for (k, c), vals in m.items():
+        api = entry_of(k)
+        if api is None or c != "TCC_EA0_RDREQ_DRAM_sum" or api not in alg:
+            continue
+        ra = statistics.mean(m[(k, "TCC_EA0_RDREQ_sum")])
+        rd = statistics.mean(vals)
+        wa = statistics.mean(m[(k, "TCC_EA0_WRREQ_sum")])
+        wd = statistics.mean(m[(k, "TCC_EA0_WRREQ_DRAM_sum")])
+        rbytes, wbytes = rd * rb_req, wd * wb_req
+        rows.append((ORDER.index(api), f"| {api} | `{k[:60]}` | {len(vals)} | {ra:.4g} | {rd:.4g} | {wa:.4g} | "
+                                       f"{wd:.4g} | {rbytes / 1e6:.1f} | {wbytes / 1e6:.1f} | {alg[api] / 1e6:.1f} | "
+                                       f"{(rbytes + wbytes) / alg[api]:.2f} |"))
+    lines += [r for _, r in sorted(rows)]
+    out = os.path.join(ROOT, "profiles", f"{args.workload}_dram_traffic.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+MIX = ["SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA",
+       "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"]
+
+
+def mix(args) -> None:
+    w = W.WORKLOADS[args.workload]
+    m = read_counters(args.csv)
+    lines = [f"# Instruction mix per kernel: {workload_title(w)}", ""]
+    lines += commands_block(args.command)
+    lines += ["Per dispatch (means).  Per-MFMA columns divide by SQ_INSTS_MFMA; SQ_INSTS_VALU includes the "
+              "matrix and transcendental instructions, so 'other VALU' = VALU - MFMA - TRANS.  Bank conflicts are "
+              "LDS cycles lost to conflicts per LDS instruction; issue wait is SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES "
+              "(wave-cycles with an instruction ready but not issued).", "",
+              "| entry point | " + " | ".join(MIX) + " | other VALU / MFMA | TRANS / MFMA | SALU / MFMA | LDS / MFMA "
+              "| conflict cycles / LDS | issue wait |",
+              "|---|" + "---|" * (len(MIX) + 6)]
+    rows = []
+    for k in sorted({k for k, _ in m}):
+        api = entry_of(k)
+        if api is None or (k, "SQ_INSTS_MFMA") not in m:
+            continue
+        v = {c: statistics.mean(m[(k, c)]) if (k, c) in m else float("nan") for c in MIX}
+        nm = v["SQ_INSTS_MFMA"] or float("nan")
+        other = v["SQ_INSTS_VALU"] - v["SQ_INSTS_MFMA"] - v["SQ_INSTS_VALU_TRANS_F32"]
+        lds = v["SQ_INSTS_LDS"] or float("nan")
+        rows.append((ORDER.index(api), f"| {api} | " + " | ".join(f"{v[c]:.4g}" for c in MIX) +
+                     f" | {other / nm:.2f} | {v['SQ_INSTS_VALU_TRANS_F32'] / nm:.2f} | {v['SQ_INSTS_SALU'] / nm:.2f} "
+                     f"| {v['SQ_INSTS_LDS'] / nm:.2f} | {v['SQ_LDS_BANK_CONFLICT'] / lds:.2f} | "
+                     f"{v['SQ_WAIT_INST_ANY'] / v['SQ_WAVE_CYCLES']:.2f} |"))
+    lines += [r for _, r in sorted(rows)]
+    out = os.path.join(ROOT, "profiles", f"{args.workload}_instruction_mix.md")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -238,11 +353,15 @@ def main() -> int:
     k = sub.add_parser("trace")
     k.add_argument("--csv", required=True)
     k.add_argument("--bench-line", required=True)
-    for p in (t, m, k):
+    dr = sub.add_parser("dram")
+    dr.add_argument("--csv", required=True)
+    mx = sub.add_parser("mix")
+    mx.add_argument("--csv", required=True)
+    for p in (t, m, k, dr, mx):
         p.add_argument("--workload", default=bench.DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
         p.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
-    {"traffic": traffic, "mfma": mfma, "trace": trace}[args.what](args)
+    {"traffic": traffic, "mfma": mfma, "trace": trace, "dram": dram, "mix": mix}[args.what](args)
     return 0
 
 

@@ -29,7 +29,8 @@ __all__ = [
     "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex", "fa_bwd_dq_ex", "Variant",
     "forward", "backward", "workspace", "fa_decode_workspace_size", "fa_decode_paged", "decode_workspace",
     "decode_paged", "fa_fp8_quantize", "fa_fwd_fp8", "quantize_fp8", "forward_fp8", "FP8_BLOCK",
-    "MASK_BLOCK", "ABI_VERSION", "fa_bwd_noalloc", "NOALLOC_MAX_ROWS",
+    "MASK_BLOCK", "ABI_VERSION", "fa_bwd_noalloc", "NOALLOC_MAX_ROWS", "load_debug", "debug_library_path",
+    "fa_debug_flags", "DEBUG_ROW_SUM", "DEBUG_NON_FINITE",
 ]
 
 MASK_BLOCK = 128
@@ -55,12 +56,27 @@ def library_path() -> str:
     return os.path.join(_PKG, "libfa.so")
 
 
+def debug_library_path() -> str:
+    """The same library built with the kernels' debug self-check (FA_DEBUG_CHECK)."""
+    return os.path.join(_PKG, "libfa_debug.so")
+
+
 def load():
     """Load libfa.so (raises if it has not been built)."""
     global _lib
     if _lib is not None:
         return _lib
-    path = library_path()
+    _lib = _open(library_path())
+    return _lib
+
+
+def load_debug():
+    """A separate handle on libfa_debug.so, with the same argument lists as
+    load(); the module's wrappers keep using libfa.so."""
+    return _open(debug_library_path())
+
+
+def _open(path: str):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m exact_io_aware_59_amd.build`")
     lib = ctypes.CDLL(path)
@@ -97,10 +113,11 @@ def load():
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
+    lib.fa_debug_flags.argtypes = [i]
+    lib.fa_debug_flags.restype = i
     if lib.fa_version() != ABI_VERSION:
         raise ImportError(f"{path} reports ABI version {lib.fa_version()}, the binding expects {ABI_VERSION}: "
                           "rebuild it with `python -m exact_io_aware_59_amd.build`")
-    _lib = lib
     return lib
 
 
@@ -110,6 +127,15 @@ def fa_status_string(status: int) -> str:
 
 def fa_version() -> int:
     return int(load().fa_version())
+
+
+DEBUG_ROW_SUM = 1      # FA_DEBUG_ROW_SUM
+DEBUG_NON_FINITE = 2   # FA_DEBUG_NON_FINITE
+
+
+def fa_debug_flags(clear: bool = False, lib=None) -> int:
+    """Self-check flags of a FA_DEBUG_CHECK build (load_debug()); 0 for libfa.so."""
+    return int((lib or load()).fa_debug_flags(1 if clear else 0))
 
 
 def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:

@@ -459,4 +459,16 @@ const char* fa_status_string(int status) {
 
 int fa_version(void) { return FA_VERSION; }
 
+int fa_debug_flags(int clear) {
+#ifdef FA_DEBUG_CHECK
+    if (hipDeviceSynchronize() != hipSuccess) return -1;
+    const unsigned f = fa::debug_flags_fwd_w64(clear) | fa::debug_flags_fwd_w128(clear) |
+                       fa::debug_flags_fwd_w256(clear) | fa::debug_flags_bwd(clear);
+    return f == ~0u ? -1 : (int)f;
+#else
+    (void)clear;
+    return 0;
+#endif
+}
+
 }  // extern "C"

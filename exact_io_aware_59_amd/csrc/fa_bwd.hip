@@ -851,6 +851,8 @@ hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
     }
 }
 
+unsigned debug_flags_bwd(bool clear) { return read_debug_flags(clear); }
+
 hipError_t launch_bwd_bf16(const BwdArgs& a) {
     hipError_t e = launch_bwd_prep_bf16(a);
     if (e != hipSuccess) return e;

@@ -243,6 +243,46 @@ __device__ __forceinline__ uint32_t lds_addr_of(const T* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
 }
 
+// ---------------------------------------------------------------------------
+// Debug self-check, compiled in with -DFA_DEBUG_CHECK (libfa_debug.so): the
+// kernels record violated invariants as bits of a device flag word, one per
+// translation unit (device globals are not shared between code objects); the
+// C ABI's fa_debug_flags() collects them.  Without the macro the checks
+// compile to nothing.
+// ---------------------------------------------------------------------------
+constexpr unsigned kDbgRowSum = 1u;     // a row saw a finite score but its sum of weights is not > 0
+constexpr unsigned kDbgNonFinite = 2u;  // an output element (O, lse, dQ, dK, dV) is NaN or infinite
+// NaN or infinity, from the exponent bits (the forwards are compiled without
+// NaN semantics, under which isnan / isfinite may fold to constants)
+__device__ __forceinline__ bool nonfinite_bits(float x) { return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u; }
+#ifdef FA_DEBUG_CHECK
+namespace {
+__device__ unsigned int g_debug_flags;
+// Flags of this translation unit's kernels (synchronous; `clear` resets them).
+inline unsigned read_debug_flags(bool clear) {
+    unsigned v = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_flags), sizeof v, 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return ~0u;
+    if (clear) {
+        const unsigned z = 0;
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_debug_flags), &z, sizeof z, 0, hipMemcpyHostToDevice) != hipSuccess)
+            return ~0u;
+    }
+    return v;
+}
+}  // namespace
+// per lane: the atomic is a vector instruction on the flag's global address
+#define FA_CHECK(cond, bit)                                 \
+    do {                                                    \
+        if (!(cond)) atomicOr(&g_debug_flags, (unsigned)(bit)); \
+    } while (0)
+#else
+#define FA_CHECK(cond, bit) \
+    do {                    \
+    } while (0)
+inline unsigned read_debug_flags(bool) { return 0u; }
+#endif
+
 // Store one wave's 32 x D block of a row-major bf16 tensor held in 32x32 MFMA
 // accumulator layout -- acc[dm][4g + e] is element (row l32, column
 // 32dm + 8g + 4h + e) -- scaled by `mul`.  Written straight from that layout
@@ -266,7 +306,10 @@ __device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], f
         for (int g = 0; g < 4; g++) {
             bf16x4 v4;
 #pragma unroll
-            for (int e = 0; e < 4; e++) v4[e] = (bf16)(acc[dm][4 * g + e] * mul);
+            for (int e = 0; e < 4; e++) {
+                v4[e] = (bf16)(acc[dm][4 * g + e] * mul);
+                FA_CHECK(!nonfinite_bits(acc[dm][4 * g + e] * mul), kDbgNonFinite);
+            }
             *reinterpret_cast<bf16x4*>(stage + l32 * SS + 32 * dm + 8 * g + 4 * h) = v4;
         }
     constexpr int CPR = D / 8;          // 16-byte chunks per row

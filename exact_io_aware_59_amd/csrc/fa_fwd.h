@@ -629,10 +629,12 @@ __global__ __launch_bounds__(64 * kWaves * KS, D == 256 ? 1 : 2 / KS) void fwd_b
         if (KS == 1 || group == 0) {
             const float l = xhalf_sum(l_part);
             const float inv = l > 0.f ? 1.f / l : 0.f;
+            FA_CHECK(m_ref == -INFINITY || l > 0.f, kDbgRowSum);
             bf16* const stage = (wave < 2 ? vbuf0s : vbuf1s) + (wave & 1) * 32 * (D + 8);
             store_rows_staged<D>(oacc, inv, stage, ro, (uint32_t)qw * hd * 2, hd, lane);
             if (h == 0) {
                 const float lse = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
+                FA_CHECK(lse == -INFINITY || !nonfinite_bits(lse), kDbgNonFinite);
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, (uint32_t)my_q * 4, 0, 0);
             }
         }

@@ -5,5 +5,6 @@
 namespace fa {
 
 hipError_t launch_fwd_w64(const FwdArgs& a) { return launch_fwd_width<64>(a); }
+unsigned debug_flags_fwd_w64(bool clear) { return read_debug_flags(clear); }
 
 }  // namespace fa

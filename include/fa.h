@@ -283,6 +283,20 @@ const char* fa_status_string(int status);
 /* FA_VERSION of the loaded library. */
 int fa_version(void);
 
+/* Debug self-check ("FlashAttention 深度解析" section 二's invariants of the
+ * online softmax): a library built with FA_DEBUG_CHECK (libfa_debug.so, built
+ * beside libfa.so) has the bf16 forward and backward kernels record, as bits
+ * of a device flag word, a row that saw a finite score but whose sum of
+ * weights is not positive (FA_DEBUG_ROW_SUM) and any output element of O,
+ * lse, dQ, dK or dV that is NaN or infinite (FA_DEBUG_NON_FINITE; lse = -inf
+ * for a row without allowed keys is not flagged).  fa_debug_flags synchronizes
+ * the device, returns the bits accumulated since the last clear (clear != 0
+ * resets them) or -1 on a HIP error.  The plain library returns 0 and checks
+ * nothing.  Meant for debugging runs, not for production calls. */
+#define FA_DEBUG_ROW_SUM 1
+#define FA_DEBUG_NON_FINITE 2
+int fa_debug_flags(int clear);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,84 @@
+"""The FA_DEBUG_CHECK build (libfa_debug.so): the kernels' self-check of the
+online-softmax invariants ("FlashAttention 深度解析" section 二: a row that
+saw a finite score has a positive sum of weights) and of finite outputs.
+
+On valid inputs it records nothing and returns bit for bit the plain
+library's outputs (the check adds no arithmetic to the results); a NaN in V
+reaches O and is recorded.  Rows without an allowed key (O = 0, lse = -inf)
+are valid and not recorded.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests.gpu_cases import say, to_device
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import exact_io_aware_59_amd as fa  # noqa: E402
+
+
+def _p(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _run(lib, q, k, v, do, scale, causal, mask):
+    B, H, N, d = q.shape
+    o, lse = torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = fa.workspace(B, H, N, d, q.device)
+    torch.cuda.synchronize()
+    assert lib.fa_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, N, d, ctypes.c_float(scale), int(causal),
+                      _p(mask), None) == 0
+    assert lib.fa_bwd(_p(q), _p(k), _p(v), _p(o), _p(do), _p(lse), _p(dq), _p(dk), _p(dv), B, H, N, d,
+                      ctypes.c_float(scale), int(causal), _p(mask), _p(ws), ws.numel(), None) == 0
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("case", [(1, 2, 300, 128, True, False), (2, 1, 200, 80, False, False),
+                                  (1, 1, 384, 64, False, True)],
+                         ids=["d128-causal", "d80", "d64-empty-rows"])
+def test_debug_build_clean_and_identical(case):
+    B, H, N, d, causal, empty_rows = case
+    say(f"[debug check] B={B} H={H} N={N} d={d} causal={causal} empty_rows={empty_rows}")
+    dl = fa.load_debug()
+    fa.fa_debug_flags(True, dl)  # clear whatever an earlier test left
+    assert fa.fa_debug_flags(False, dl) == 0
+    x = W.make_inputs(B, H, N, d, "bf16", seed=71, with_do=True)
+    q, k, v, do = (to_device(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    mask = None
+    if empty_rows:
+        m = np.ones((3, 3), dtype=np.uint8)
+        m[1, :] = 0
+        mask = torch.from_numpy(m).to("cuda:0")
+    scale = float(np.float32(1 / math.sqrt(d)))
+    plain = _run(fa.load(), q, k, v, do, scale, causal, mask)
+    debug = _run(dl, q, k, v, do, scale, causal, mask)
+    assert fa.fa_debug_flags(True, dl) == 0
+    assert fa.fa_debug_flags(False, fa.load()) == 0  # the plain library checks nothing
+    for a, b in zip(plain, debug):
+        assert torch.equal(a, b)
+
+
+def test_debug_build_flags_nan():
+    say("[debug check] NaN in V")
+    dl = fa.load_debug()
+    fa.fa_debug_flags(True, dl)
+    B, H, N, d = 1, 1, 256, 128
+    x = W.make_inputs(B, H, N, d, "bf16", seed=72, with_do=True)
+    q, k, v, do = (to_device(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    v[0, 0, 5, 3] = float("nan")
+    _run(dl, q, k, v, do, float(np.float32(1 / math.sqrt(d))), True, None)
+    flags = fa.fa_debug_flags(True, dl)
+    assert flags & fa.DEBUG_NON_FINITE, flags
+    assert fa.fa_debug_flags(False, dl) == 0  # cleared
