@@ -18,11 +18,13 @@
 //     S^T = K Q^T with the K and Q block exponents as the instruction's scales
 //     (S comes out dequantized), then O^T += V^T P^T with P = 2^(c s - c m)
 //     times 2^8 rounded to E4M3 (its scale 2^-8 and the V block exponent are
-//     again the instruction's scales).  The reference max follows the row max
-//     exactly, so P <= 1 and 2^8 P stays inside E4M3's range with 17 binades
-//     below it.  V^T is read with ds_read_b64_tr_b8 in the key order of the
-//     S^T accumulator, so P never leaves registers.  The row sum uses the fp32
-//     probabilities.
+//     again the instruction's scales).  The reference max trails the row max
+//     by less than kF8LazyMax (log2 units): it moves only when the max grows
+//     by more than that, so P < 2^0.75 and 2^8 P stays below 431, inside
+//     E4M3's range (448), with 17 binades below it, while most rescales of O
+//     (every growth of the max, with an exact reference) are skipped.  V^T is
+//     read with ds_read_b64_tr_b8 in the key order of the S^T accumulator, so
+//     P never leaves registers.  The row sum uses the fp32 probabilities.
 #include <type_traits>
 
 #include "fa_common.h"
@@ -36,6 +38,9 @@ constexpr int kF8Waves = 4;
 constexpr int kF8Threads = 64 * kF8Waves;
 constexpr int kF8Br = 32 * kF8Waves;  // queries per workgroup
 constexpr int kPExp = 8;              // P is stored as 2^8 p
+// the reference max moves when the row max exceeds it by more than this (log2
+// units): 2^8 * 2^0.75 = 430.5 < 448, the largest finite E4M3 value
+constexpr float kF8LazyMax = 0.75f;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -301,13 +306,15 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
         // scores of a tile at kv0: keys past the diagonal or N to -inf, then the row max
         auto finish = [&](f32x16 (&sv)[2], int kv0) -> float {
             if (needs_mask(kv0)) {
+                // a lane's keys increase with the register index: one compare of the
+                // element's key offset against the lane's last live key
+                const int last = CAUSAL ? min(my_q, N - 1) : N - 1;
 #pragma unroll
-                for (int kb = 0; kb < 2; kb++)
+                for (int kb = 0; kb < 2; kb++) {
+                    const int lim = last - (kv0 + 32 * kb + 4 * h);
 #pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        sv[kb][r] = ((CAUSAL && key > my_q) || key >= N) ? -INFINITY : sv[kb][r];
-                    }
+                    for (int r = 0; r < 16; r++) sv[kb][r] = 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : sv[kb][r];
+                }
             }
             float mx = -INFINITY;
 #pragma unroll
@@ -360,9 +367,9 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
             const bool has_next = it + 1 < ntiles;
             const int kv1 = kv_of(it + 1), kv2 = kv_of(it + 2);
             const int sk1 = kscale(it + 1), sv0 = 127 + ve[it];
-            // ---- reference-max update for tile it ----
+            // ---- reference-max update for tile it (lazy, within E4M3's range) ----
             {
-                const bool bump = mx_cur > m_ref;
+                const bool bump = mx_cur != -INFINITY && (m_ref == -INFINITY || (mx_cur - m_ref) * c > kF8LazyMax);
                 if (__ballot(bump) != 0) {
                     const float alpha = bump ? (m_ref == -INFINITY ? 0.f : exp2f_hw((m_ref - mx_cur) * c)) : 1.f;
                     if (bump) m_ref = mx_cur;
@@ -457,20 +464,15 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
         }
         if (it < ntiles) step(std::integral_constant<int, 0>{}, it, sa, sb);
 
-        // epilogue: one division per row, bf16 output, lse (rows >= N dropped)
+        // epilogue: one division per row, bf16 output (staged through the tile
+        // buffers, one per wave, which every wave finished reading before the
+        // last step's barrier), lse (rows >= N dropped)
         const float l = xhalf_sum(l_part) * (1.f / (float)(1 << kPExp));
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const rsrc_t ro = make_rsrc(O + head_off, head_bytes * 2);
-#pragma unroll
-        for (int dm = 0; dm < C::NDM; dm++)
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                bf16x4 v4;
-#pragma unroll
-                for (int e = 0; e < 4; e++) v4[e] = (bf16)(oacc[dm][4 * g + e] * inv);
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), ro,
-                                                      (uint32_t)(my_q * D + 32 * dm + 8 * g + 4 * h) * 2, 0, 0);
-            }
+        static_assert(32 * (D + 8) * 2 <= C::TILE && kF8Waves == 4, "output staging: one tile buffer per wave");
+        uint8_t* const stage = wave == 0 ? kbuf0 : wave == 1 ? kbuf1 : wave == 2 ? vbuf0 : vbuf1;
+        store_rows_staged<D>(oacc, inv, reinterpret_cast<bf16*>(stage), ro, (uint32_t)qw * D * 2, D, lane);
         if (h == 0 && my_q < N) LSE[(size_t)bh * N + my_q] = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
         __syncthreads();  // the next query block reuses the tiles
     }
