@@ -10,9 +10,11 @@ Workload: B=2, H=16, N=4096, d=128, bf16, causal, iid N(0,1) inputs (seed 0).
 Prints one JSON line.  `value` is the whole step's throughput in TFLOP/s with
 the FLOP convention 4*B*H*N^2*d for the forward (halved for causal) and 2.5x
 that for the backward; inputs are resident in HBM before timing starts.
-HIP events on the launch stream time every kernel call of every timed step;
-`roofline` reports the backward's key-outer kernel (the dominant one: four of
-the five products) against the bf16 dense matrix-core peak.  `cpu_baseline` times the fp64 oracle on a
+The K timed steps enqueue nothing but the step's own launches; K further
+steps with HIP events recorded on the launch stream around every call give
+the per-call times, and `roofline` reports the backward's key-outer kernel
+(the dominant one: four of the five products) from them against the bf16
+dense matrix-core peak.  `cpu_baseline` times the fp64 oracle on a
 bounded sample of the same workload (a few heads).
 
 Timing: W untimed warm-up steps, then untimed settle steps until --settle-s
@@ -27,7 +29,9 @@ supported: the implementation runs on a single GPU), --workload NAME (another
 workload of workloads.WORKLOADS, forward only unless it has a backward; the
 paged decode workload reports GB/s against the HBM peak),
 --no-cpu-baseline, --copy-calib (run a plain device copy first, for the
-profiler's traffic calibration), --settle-s S.
+profiler's traffic calibration), --settle-s S, --launch stream|graph (the
+timed steps as separate launches on the stream, or replays of one captured
+HIP graph of the step, checked bit for bit against the eager step first).
 """
 from __future__ import annotations
 
@@ -301,6 +305,38 @@ def bench_decode(args, w) -> int:
     return 0
 
 
+def capture_step(torch, step, outputs):
+    """Capture one step (its kernel launches only: the step allocates nothing and
+    enqueues no memset) into a HIP graph and return its replay.  Replays must
+    reproduce the eager step bit for bit (every kernel is deterministic): three
+    replays, each after an eager step and a synchronization, are compared
+    before the graph is used; a mismatch stops the benchmark."""
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step(stream=side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in outputs:
+            t.fill_(float("nan"))
+        step()
+        torch.cuda.synchronize()
+        for t in outputs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outputs, ref):
+            if not torch.equal(t, r):
+                raise RuntimeError("graph replay differs from the eager step")
+    return g.replay
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,8 +344,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--launch", choices=("stream", "graph"), default="stream",
+                    help="timed steps launched call by call on the stream, or as one captured HIP graph "
+                         "(checked bit for bit against the eager step before timing)")
     ap.add_argument("--settle-s", type=float, default=0.3,
                     help="after the warm-up steps, run further untimed steps until this many seconds of "
                          "sustained load have passed (the GPU clock ramps up over ~0.1 s); 0 disables")
@@ -371,7 +410,7 @@ def main() -> int:
         k8, ke = fa.quantize_fp8(k, signs, True, stream)
         v8, ve = fa.quantize_fp8(v, None, False, stream)
 
-    def step(evs=None):
+    def step(evs=None, stream=stream):
         if evs is not None:
             evs[0].record(stream)
         if fp8:
@@ -405,13 +444,24 @@ def main() -> int:
     torch.cuda.synchronize()
     settle_steps = settle_until(step, t_warm, args.settle_s)
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    launch = step
+    if args.launch == "graph":
+        launch = capture_step(torch, step, [o, lse] + ([dq, dk, dv] if w.backward else []))
+
+    # the timed steps: nothing but the step's launches between the two synchronizations
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        launch()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-call times: the same number of steps again, each call bracketed by events on the launch stream
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     for s in range(args.steps):
         step(events[s])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
     t_fwd = [e[0].elapsed_time(e[1]) for e in events]
     res = {"fwd_ms": statistics.median(t_fwd)}
@@ -494,6 +544,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_steps": settle_steps,
+        "launch": args.launch,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -181,7 +181,10 @@ def mfma(args) -> None:
     mops_names = [c for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
                               "SQ_INSTS_VALU_MFMA_MOPS_F6F4") if any(c == n for _, n in m)]
     lines += ["GRBM_GUI_ACTIVE is summed over the 8 XCDs; busy per SIMD = SQ_VALU_MFMA_BUSY_CYCLES / "
-              "(1024 SIMDs x GRBM_GUI_ACTIVE / 8); clock = (GRBM_GUI_ACTIVE / 8) / dispatch duration.  "
+              "(1024 SIMDs x GRBM_GUI_ACTIVE / 8); clock = (GRBM_GUI_ACTIVE / 8) / dispatch duration; medians over "
+              "the dispatches.  GRBM_GUI_ACTIVE also counts ~20k cycles around each dispatch (the 12 µs rowdot "
+              "stage reads 45k), so busy reads a few per cent low and the clock a few per cent high on the long "
+              "kernels.  "
               "Executed matrix FLOPs = " + " + ".join(mops_names or ["(no MOPS counter)"]) + " x 512 per "
               "dispatch (the SQ counters read per dispatch: the forward's SQ_INSTS_MFMA equals its product "
               "count computed from the tiling); credited = the FLOPs the metric gives that entry point.", "",
@@ -193,11 +196,11 @@ def mfma(args) -> None:
         api = entry_of(k)
         if api is None:
             continue
-        g = statistics.mean(m[(k, "GRBM_GUI_ACTIVE")])
-        b = statistics.mean(m[(k, "SQ_VALU_MFMA_BUSY_CYCLES")])
-        d = statistics.mean(dur[k])
-        ni = statistics.mean(m[(k, "SQ_INSTS_MFMA")]) if (k, "SQ_INSTS_MFMA") in m else None
-        ex = sum(statistics.mean(m[(k, c)]) for c in mops_names if (k, c) in m) * 512 if mops_names else None
+        g = statistics.median(m[(k, "GRBM_GUI_ACTIVE")])
+        b = statistics.median(m[(k, "SQ_VALU_MFMA_BUSY_CYCLES")])
+        d = statistics.median(dur[k])
+        ni = statistics.median(m[(k, "SQ_INSTS_MFMA")]) if (k, "SQ_INSTS_MFMA") in m else None
+        ex = sum(statistics.median(m[(k, c)]) for c in mops_names if (k, c) in m) * 512 if mops_names else None
         cr = credited.get(api)
         rows.append((ORDER.index(api), f"| {api} | {len(dur[k])} | {g:.4g} | {b:.4g} | {b / (1024 * g / 8):.3f} | "
                                        f"{g / 8 / d / 1e9:.2f} | {'' if ni is None else f'{ni:.4g}'} | "
@@ -206,7 +209,7 @@ def mfma(args) -> None:
                                        f"{'' if (ex is None or not cr) else f'{ex / cr:.3f}'} |"))
     lines += [r for _, r in sorted(rows)]
     lines += ["", "The published peaks assume 2.4 GHz; a dispatch too short for the estimate (the rowdot stage) "
-              "reads a clock dominated by launch overhead."]
+              "reads a clock dominated by that overhead."]
     out = os.path.join(ROOT, "profiles", f"{args.workload}_mfma_busy.md")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -315,9 +318,15 @@ def trace(args) -> None:
     ev = {"fa_fwd": line.get("fwd_ms"), "fa_bwd_prep": line.get("bwd_prep_ms"),
           "fa_bwd_main": line.get("bwd_main_ms"), "fa_bwd_dq": line.get("bwd_dq_ms"),
           "fa_fwd_fp8": line.get("fwd_ms") if "fwd_pct_peak_fp8" in line else None,
-          "fa_decode_paged": line["call_us"]["median"] / 1e3 if "call_us" in line else None}
+          "fa_decode_paged": None}
     if "fwd_pct_peak_fp8" in line:
         ev["fa_fwd"] = None
+    calls = line.get("call_us", {})
+    if "median" in calls:  # one entry point per step (paged decode)
+        ev["fa_decode_paged"] = calls["median"] / 1e3
+    for api, c in calls.items():
+        if isinstance(c, dict) and "median" in c:
+            ev[api] = c["median"] / 1e3
     lines = [f"# Kernel trace: {workload_title(w) if getattr(w, 'kind', 'attn') == 'attn' else w.description}", ""]
     lines += commands_block(args.command)
     lines += [f"{warm} warm-up steps, then {steps} timed steps.  The last column is the median of the HIP-event "
