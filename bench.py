@@ -2,9 +2,10 @@
 """Benchmark: exact attention forward + recompute backward on one MI355X.
 
 One step is the whole hot path over one batch of synthetic inputs:
-fa_fwd (fused forward, writes O and lse) followed by the backward's three
-stages fa_bwd_prep, fa_bwd_main (key-outer: dK, dV) and fa_bwd_dq
-(query-outer: dQ) -- exactly what fa_bwd enqueues.
+fa_fwd (fused forward, writes O and lse) followed by the backward's two
+stages fa_bwd_dq_first (query-outer: dQ, plus the row terms D = rowsum(dO*O)
+and lse*log2(e) for the next stage) and fa_bwd_main (key-outer: dK, dV) --
+exactly what fa_bwd enqueues.
 Workload: B=2, H=16, N=4096, d=128, bf16, causal, iid N(0,1) inputs (seed 0).
 
 Prints one JSON line.  `value` is the whole step's throughput in TFLOP/s with
@@ -397,7 +398,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    n_ev = 5 if w.backward else 2
+    n_ev = 4 if w.backward else 2
 
     window, slopes_np = W.workload_variant(w)
     slopes = torch.from_numpy(slopes_np).to(dev) if slopes_np is not None else None
@@ -422,7 +423,11 @@ def main() -> int:
         if evs is not None:
             evs[1].record(stream)
         if w.backward:
-            fa.fa_bwd_prep(o, do, lse, ws, stream)
+            if w.variant:
+                fa.fa_bwd_dq_first_ex(q, k, v, o, do, lse, dq, w.scale, w.causal, mask, workspace=ws,
+                                      stream=stream, **var)
+            else:
+                fa.fa_bwd_dq_first(q, k, v, o, do, lse, dq, w.scale, w.causal, mask, ws, stream)
             if evs is not None:
                 evs[2].record(stream)
             if w.variant:
@@ -431,12 +436,6 @@ def main() -> int:
                 fa.fa_bwd_main(q, k, v, do, dk, dv, w.scale, w.causal, mask, ws, stream)
             if evs is not None:
                 evs[3].record(stream)
-            if w.variant:
-                fa.fa_bwd_dq_ex(q, k, v, do, dq, w.scale, w.causal, mask, workspace=ws, stream=stream, **var)
-            else:
-                fa.fa_bwd_dq(q, k, v, do, dq, w.scale, w.causal, mask, ws, stream)
-            if evs is not None:
-                evs[4].record(stream)
 
     t_warm = time.perf_counter()
     for _ in range(args.warmup):
@@ -467,13 +466,10 @@ def main() -> int:
     res = {"fwd_ms": statistics.median(t_fwd)}
     per_call = {"fa_fwd_fp8" if w.precision == "fp8" else "fa_fwd": t_fwd}
     if w.backward:
-        t_prep = [e[1].elapsed_time(e[2]) for e in events]
+        t_dq = [e[1].elapsed_time(e[2]) for e in events]
         t_main = [e[2].elapsed_time(e[3]) for e in events]
-        t_dq = [e[3].elapsed_time(e[4]) for e in events]
-        res.update(bwd_prep_ms=statistics.median(t_prep), bwd_main_ms=statistics.median(t_main),
-                   bwd_dq_ms=statistics.median(t_dq))
-        per_call.update(fa_bwd_prep=t_prep, fa_bwd_main=t_main, fa_bwd_dq=t_dq,
-                        fa_bwd=[a + b + c for a, b, c in zip(t_prep, t_main, t_dq)])
+        res.update(bwd_dq_ms=statistics.median(t_dq), bwd_main_ms=statistics.median(t_main))
+        per_call.update(fa_bwd_dq_first=t_dq, fa_bwd_main=t_main, fa_bwd=[a + b for a, b in zip(t_dq, t_main)])
 
     quant_ms = None
     if fp8:
@@ -499,15 +495,14 @@ def main() -> int:
         "fwd_pct_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
     }
     if w.backward:
-        bwd_ms = res["bwd_prep_ms"] + res["bwd_main_ms"] + res["bwd_dq_ms"]
+        bwd_ms = statistics.median(per_call["fa_bwd"])
         bwd_tflops = flops["bwd"] / (bwd_ms * 1e-3) / 1e12
         extra.update({
             "bwd_ms": round(bwd_ms, 4),
             "bwd_tflops": round(bwd_tflops, 1),
             "bwd_pct_peak": round(100 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
-            "bwd_prep_ms": round(res["bwd_prep_ms"], 4),
-            "bwd_main_ms": round(res["bwd_main_ms"], 4),
             "bwd_dq_ms": round(res["bwd_dq_ms"], 4),
+            "bwd_main_ms": round(res["bwd_main_ms"], 4),
         })
         # fa_bwd_main computes four of the backward's five products (S, dP, dV, dK): 4/5 of its FLOPs
         dom_name, dom_ms, dom_flops = "bwd_bf16_kernel (fa_bwd_main)", res["bwd_main_ms"], flops["bwd"] * 4 / 5

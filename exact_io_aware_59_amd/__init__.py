@@ -25,7 +25,8 @@ from typing import Optional, Tuple
 
 __all__ = [
     "FAError", "library_path", "load", "fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32",
-    "fa_bwd_workspace_size", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq", "fa_status_string", "fa_version",
+    "fa_bwd_workspace_size", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_first", "fa_status_string",
+    "fa_version", "fa_bwd_dq_first_ex",
     "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex", "fa_bwd_dq_ex", "Variant",
     "forward", "backward", "workspace", "fa_decode_workspace_size", "fa_decode_paged", "decode_workspace",
     "decode_paged", "fa_fp8_quantize", "fa_fwd_fp8", "quantize_fp8", "forward_fp8", "FP8_BLOCK",
@@ -34,7 +35,7 @@ __all__ = [
 ]
 
 MASK_BLOCK = 128
-ABI_VERSION = 6  # FA_VERSION of the fa.h these argument lists follow
+ABI_VERSION = 7  # FA_VERSION of the fa.h these argument lists follow
 NOALLOC_MAX_ROWS = 2097152  # FA_NOALLOC_MAX_ROWS
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -96,9 +97,12 @@ def _open(path: str):
     lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp]
     lib.fa_bwd_main_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp, sz, vp]
     lib.fa_bwd_dq_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp, sz, vp]
+    lib.fa_bwd_dq_first.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
+    lib.fa_bwd_dq_first_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vr, vp, sz, vp]
     for name in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_f32", "fa_bwd_prep", "fa_bwd_main", "fa_bwd_dq",
                  "fa_version", "fa_fwd_ex", "fa_fwd_f32_ex", "fa_bwd_ex", "fa_bwd_f32_ex", "fa_bwd_main_ex",
-                 "fa_bwd_dq_ex", "fa_decode_paged", "fa_fp8_quantize", "fa_fwd_fp8", "fa_bwd_noalloc"):
+                 "fa_bwd_dq_ex", "fa_bwd_dq_first", "fa_bwd_dq_first_ex", "fa_decode_paged", "fa_fp8_quantize",
+                 "fa_fwd_fp8", "fa_bwd_noalloc"):
         getattr(lib, name).restype = i
     lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_decode_workspace_size.restype = sz
@@ -329,6 +333,16 @@ def fa_bwd_dq(q, k, v, do, dq, scale: float, causal: bool = False, blockmask=Non
                             _stream(stream)), "fa_bwd_dq")
 
 
+def fa_bwd_dq_first(q, k, v, o, do, lse, dq, scale: float, causal: bool = False, blockmask=None, workspace=None,
+                    stream=None):
+    B, H, N, d = _dims(q)
+    _tensors("fa_bwd_dq_first", _attn_specs("bf16", q, B, H, N, d, k=k, v=v, o=o, do=do, lse=lse, dq=dq)
+             + [_mask_spec(blockmask, N), _ws_spec(workspace)])
+    _check(load().fa_bwd_dq_first(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), B, H, N, d,
+                                  float(scale), int(bool(causal)), _ptr(blockmask), _ptr(workspace),
+                                  _nbytes(workspace), _stream(stream)), "fa_bwd_dq_first")
+
+
 def fa_fwd_ex(q, k, v, o, lse, scale: float, causal: bool = False, blockmask=None, window=None,
               alibi_slopes=None, stream=None):
     B, H, N, d = _dims(q)
@@ -402,6 +416,17 @@ def fa_bwd_dq_ex(q, k, v, do, dq, scale: float, causal: bool = False, blockmask=
     _check(load().fa_bwd_dq_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), B, H, N, d, float(scale),
                                int(bool(causal)), _ptr(blockmask), _variant(window, alibi_slopes), _ptr(workspace),
                                _nbytes(workspace), _stream(stream)), "fa_bwd_dq_ex")
+
+
+def fa_bwd_dq_first_ex(q, k, v, o, do, lse, dq, scale: float, causal: bool = False, blockmask=None, window=None,
+                       alibi_slopes=None, workspace=None, stream=None):
+    B, H, N, d = _dims(q)
+    _tensors("fa_bwd_dq_first_ex", _attn_specs("bf16", q, B, H, N, d, k=k, v=v, o=o, do=do, lse=lse, dq=dq)
+             + [_mask_spec(blockmask, N), _ws_spec(workspace)] + _variant_specs(H, window, alibi_slopes))
+    _check(load().fa_bwd_dq_first_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), B, H, N,
+                                     d, float(scale), int(bool(causal)), _ptr(blockmask),
+                                     _variant(window, alibi_slopes), _ptr(workspace), _nbytes(workspace),
+                                     _stream(stream)), "fa_bwd_dq_first_ex")
 
 
 # ----------------------------------------------------------------------------

@@ -100,7 +100,7 @@ int fwd_common(const T* q, const T* k, const T* v, T* o, float* lse, int B, int 
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-enum Stage { kAll = 0, kPrep = 1, kMain = 2, kDq = 3 };
+enum Stage { kAll = 0, kPrep = 1, kMain = 2, kDq = 3, kDqFirst = 4 };
 
 // Validates and enqueues the backward (or one stage of it).  Tensors a stage
 // does not use may be NULL and are not checked.
@@ -109,10 +109,10 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
                int B, int H, int N, int d, float scale, int causal, const uint8_t* mask, const fa_variant* var,
                void* ws, size_t ws_bytes, void* stream, bool bf16, Stage stage) {
     const bool use_qkv = stage != kPrep;
-    const bool use_o = stage == kAll || stage == kPrep;
-    const bool use_lse = stage == kAll || stage == kPrep;
+    const bool use_o = stage == kAll || stage == kPrep || stage == kDqFirst;
+    const bool use_lse = stage == kAll || stage == kPrep || stage == kDqFirst;
     const bool use_do = true;
-    const bool use_dq = stage == kAll || stage == kDq;
+    const bool use_dq = stage == kAll || stage == kDq || stage == kDqFirst;
     const bool use_dkdv = stage == kAll || stage == kMain;
     if (use_qkv && (!q || !k || !v)) return FA_ERR_INVALID_ARG;
     if (use_lse && !lse) return FA_ERR_INVALID_ARG;
@@ -167,6 +167,7 @@ int bwd_common(const T* q, const T* k, const T* v, const T* o, const T* dO, cons
     else if (stage == kPrep) e = fa::launch_bwd_prep_bf16(a);
     else if (stage == kMain) e = fa::launch_bwd_main_bf16(a);
     else if (stage == kDq) e = fa::launch_bwd_dq_bf16(a);
+    else if (stage == kDqFirst) e = fa::launch_bwd_dq_first_bf16(a);
     else e = fa::launch_bwd_bf16(a);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -296,6 +297,21 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void*
               void* stream) {
     return fa_bwd_dq_ex(q, k, v, dO, dq, B, H, N, d, scale, causal, blockmask, nullptr, workspace, workspace_bytes,
                         stream);
+}
+
+int fa_bwd_dq_first_ex(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                       void* dq, int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+                       const fa_variant* variant, void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_common<uint16_t>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+                                (const uint16_t*)dO, lse, (uint16_t*)dq, nullptr, nullptr, B, H, N, d, scale,
+                                causal, blockmask, variant, workspace, workspace_bytes, stream, true, kDqFirst);
+}
+
+int fa_bwd_dq_first(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                    void* dq, int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    return fa_bwd_dq_first_ex(q, k, v, o, dO, lse, dq, B, H, N, d, scale, causal, blockmask, nullptr, workspace,
+                              workspace_bytes, stream);
 }
 
 int fa_bwd_f32_ex(const float* q, const float* k, const float* v, const float* o, const float* dO, const float* lse,

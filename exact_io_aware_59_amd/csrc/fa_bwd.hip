@@ -548,10 +548,19 @@ __device__ __forceinline__ void dq_load_tile(rsrc_t r, bf16* tile, int kv0, int 
 // addend, slope2 (kv0 + 32 kb + 4h - q) per 32-key block plus slope2 r' per element.
 // PAD = false when the rows hold exactly D elements (the row length is then a
 // compile-time constant, as the runtime one costs registers here).
+//
+// With O != null the kernel runs before the key-outer one and also does the
+// preprocessing: for each of its query rows it computes D = rowsum(dO o O)
+// and lse2 = lse log2(e) itself and stores them in the workspace rows that
+// the key-outer kernel reads.  D is summed in exactly the order of
+// rowdot_kernel (an FMA chain per 8-element chunk, then the chunks pairwise:
+// 0+1, 2+3, ..., then those sums pairwise, and so on), so both orders of the
+// stages give the same bits.
 template <int D, bool CAUSAL, bool MASK, int VK, bool PAD>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
+    const bf16* __restrict__ dO, const bf16* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ LSE2, float* __restrict__ Dv,
     bf16* __restrict__ dQ, int N, int hd_arg, float c, float scale, const uint8_t* __restrict__ mask, int nb,
     int nqb, int n_items, int H, int wl, int wr, const float* __restrict__ slopes) {
     using C = DqCfg<D>;
@@ -661,8 +670,44 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             qf[kk] = __builtin_bit_cast(bf16x8, col < hd ? buf_load16(rq, off) : z);
             of[kk] = __builtin_bit_cast(bf16x8, col < hd ? buf_load16(rdo, off) : z);
         }
-        const float l2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)my_q * 4, 0, 0));
-        const float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)my_q * 4, 0, 0));
+        float l2, dd;
+        if (O != nullptr) {
+            // ---- preprocessing of this block's rows (see above) ----
+            const rsrc_t ro = make_rsrc(O + head_off, head_bytes);
+            float cs[C::NKK];  // chunk 2kk + h of the row: FMA chain over its 8 elements
+#pragma unroll
+            for (int kk = 0; kk < C::NKK; kk++) {
+                const int col = 16 * kk + 8 * h;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                const bf16x8 ob = __builtin_bit_cast(
+                    bf16x8, col < hd ? buf_load16(ro, (uint32_t)(my_q * hd + col) * 2) : z);
+                float a = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; i++) a = __builtin_fmaf((float)ob[i], (float)of[kk][i], a);
+                cs[kk] = a;
+            }
+            // chunks 2kk and 2kk + 1 sit in lanes l and l ^ 32: their sum (the
+            // same bits in both lanes), then the pairwise tree over kk
+#pragma unroll
+            for (int kk = 0; kk < C::NKK; kk++) cs[kk] = xhalf_sum(cs[kk]);
+#pragma unroll
+            for (int w = 1; w < C::NKK; w <<= 1)
+#pragma unroll
+                for (int kk = 0; kk < C::NKK; kk += 2 * w) cs[kk] = cs[kk] + cs[kk + w];
+            dd = cs[0];
+            const float l = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4),
+                                                     (uint32_t)my_q * 4, 0, 0));
+            // a row without any allowed key (lse = -inf) gets +inf, so its P = 2^(c s - lse2) = 0
+            l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+            if (h == 0 && my_q < N) {
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dd), rd, (uint32_t)my_q * 4, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l2), rl, (uint32_t)my_q * 4, 0, 0);
+            }
+        } else {
+            l2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)my_q * 4, 0, 0));
+            dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)my_q * 4, 0, 0));
+        }
         const float ml2 = (my_q < N) ? -l2 : -INFINITY;  // rows past N get P = 0
 
         f32x16 acc[C::NDM];
@@ -760,7 +805,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 }
 
 template <int D, bool CAUSAL, bool MASK, int VK, bool PAD>
-hipError_t launch_dq_pad(const BwdArgs& a) {
+hipError_t launch_dq_pad(const BwdArgs& a, bool fused) {
     const int nqb = (a.N + kDqBr - 1) / kDqBr;
     const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
     const int n_items = a.BH * per_head;
@@ -771,14 +816,16 @@ hipError_t launch_dq_pad(const BwdArgs& a) {
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(n_items), dim3(kThreads), dyn, a.stream, (const bf16*)a.q, (const bf16*)a.k,
-                       (const bf16*)a.v, (const bf16*)a.dO, a.ws_lse2, a.ws_D, (bf16*)a.dq, a.N, a.d,
-                       a.scale * kLog2e, a.scale, a.mask, a.nb, nqb, n_items, a.H, a.wl, a.wr, a.slopes);
+                       (const bf16*)a.v, (const bf16*)a.dO, fused ? (const bf16*)a.o : nullptr, a.lse, a.ws_lse2,
+                       a.ws_D, (bf16*)a.dq, a.N, a.d, a.scale * kLog2e, a.scale, a.mask, a.nb, nqb, n_items, a.H,
+                       a.wl, a.wr, a.slopes);
     return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool MASK, int VK>
-hipError_t launch_dq(const BwdArgs& a) {
-    return a.d == D ? launch_dq_pad<D, CAUSAL, MASK, VK, false>(a) : launch_dq_pad<D, CAUSAL, MASK, VK, true>(a);
+hipError_t launch_dq(const BwdArgs& a, bool fused) {
+    return a.d == D ? launch_dq_pad<D, CAUSAL, MASK, VK, false>(a, fused)
+                    : launch_dq_pad<D, CAUSAL, MASK, VK, true>(a, fused);
 }
 
 template <int D, bool CAUSAL, bool MASK, int VK>
@@ -814,11 +861,13 @@ hipError_t launch_main_all(const BwdArgs& a) {
 }
 
 template <int D, int VK>
-hipError_t launch_dq_all(const BwdArgs& a) {
+hipError_t launch_dq_all(const BwdArgs& a, bool fused) {
     const bool m = a.mask != nullptr;
-    if (a.causal) return m ? launch_dq<D, true, true, VK>(a) : launch_dq<D, true, false, VK>(a);
-    return m ? launch_dq<D, false, true, VK>(a) : launch_dq<D, false, false, VK>(a);
+    if (a.causal) return m ? launch_dq<D, true, true, VK>(a, fused) : launch_dq<D, true, false, VK>(a, fused);
+    return m ? launch_dq<D, false, true, VK>(a, fused) : launch_dq<D, false, false, VK>(a, fused);
 }
+
+hipError_t launch_dq_any(const BwdArgs& a, bool fused);
 
 // The ALiBi bias is linear in the key over the live pairs only when they all
 // precede their query; the key-outer kernel also divides the slope by c.
@@ -843,22 +892,28 @@ hipError_t launch_bwd_main_bf16(const BwdArgs& a) {
     }
 }
 
-hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
+namespace {
+hipError_t launch_dq_any(const BwdArgs& a, bool fused) {
     switch (variant_kind(a, false)) {
-        case 0: return a.d > 64 ? launch_dq_all<128, 0>(a) : launch_dq_all<64, 0>(a);
-        case 1: return a.d > 64 ? launch_dq_all<128, 1>(a) : launch_dq_all<64, 1>(a);
-        default: return a.d > 64 ? launch_dq_all<128, 2>(a) : launch_dq_all<64, 2>(a);
+        case 0: return a.d > 64 ? launch_dq_all<128, 0>(a, fused) : launch_dq_all<64, 0>(a, fused);
+        case 1: return a.d > 64 ? launch_dq_all<128, 1>(a, fused) : launch_dq_all<64, 1>(a, fused);
+        default: return a.d > 64 ? launch_dq_all<128, 2>(a, fused) : launch_dq_all<64, 2>(a, fused);
     }
 }
+}  // namespace
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a) { return launch_dq_any(a, false); }
+
+hipError_t launch_bwd_dq_first_bf16(const BwdArgs& a) { return launch_dq_any(a, true); }
 
 unsigned debug_flags_bwd(bool clear) { return read_debug_flags(clear); }
 
+// dQ first (it also writes D and lse2), then dK and dV: the preprocessing
+// pass and its launch are saved; the results are those of prep, main, dQ.
 hipError_t launch_bwd_bf16(const BwdArgs& a) {
-    hipError_t e = launch_bwd_prep_bf16(a);
+    hipError_t e = launch_bwd_dq_first_bf16(a);
     if (e != hipSuccess) return e;
-    e = launch_bwd_main_bf16(a);
-    if (e != hipSuccess) return e;
-    return launch_bwd_dq_bf16(a);
+    return launch_bwd_main_bf16(a);
 }
 
 }  // namespace fa

@@ -101,10 +101,11 @@ struct F8FwdArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
-hipError_t launch_bwd_bf16(const BwdArgs& a);  // the three stages below, in order
+hipError_t launch_bwd_bf16(const BwdArgs& a);  // dq_first then main (= prep, main, dq)
 hipError_t launch_bwd_prep_bf16(const BwdArgs& a);
 hipError_t launch_bwd_main_bf16(const BwdArgs& a);
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a);
+hipError_t launch_bwd_dq_first_bf16(const BwdArgs& a);  // dQ plus the preprocessing (needs o, lse)
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_f32(const BwdArgs& a);
 hipError_t launch_decode_bf16(const DecArgs& a);

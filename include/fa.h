@@ -76,7 +76,7 @@ typedef enum {
 } fa_status;
 
 #define FA_MASK_BLOCK 128 /* block-mask granularity in rows and columns */
-#define FA_VERSION 6
+#define FA_VERSION 7
 
 /*
  * Local window and ALiBi, the two further built-in variants "FlashAttention
@@ -146,9 +146,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* stream);
 
 /*
- * The three stages fa_bwd enqueues, for callers that want to schedule or time
- * them separately.  fa_bwd(...) is exactly fa_bwd_prep, fa_bwd_main and
- * fa_bwd_dq on the same stream with the same workspace.
+ * The stages of the backward, for callers that want to schedule or time them
+ * separately.  Both orders below give exactly fa_bwd's results, bit for bit,
+ * on the same stream with the same workspace; fa_bwd itself enqueues the
+ * second, which saves the preprocessing pass.
+ *   order 1: fa_bwd_prep, fa_bwd_main, fa_bwd_dq;
+ *   order 2: fa_bwd_dq_first, fa_bwd_main.
  *   fa_bwd_prep: D_i = sum_c dO_ic O_ic and lse_i * log2(e) into the
  *                workspace.  Reads o, dO, lse.
  *   fa_bwd_main: key-outer pass: recomputes S, P, dP and dS per tile from q, k,
@@ -156,6 +159,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  *   fa_bwd_dq:   query-outer pass: recomputes S, P, dP and dS per tile; writes
  *                dq (bf16).  Independent of fa_bwd_main (both need only the
  *                workspace as left by fa_bwd_prep).
+ *   fa_bwd_dq_first: fa_bwd_dq that also does fa_bwd_prep's work for its own
+ *                rows (same summation order, same bits) and leaves D and
+ *                lse * log2(e) in the workspace for fa_bwd_main.  Reads q, k,
+ *                v, o, dO, lse; writes dq and the workspace.
  * Validation and error codes as for fa_bwd.
  */
 int fa_bwd_prep(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
@@ -166,6 +173,9 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, voi
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void* dq, int B, int H,
               int N, int d, float scale, int causal, const uint8_t* blockmask, void* workspace,
               size_t workspace_bytes, void* stream);
+int fa_bwd_dq_first(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                    const float* lse, void* dq, int B, int H, int N, int d, float scale, int causal,
+                    const uint8_t* blockmask, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * fa_bwd_ex without a workspace argument, for callers that cannot allocate
@@ -206,6 +216,10 @@ int fa_bwd_main_ex(const void* q, const void* k, const void* v, const void* dO, 
 int fa_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO, void* dq, int B, int H,
                  int N, int d, float scale, int causal, const uint8_t* blockmask,
                  const fa_variant* variant, void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_dq_first_ex(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                       const float* lse, void* dq, int B, int H, int N, int d, float scale, int causal,
+                       const uint8_t* blockmask, const fa_variant* variant, void* workspace,
+                       size_t workspace_bytes, void* stream);
 int fa_bwd_f32_ex(const float* q, const float* k, const float* v, const float* o, const float* dO,
                   const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
                   float scale, int causal, const uint8_t* blockmask, const fa_variant* variant,

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status(lib):
-    assert fa.fa_version() == fa.ABI_VERSION == 6
+    assert fa.fa_version() == fa.ABI_VERSION == 7
     for s in range(6):
         assert fa.fa_status_string(s)
     assert fa.fa_status_string(99) == "unknown status"
@@ -136,6 +136,18 @@ def test_stage_validation(lib):
                            1, 1, 128, 64, ctypes.c_float(0.1), 0, None, ws, nbytes, None) == 1
     assert lib.fa_bwd_main(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 4 * BIG,
                            1, 1, 128, 64, ctypes.c_float(0.1), 0, None, ws, nbytes, None) == 1  # dk aliases dv
+    s = ctypes.c_float(0.1)
+    # fa_bwd_dq_first(q, k, v, o, dO, lse, dq, ...): o and lse are required, dq must not alias an input
+    assert lib.fa_bwd_dq_first(P1, P1 + BIG, P1 + 2 * BIG, None, P1 + 4 * BIG, P1 + 5 * BIG, P1 + 6 * BIG,
+                               1, 1, 128, 64, s, 0, None, ws, nbytes, None) == 1
+    assert lib.fa_bwd_dq_first(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, None, P1 + 6 * BIG,
+                               1, 1, 128, 64, s, 0, None, ws, nbytes, None) == 1
+    assert lib.fa_bwd_dq_first(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG,
+                               P1 + 3 * BIG, 1, 1, 128, 64, s, 0, None, ws, nbytes, None) == 1  # dq aliases o
+    assert lib.fa_bwd_dq_first(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG,
+                               P1 + 6 * BIG, 1, 1, 128, 64, s, 0, None, ws, nbytes - 1, None) == 3
+    assert lib.fa_bwd_dq_first(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG,
+                               P1 + 6 * BIG, 1, 1, 128, 144, s, 0, None, ws, nbytes, None) == 2
 
 
 def test_variant_validation(lib):
@@ -158,6 +170,8 @@ def test_variant_validation(lib):
                               1, 1, 128, 64, s, 0, None, bad, ws, nbytes, None) == 1
     assert lib.fa_bwd_dq_ex(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, 1, 1, 128, 64, s, 0, None,
                             bad, ws, nbytes, None) == 1
+    assert lib.fa_bwd_dq_first_ex(P1, P1 + BIG, P1 + 2 * BIG, P1 + 3 * BIG, P1 + 4 * BIG, P1 + 5 * BIG,
+                                  P1 + 6 * BIG, 1, 1, 128, 64, s, 0, None, bad, ws, nbytes, None) == 1
 
 
 def _dec(lib, q=P1, kc=P1 + BIG, vc=P1 + 2 * BIG, bt=P1 + 3 * BIG, sl=P1 + 4 * BIG, o=P1 + 5 * BIG,

@@ -93,6 +93,10 @@ def test_bwd_rejects():
     raises("dv has dtype", fa.fa_bwd_main, x["q"], x["k"], x["v"], x["do"], x["dk"], t((B, H, N, d), torch.float32),
            0.1, False, None, ws)
     raises("dq has shape", fa.fa_bwd_dq, x["q"], x["k"], x["v"], x["do"], t((B, H, N, 32)), 0.1, False, None, ws)
+    raises("o has dtype", fa.fa_bwd_dq_first, x["q"], x["k"], x["v"], t((B, H, N, d), torch.float32), x["do"], lse(),
+           x["dq"], 0.1, False, None, ws)
+    raises("lse has shape", fa.fa_bwd_dq_first_ex, x["q"], x["k"], x["v"], x["o"], x["do"],
+           t((B, H, N - 1), torch.float32), x["dq"], 0.1, False, None, workspace=ws)
     y = attn(torch.float32)
     raises("dq has dtype torch.bfloat16", fa.fa_bwd_f32, *[y[n] for n in ("q", "k", "v", "o", "do")], lse(),
            x["dq"], y["dk"], y["dv"], 0.1, False, None, ws)

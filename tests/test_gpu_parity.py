@@ -211,22 +211,47 @@ def test_bwd_deterministic():
         assert torch.equal(a, b)
 
 
-def test_bwd_stages_equal_monolithic():
-    """fa_bwd_prep + fa_bwd_main + fa_bwd_dq reproduce fa_bwd exactly."""
-    say("[bwd stages] B=2 H=2 N=640 d=64 causal")
-    B, H, N, d = 2, 2, 640, 64
+@pytest.mark.parametrize("case", [(2, 2, 640, 64, True, None), (1, 2, 777, 128, True, None),
+                                  (1, 1, 300, 96, False, None), (1, 2, 520, 128, False, "rand")],
+                         ids=lambda c: "B{}H{}N{}d{}{}{}".format(*c[:4], "c" if c[4] else "", c[5] or ""))
+def test_bwd_stages_equal_monolithic(case):
+    """Both stage orders reproduce fa_bwd exactly: fa_bwd_prep + fa_bwd_main +
+    fa_bwd_dq, and fa_bwd_dq_first + fa_bwd_main; the workspace rows that
+    fa_bwd_dq_first leaves (D and lse*log2e, rows of every block including
+    empty and tail ones) are bit-identical to fa_bwd_prep's."""
+    B, H, N, d, causal, mk = case
+    say(f"[bwd stages] B={B} H={H} N={N} d={d} causal={causal} mask={mk}")
     x = W.make_inputs(B, H, N, d, "bf16", seed=44, with_do=True)
     q, k, v, do = (to_device(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    nb = (N + 127) // 128
+    m = None
+    if mk == "rand":
+        mm = np.random.default_rng(45).random((nb, nb)) < 0.5
+        mm[1, :] = False  # a query block with no key
+        m = _dev_mask(mm.astype(np.uint8))
     s = 0.125
-    o, lse = fa.forward(q, k, v, s, True)
-    dq, dk, dv = fa.backward(q, k, v, o, do, lse, s, True)
+    o, lse = fa.forward(q, k, v, s, causal, m)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, s, causal, m)
     ws = fa.workspace(B, H, N, d, q.device)
     dq2, dk2, dv2 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     fa.fa_bwd_prep(o, do, lse, ws)
-    fa.fa_bwd_main(q, k, v, do, dk2, dv2, s, True, None, ws)
-    fa.fa_bwd_dq(q, k, v, do, dq2, s, True, None, ws)
+    ws_prep = ws.clone()
+    fa.fa_bwd_main(q, k, v, do, dk2, dv2, s, causal, m, ws)
+    fa.fa_bwd_dq(q, k, v, do, dq2, s, causal, m, ws)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    ws.fill_(7)
+    dq3, dk3, dv3 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa.fa_bwd_dq_first(q, k, v, o, do, lse, dq3, s, causal, m, ws)
+    torch.cuda.synchronize()
+    # the workspace holds D, then lse*log2e, each 256-byte aligned
+    nbytes = B * H * N * 4
+    off = (nbytes + 255) // 256 * 256
+    for lo in (0, off):
+        assert torch.equal(ws[lo:lo + nbytes], ws_prep[lo:lo + nbytes])
+    fa.fa_bwd_main(q, k, v, do, dk3, dv3, s, causal, m, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq3) and torch.equal(dk, dk3) and torch.equal(dv, dv3)
 
 
 def test_empty_rows_exact():

@@ -194,7 +194,8 @@ def test_variant_f32(case):
 
 
 def test_variant_stages_equal_monolithic():
-    """fa_bwd_prep + fa_bwd_main_ex + fa_bwd_dq_ex == fa_bwd_ex, bit for bit."""
+    """fa_bwd_prep + fa_bwd_main_ex + fa_bwd_dq_ex == fa_bwd_dq_first_ex + fa_bwd_main_ex == fa_bwd_ex,
+    bit for bit."""
     B, H, N, d = 1, 2, 300, 128
     scale = float(np.float32(1 / math.sqrt(d)))
     x = W.make_inputs(B, H, N, d, "bf16", seed=61, with_do=True)
@@ -209,6 +210,14 @@ def test_variant_stages_equal_monolithic():
     fa.fa_bwd_dq_ex(q, k, v, do, dq2, scale, True, None, workspace=ws, **kw)
     torch.cuda.synchronize()
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a, b)
+    # the other order: dQ first (with the preprocessing), then dK and dV
+    dq3, dk3, dv3 = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws.fill_(7)
+    fa.fa_bwd_dq_first_ex(q, k, v, o, do, lse, dq3, scale, True, None, workspace=ws, **kw)
+    fa.fa_bwd_main_ex(q, k, v, do, dk3, dv3, scale, True, None, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq3), (dk, dk3), (dv, dv3)):
         assert torch.equal(a, b)
 
 

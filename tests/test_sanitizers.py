@@ -67,6 +67,7 @@ hipError_t launch_bwd_bf16(const BwdArgs&) { return rec(); }
 hipError_t launch_bwd_prep_bf16(const BwdArgs&) { return rec(); }
 hipError_t launch_bwd_main_bf16(const BwdArgs&) { return rec(); }
 hipError_t launch_bwd_dq_bf16(const BwdArgs&) { return rec(); }
+hipError_t launch_bwd_dq_first_bf16(const BwdArgs&) { return rec(); }
 hipError_t launch_fwd_f32(const FwdArgs&) { return rec(); }
 hipError_t launch_bwd_f32(const BwdArgs&) { return rec(); }
 hipError_t launch_decode_bf16(const DecArgs&) { return rec(); }
@@ -101,6 +102,10 @@ int main(void) {
     EXPECT(fa_bwd_main(P(1), P(2), P(3), P(5), P(8), P(9), 2, 16, 4096, 128, 0.088f, 1, NULL, P(10), ws, NULL),
            FA_OK);
     EXPECT(fa_bwd_dq(P(1), P(2), P(3), P(5), P(7), 2, 16, 4096, 128, 0.088f, 1, NULL, P(10), ws, NULL), FA_OK);
+    EXPECT(fa_bwd_dq_first(P(1), P(2), P(3), P(4), P(5), (float*)P(6), P(7), 2, 16, 4096, 128, 0.088f, 1, NULL,
+                           P(10), ws, NULL), FA_OK);
+    EXPECT(fa_bwd_dq_first(P(1), P(2), P(3), NULL, P(5), (float*)P(6), P(7), 2, 16, 4096, 128, 0.088f, 1, NULL,
+                           P(10), ws, NULL), FA_ERR_INVALID_ARG);
     fa_variant var = {100, -1, (const float*)P(11)};
     EXPECT(fa_fwd_ex(P(1), P(2), P(3), P(4), (float*)P(5), 2, 16, 4096, 128, 0.088f, 1, NULL, &var, NULL), FA_OK);
     size_t dws = fa_decode_workspace_size(16, 32, 8, 1, 128, 256, 32);

@@ -119,10 +119,10 @@ def bwd_bytes(B: int, H: int, N: int, d: int, dtype: str, nb_mask: int = 0) -> i
 def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     """Extra traffic of this implementation's backward beyond the floor: two
     fp32 row vectors (D = rowsum(dO*O) and lse in log2 units), each written once
-    by the preprocessing kernel and read by the key-outer and dQ kernels.  dQ
-    is accumulated in registers by the query-outer kernel, so there is no O(N d)
-    fp32 accumulator and no atomic traffic."""
-    return 2 * F32_BYTES * B * H * N * 3
+    by the dQ kernel, which runs first, and read once by the key-outer kernel.
+    dQ is accumulated in registers by the query-outer kernel, so there is no
+    O(N d) fp32 accumulator and no atomic traffic."""
+    return 2 * F32_BYTES * B * H * N * 2
 
 
 def naive_score_bytes(B: int, H: int, N: int, dtype_bytes: int) -> int:
@@ -166,8 +166,10 @@ def launch_bytes(w: Workload, mask: Optional[np.ndarray] = None) -> dict:
 
     fa_fwd reads q, k, v and writes o and lse; fa_bwd_prep reads o, do and lse
     and writes D = rowsum(dO*O) and the scaled lse; fa_bwd_main reads q, k, v,
-    do, lse and D and writes dk and dv; fa_bwd_dq reads the same and writes dq.
-    The block mask, when there is one, is read by every launch that uses it.
+    do, lse and D and writes dk and dv; fa_bwd_dq reads the same and writes dq;
+    fa_bwd_dq_first reads q, k, v, o, do and lse and writes dq, D and the
+    scaled lse.  The block mask, when there is one, is read by every launch
+    that uses it.
     """
     e = elem_bytes(w.dtype)
     t = w.B * w.H * w.N * w.d * e
@@ -183,7 +185,8 @@ def launch_bytes(w: Workload, mask: Optional[np.ndarray] = None) -> dict:
     if w.backward:
         out.update({"fa_bwd_prep": 2 * t + 3 * r,
                     "fa_bwd_main": 6 * t + 2 * r + m,
-                    "fa_bwd_dq": 5 * t + 2 * r + m})
+                    "fa_bwd_dq": 5 * t + 2 * r + m,
+                    "fa_bwd_dq_first": 6 * t + 3 * r + m})
     return out
 
 
