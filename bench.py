@@ -230,19 +230,25 @@ def bench_decode(args, w) -> int:
     def step():
         fa.fa_decode_paged(q, kc, vc, bt, sl, o, lse, w.scale, w.causal, ws, stream)
 
+    # (events created before the warm-up: creating them leaves the GPU idle long enough to cool its clock)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t_warm = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     settle_steps = settle_until(step, t_warm, args.settle_s)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # timed steps: nothing but the launches between the synchronizations; then as many again with events
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     for a, b in ev:
         a.record(stream)
         step()
         b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     times = sorted(a.elapsed_time(b) for a, b in ev)
     med = statistics.median(times)
     lens = x["seqlens"]
@@ -437,15 +443,16 @@ def main() -> int:
             if evs is not None:
                 evs[3].record(stream)
 
-    t_warm = time.perf_counter()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    settle_steps = settle_until(step, t_warm, args.settle_s)
-
     launch = step
     if args.launch == "graph":
         launch = capture_step(torch, step, [o, lse] + ([dq, dk, dv] if w.backward else []))
+    # (created up front: creating them takes tens of ms, an idle gap long enough for the clock to drop)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    t_warm = time.perf_counter()
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    settle_steps = settle_until(launch, t_warm, args.settle_s)
 
     # the timed steps: nothing but the step's launches between the two synchronizations
     torch.cuda.synchronize()
@@ -455,9 +462,8 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-call times: the same number of steps again, each call bracketed by events on the launch stream
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # per-call times: the same number of steps again, right after, each call bracketed by events on the
+    # launch stream
     for s in range(args.steps):
         step(events[s])
     torch.cuda.synchronize()

@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
             const uint32_t k_src = (uint32_t)kv2 * D, v_src = (uint32_t)kv1 * D;
             i32x8 opnd[C::NSLOT];
             i32x8 pb;
-            float ls[4] = {0.f, 0.f, 0.f, 0.f};
+            float ls[4];  // partial row sums, each started by its first term
             float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             float pw[4];
             auto read_operand = [&](auto jc) {
@@ -427,10 +427,13 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
                         float p = exp2f_hw(__builtin_fmaf(sc[idx / 16][idx % 16], c, -mc8));
                         pin(p);
                         pw[idx % 4] = p;
-                        ls[idx % 4] += p;
+                        if constexpr (idx < 4) ls[idx] = p;
+                        else ls[idx % 4] += p;
                         pin(ls[idx % 4]);
                         if constexpr (idx % 4 == 3) {
-                            int word = __builtin_amdgcn_cvt_pk_fp8_f32(pw[0], pw[1], 0, false);
+                            // both halves of the word are written, so the first conversion's
+                            // "old" operand may be any register: pw[0]'s own saves a move
+                            int word = __builtin_amdgcn_cvt_pk_fp8_f32(pw[0], pw[1], __float_as_int(pw[0]), false);
                             word = __builtin_amdgcn_cvt_pk_fp8_f32(pw[2], pw[3], word, true);
                             pb[idx / 4] = word;
                         }
