@@ -171,7 +171,9 @@ struct PadK {  // tiles read with ds_read_b128 (16 rows x 16 B)
 };
 template <int D>
 struct PadV {  // tiles read with ds_read_tr16_b64 (4 rows x 64 B per half-wave)
-    static constexpr int STRIDE = D + 32;  // 320 B (d=128) or 192 B (d=64)
+    // 320 B (d=128), 192 B (d=64), 576 B (d=256): 64 or 192 mod 256; 96-wide
+    // rows are 192 B already
+    static constexpr int STRIDE = D == 96 ? D : D + 32;
 };
 
 // Transposing A-operand read from a padded row-major tile (see
@@ -312,14 +314,19 @@ __device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], f
             }
             *reinterpret_cast<bf16x4*>(stage + l32 * SS + 32 * dm + 8 * g + 4 * h) = v4;
         }
-    constexpr int CPR = D / 8;          // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;       // rows per store instruction
-    const int rr = lane / CPR, ch = lane % CPR;
+    // chunk 64 i + lane of the block, row-major: 16-byte chunk `ch` of row
+    // `row` (when CPR divides 64 every lane stores; otherwise the last
+    // instruction's spare lanes do nothing)
+    constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    constexpr int NCH = (32 * CPR + 63) / 64;   // store instructions
 #pragma unroll
-    for (int i = 0; i < 32 / RPI; i++) {
-        const int row = RPI * i + rr;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * SS + 8 * ch);
-        if (8 * ch < ld) __builtin_amdgcn_raw_buffer_store_b128(v, r, row0_off + (uint32_t)(row * ld + 8 * ch) * 2, 0, 0);
+    for (int i = 0; i < NCH; i++) {
+        const int g = 64 * i + lane, row = g / CPR, ch = g % CPR;
+        if (row < 32) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * SS + 8 * ch);
+            if (8 * ch < ld)
+                __builtin_amdgcn_raw_buffer_store_b128(v, r, row0_off + (uint32_t)(row * ld + 8 * ch) * 2, 0, 0);
+        }
     }
 }
 

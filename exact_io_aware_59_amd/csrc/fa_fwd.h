@@ -231,7 +231,7 @@ __device__ __forceinline__ void tile_pv(const bf16* vl, const bf16x8 (&pb)[FwdCf
 // the online-softmax rescale ("FlashAttention 深度解析" section 二) and writes
 // the block.
 //
-// D is the tile width: 64, 128 or 256.  The tensors' rows hold hd <= D
+// D is the tile width: 64, 96, 128 or 256.  The tensors' rows hold hd <= D
 // elements (a multiple of 16); Q columns from hd on are zero in registers, so
 // the padded columns of the K and V tiles never reach a score.  PAD = false
 // when hd == D: the row length is then the compile-time D (a runtime length
@@ -622,15 +622,19 @@ __global__ __launch_bounds__(64 * kWaves * KS, D == 256 ? 1 : 2 / KS) void fwd_b
         }
 
         // ---- epilogue: one division per row, bf16 output, lse (buffer stores drop rows >= N) ----
-        // O goes out through a staging area in the V buffers (every wave finished
-        // reading them before the last step's barrier); the barrier after it keeps
+        // O goes out through a staging area in the tile buffers (every wave finished
+        // reading them before the last step's barrier): two waves per V buffer, or
+        // with 96-wide tiles one wave per K or V buffer; the barrier after it keeps
         // the next block's first copies from landing there too early.
-        static_assert(2 * 32 * (D + 8) <= C::VTILE, "output staging must fit in the V buffers");
+        constexpr bool kTwoPerV = 2 * 32 * (D + 8) <= C::VTILE;
+        static_assert(kTwoPerV || (KS == 1 && 32 * (D + 8) <= C::VTILE && 32 * (D + 8) <= C::KTILE),
+                      "output staging must fit in the tile buffers");
         if (KS == 1 || group == 0) {
             const float l = xhalf_sum(l_part);
             const float inv = l > 0.f ? 1.f / l : 0.f;
             FA_CHECK(m_ref == -INFINITY || l > 0.f, kDbgRowSum);
-            bf16* const stage = (wave < 2 ? vbuf0s : vbuf1s) + (wave & 1) * 32 * (D + 8);
+            bf16* const stage = kTwoPerV ? (wave < 2 ? vbuf0s : vbuf1s) + (wave & 1) * 32 * (D + 8)
+                                         : (wave == 0 ? kbuf0s : wave == 1 ? kbuf1s : wave == 2 ? vbuf0s : vbuf1s);
             store_rows_staged<D>(oacc, inv, stage, ro, (uint32_t)qw * hd * 2, hd, lane);
             if (h == 0) {
                 const float lse = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
@@ -680,7 +684,7 @@ hipError_t launch(const FwdArgs& a) {
     const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
     const int n_items = a.BH * per_head;
     const bool pad = a.d != D;
-    if constexpr (D == 256) {  // two tile groups would not fit in LDS
+    if constexpr (D == 256 || D == 96) {  // two tile groups: LDS (256) or the O exchange (96) would not fit
         return pad ? launch_ks<D, CAUSAL, MASK, VK, 1, true>(a, nqb, n_items)
                    : launch_ks<D, CAUSAL, MASK, VK, 1, false>(a, nqb, n_items);
     } else {

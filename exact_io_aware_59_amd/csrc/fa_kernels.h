@@ -115,6 +115,7 @@ hipError_t launch_fwd_fp8(const F8FwdArgs& a);
 // Debug self-check flags of the bf16 kernels' translation units (always 0
 // unless built with FA_DEBUG_CHECK); synchronous, `clear` resets them.
 unsigned debug_flags_fwd_w64(bool clear);
+unsigned debug_flags_fwd_w96(bool clear);
 unsigned debug_flags_fwd_w128(bool clear);
 unsigned debug_flags_fwd_w256(bool clear);
 unsigned debug_flags_bwd(bool clear);
