@@ -258,6 +258,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(
 
     // ---- epilogue: result (db, r) is dim 16 db + 4 gq + r of query l16 ----
     const float l = xquad_sum(l_part);
+    if (row_ok) FA_CHECK(m_ref == -INFINITY || l > 0.f, kDbgRowSum);
     if (n_parts == 1) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         if (row_ok) {
@@ -266,10 +267,15 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(
             for (int db = 0; db < C::NDB; db++) {
                 bf16x4 v4;
 #pragma unroll
-                for (int e = 0; e < 4; e++) v4[e] = (bf16)(oacc[db][e] * inv);
+                for (int e = 0; e < 4; e++) {
+                    v4[e] = (bf16)(oacc[db][e] * inv);
+                    FA_CHECK(!nonfinite_bits(oacc[db][e] * inv), kDbgNonFinite);
+                }
                 *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * gq) = v4;
             }
-            if (gq == 0) LSE[row_id] = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
+            const float lse = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
+            FA_CHECK(lse == -INFINITY || !nonfinite_bits(lse), kDbgNonFinite);
+            if (gq == 0) LSE[row_id] = lse;
         }
     } else if (row_ok) {
         float* wo = ws_o + (row_id * n_parts + part) * D;
@@ -335,10 +341,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
             for (int e = 0; e < PER; e++) acc[e] += wu * src[(size_t)p * D + e];
         }
     }
+    FA_CHECK(M == -INFINITY || lsum > 0.f, kDbgRowSum);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
-    for (int e = 0; e < PER; e++) O[(size_t)row * D + lane * PER + e] = (bf16)(acc[e] * inv);
-    if (lane == 0) LSE[row] = lsum > 0.f ? (M + log2f_hw(lsum)) * kLn2 : -INFINITY;
+    for (int e = 0; e < PER; e++) {
+        O[(size_t)row * D + lane * PER + e] = (bf16)(acc[e] * inv);
+        FA_CHECK(!nonfinite_bits(acc[e] * inv), kDbgNonFinite);
+    }
+    const float lse = lsum > 0.f ? (M + log2f_hw(lsum)) * kLn2 : -INFINITY;
+    FA_CHECK(lse == -INFINITY || !nonfinite_bits(lse), kDbgNonFinite);
+    if (lane == 0) LSE[row] = lse;
 }
 
 template <int D, bool CAUSAL>
@@ -365,5 +377,7 @@ hipError_t launch_decode_bf16(const DecArgs& a) {
     if (a.d == 128) return a.causal ? launch_decode_d<128, true>(a) : launch_decode_d<128, false>(a);
     return a.causal ? launch_decode_d<64, true>(a) : launch_decode_d<64, false>(a);
 }
+
+unsigned debug_flags_decode(bool clear) { return read_debug_flags(clear); }
 
 }  // namespace fa

@@ -66,10 +66,16 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
         m = m_new;
     }
     if (!row_ok) return;
+    FA_CHECK(m == -INFINITY || l > 0.f, kDbgRowSum);
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int e = 0; e < D; e++) O[head + (size_t)i * D + e] = o[e] * inv;
-    LSE[(size_t)bh * N + i] = l > 0.f ? (m + log2f_hw(l)) * kLn2 : -INFINITY;
+    for (int e = 0; e < D; e++) {
+        O[head + (size_t)i * D + e] = o[e] * inv;
+        FA_CHECK(!nonfinite_bits(o[e] * inv), kDbgNonFinite);
+    }
+    const float lse = l > 0.f ? (m + log2f_hw(l)) * kLn2 : -INFINITY;
+    FA_CHECK(lse == -INFINITY || !nonfinite_bits(lse), kDbgNonFinite);
+    LSE[(size_t)bh * N + i] = lse;
 }
 
 // D_i = sum_c dO_ic O_ic
@@ -121,7 +127,10 @@ __global__ __launch_bounds__(64) void dq_f32_kernel(const float* __restrict__ Q,
         for (int e = 0; e < D; e++) acc[e] = __builtin_fmaf(ds, kj[e], acc[e]);
     }
 #pragma unroll
-    for (int e = 0; e < D; e++) dQ[head + (size_t)i * D + e] = acc[e] * scale;
+    for (int e = 0; e < D; e++) {
+        dQ[head + (size_t)i * D + e] = acc[e] * scale;
+        FA_CHECK(!nonfinite_bits(acc[e] * scale), kDbgNonFinite);
+    }
 }
 
 // dV_j = sum_i P_ij dO_i and dK_j = scale * sum_i dS_ij q_i, one thread per key row
@@ -173,6 +182,7 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(const float* __restrict__ 
     for (int e = 0; e < D; e++) {
         dK[head + (size_t)j * D + e] = gk[e] * scale;
         dV[head + (size_t)j * D + e] = gv[e];
+        FA_CHECK(!nonfinite_bits(gk[e] * scale) && !nonfinite_bits(gv[e]), kDbgNonFinite);
     }
 }
 
@@ -234,5 +244,7 @@ struct BwdF32 {
 
 hipError_t launch_fwd_f32(const FwdArgs& a) { return by_head_dim<FwdF32>(a); }
 hipError_t launch_bwd_f32(const BwdArgs& a) { return by_head_dim<BwdF32>(a); }
+
+unsigned debug_flags_f32(bool clear) { return read_debug_flags(clear); }
 
 }  // namespace fa

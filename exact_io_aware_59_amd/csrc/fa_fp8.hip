@@ -471,12 +471,15 @@ __global__ __launch_bounds__(kF8Threads, 2) void fwd_fp8_kernel(
         // buffers, one per wave, which every wave finished reading before the
         // last step's barrier), lse (rows >= N dropped)
         const float l = xhalf_sum(l_part) * (1.f / (float)(1 << kPExp));
+        FA_CHECK(m_ref == -INFINITY || l > 0.f, kDbgRowSum);
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const rsrc_t ro = make_rsrc(O + head_off, head_bytes * 2);
         static_assert(32 * (D + 8) * 2 <= C::TILE && kF8Waves == 4, "output staging: one tile buffer per wave");
         uint8_t* const stage = wave == 0 ? kbuf0 : wave == 1 ? kbuf1 : wave == 2 ? vbuf0 : vbuf1;
         store_rows_staged<D>(oacc, inv, reinterpret_cast<bf16*>(stage), ro, (uint32_t)qw * D * 2, D, lane);
-        if (h == 0 && my_q < N) LSE[(size_t)bh * N + my_q] = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
+        const float lse = l > 0.f ? (m_ref * c + log2f_hw(l)) * kLn2 : -INFINITY;
+        FA_CHECK(lse == -INFINITY || !nonfinite_bits(lse), kDbgNonFinite);
+        if (h == 0 && my_q < N) LSE[(size_t)bh * N + my_q] = lse;
         __syncthreads();  // the next query block reuses the tiles
     }
 }
@@ -508,5 +511,7 @@ hipError_t launch_fwd_fp8(const F8FwdArgs& a) {
     if (a.d == 128) return a.causal ? launch_fwd8_d<128, true>(a) : launch_fwd8_d<128, false>(a);
     return a.causal ? launch_fwd8_d<64, true>(a) : launch_fwd8_d<64, false>(a);
 }
+
+unsigned debug_flags_fp8(bool clear) { return read_debug_flags(clear); }
 
 }  // namespace fa

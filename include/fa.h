@@ -299,7 +299,8 @@ int fa_version(void);
 
 /* Debug self-check ("FlashAttention 深度解析" section 二's invariants of the
  * online softmax): a library built with FA_DEBUG_CHECK (libfa_debug.so, built
- * beside libfa.so) has the bf16 forward and backward kernels record, as bits
+ * beside libfa.so) has every attention kernel (bf16 and float32 forward and
+ * backward, FP8 forward, paged decode and its merge) record, as bits
  * of a device flag word, a row that saw a finite score but whose sum of
  * weights is not positive (FA_DEBUG_ROW_SUM) and any output element of O,
  * lse, dQ, dK or dV that is NaN or infinite (FA_DEBUG_NON_FINITE; lse = -inf

@@ -82,3 +82,69 @@ def test_debug_build_flags_nan():
     flags = fa.fa_debug_flags(True, dl)
     assert flags & fa.DEBUG_NON_FINITE, flags
     assert fa.fa_debug_flags(False, dl) == 0  # cleared
+
+
+def test_debug_build_other_paths_clean_and_identical():
+    """The float32 path, the FP8 forward and the paged decode under the debug
+    build: no flag on valid inputs, outputs bit for bit those of libfa.so."""
+    say("[debug check] f32 fwd+bwd, FP8 fwd, paged decode")
+    dl = fa.load_debug()
+    plain = fa.load()
+    fa.fa_debug_flags(True, dl)
+    # float32 forward + backward
+    B, H, N, d = 1, 2, 200, 48
+    x = W.make_inputs(B, H, N, d, "f32", seed=73, with_do=True)
+    q, k, v, do = (to_device(x[n], "f32") for n in ("q", "k", "v", "do"))
+    outs = []
+    for lib in (plain, dl):
+        o, lse = torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = fa.workspace(B, H, N, d, q.device)
+        s = ctypes.c_float(0.15)
+        assert lib.fa_fwd_f32(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, N, d, s, 1, None, None) == 0
+        assert lib.fa_bwd_f32(_p(q), _p(k), _p(v), _p(o), _p(do), _p(lse), _p(dq), _p(dk), _p(dv), B, H, N, d, s, 1,
+                              None, _p(ws), ws.numel(), None) == 0
+        torch.cuda.synchronize()
+        outs.append((o, lse, dq, dk, dv))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    # FP8 forward (codes made by the plain library's quantizer)
+    B, H, N, d = 1, 2, 300, 128
+    x = W.make_inputs(B, H, N, d, "bf16", seed=74)
+    qb, kb, vb = (to_device(x[n], "bf16") for n in ("q", "k", "v"))
+    q8, qe = fa.quantize_fp8(qb)
+    k8, ke = fa.quantize_fp8(kb)
+    v8, ve = fa.quantize_fp8(vb)
+    outs = []
+    for lib in (plain, dl):
+        o, lse = torch.empty_like(qb), torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+        assert lib.fa_fwd_fp8(_p(q8), _p(qe), _p(k8), _p(ke), _p(v8), _p(ve), _p(o), _p(lse), B, H, N, d,
+                              ctypes.c_float(0.088), 1, None) == 0
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    # paged decode: split key ranges and their merge, and a sequence without keys
+    w = W.WORKLOADS["bf16_paged_decode_b16h32kv8d128_len1k_8k"]
+    xi = W.decode_inputs(w, seed=0)
+    dev = "cuda:0"
+    qd = to_device(xi["q"], "bf16")
+    kc, vc = to_device(xi["k_cache"], "bf16"), to_device(xi["v_cache"], "bf16")
+    bt = torch.from_numpy(xi["block_table"]).to(dev)
+    lens = xi["seqlens"].copy()
+    lens[3] = 0
+    sl = torch.from_numpy(lens).to(dev)
+    Bq, Hq, Nq, dd = qd.shape
+    outs = []
+    for lib in (plain, dl):
+        o, lse = torch.empty_like(qd), torch.empty((Bq, Hq, Nq), dtype=torch.float32, device=dev)
+        wsb = lib.fa_decode_workspace_size(Bq, Hq, w.Hkv, Nq, dd, w.page_size, bt.shape[1])
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        assert lib.fa_decode_paged(_p(qd), _p(kc), _p(vc), _p(bt), _p(sl), _p(o), _p(lse), Bq, Hq, w.Hkv, Nq, dd,
+                                   kc.shape[0], w.page_size, bt.shape[1], ctypes.c_float(w.scale), int(w.causal),
+                                   _p(ws), wsb, None) == 0
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    assert fa.fa_debug_flags(True, dl) == 0
