@@ -38,24 +38,28 @@ constexpr int kBrq = 64;   // queries per step
 // ---------------------------------------------------------------------------
 // D (64 or 128) bounds the row length hd; chunks past hd contribute nothing.
 template <int D>
+constexpr int rowdot_lanes() { return D <= 64 ? 8 : 16; }  // lanes per row: chunks per row, to a power of two
+
+template <int D>
 __global__ __launch_bounds__(256) void rowdot_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
                                                      const float* __restrict__ LSE, float* __restrict__ Dv,
                                                      float* __restrict__ lse2, long rows, int hd) {
-    constexpr int CPR = D / 8;  // 16-byte chunks per row (at most)
+    constexpr int CPR = D / 8;                   // 16-byte chunks per row (at most)
+    constexpr int LPR = rowdot_lanes<D>();       // lanes per row (chunks past CPR add zeros)
     const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long row = gid / CPR;
-    const int ch = (int)(gid % CPR);
+    const long row = gid / LPR;
+    const int ch = (int)(gid % LPR);
     float acc = 0.f;
-    if (row < rows && 8 * ch < hd) {
+    if (row < rows && ch < CPR && 8 * ch < hd) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * hd + ch * 8);
         const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * hd + ch * 8);
         const bf16x8 x = __builtin_bit_cast(bf16x8, a), y = __builtin_bit_cast(bf16x8, b);
 #pragma unroll
         for (int i = 0; i < 8; i++) acc = __builtin_fmaf((float)x[i], (float)y[i], acc);
     }
-    // reduce over the CPR lanes of the row (CPR divides 64, rows never straddle waves)
+    // reduce over the LPR lanes of the row (LPR divides 64, rows never straddle waves)
 #pragma unroll
-    for (int m = 1; m < CPR; m <<= 1) acc += __shfl_xor(acc, m);
+    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m);
     if (row < rows && ch == 0) {
         Dv[row] = acc;
         // a row without any allowed key (lse = -inf) gets +inf, so its P = 2^(c s - lse2) = 0
@@ -227,9 +231,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < C::SEG_PER_WAVE; i++) {
         constexpr int CPR = D / 8;  // chunks per row
-        const int seg = i * kWaves + wave;
-        const int row = seg * (512 / D) + lane / CPR;
-        const int col = 8 * ((lane % CPR) ^ swz_sigma<D>(row & 15));
+        const int g = (i * kWaves + wave) * 64 + lane;  // chunk position in the tile
+        const int row = g / CPR;
+        const int col = 8 * chunk_at<D>(row, g % CPR);
         seg_off[i] = (uint32_t)(row * hd + (col < hd ? col : 0)) * 2;
     }
     // copy k (0 .. NDMA-1) of the tile starting at query q0 into ring slot `buf`
@@ -264,17 +268,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(
     //   transposing reads of a dV / dK A operand, see lds_tr_operand_pad).
     uint32_t a_off[C::NKK], tr_lo[C::NDM], tr_hi[C::NDM];
     {
-        const int sig = swz_sigma<D>(l32 & 15);
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; kk++) a_off[kk] = l32 * C::RB + (((2 * kk + h) ^ sig) << 4);
+        for (int kk = 0; kk < C::NKK; kk++) a_off[kk] = l32 * C::RB + (chunk_pos<D>(l32, 2 * kk + h) << 4);
         const int sl = lane & 15, j = sl >> 2, q = sl & 3, g = (lane >> 4) & 1;
         const int r = 4 * h + j;
-        const int slo = swz_sigma<D>(r), shi = swz_sigma<D>(r + 8);
 #pragma unroll
         for (int dm = 0; dm < C::NDM; dm++) {
             const int cc = 4 * dm + 2 * g + (q >> 1);
-            tr_lo[dm] = r * C::RB + ((cc ^ slo) << 4) + (q & 1) * 8;
-            tr_hi[dm] = (r + 8) * C::RB + ((cc ^ shi) << 4) + (q & 1) * 8;
+            tr_lo[dm] = r * C::RB + (chunk_pos<D>(r, cc) << 4) + (q & 1) * 8;
+            tr_hi[dm] = (r + 8) * C::RB + (chunk_pos<D>(r + 8, cc) << 4) + (q & 1) * 8;
         }
     }
 
@@ -522,8 +524,9 @@ __device__ __forceinline__ void dq_load_tile_swz(rsrc_t r, bf16* tile, int kv0, 
     for (int i = 0; i < (SEGS + kWaves - 1) / kWaves; i++) {
         const int s = i * kWaves + wave;
         if (s < SEGS) {
-            const int row = s * (512 / D) + lane / CPR;
-            const int col = 8 * ((lane % CPR) ^ swz_sigma<D>(row & 15));
+            const int g = s * 64 + lane;  // chunk position in the tile
+            const int row = g / CPR;
+            const int col = 8 * chunk_at<D>(row, g % CPR);
             buf_load16_lds(r, tile + s * 512, ((uint32_t)(kv0 + row) * hd + (col < hd ? col : 0)) * 2);
         }
     }
@@ -584,17 +587,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     //   transposing reads of the dQ^T A operand, see lds_tr_operand_pad).
     uint32_t k_off[C::NKK], kt_lo[C::NDM], kt_hi[C::NDM];
     {
-        const int sig = swz_sigma<D>(l32 & 15);
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; kk++) k_off[kk] = l32 * C::RB + (((2 * kk + h) ^ sig) << 4);
+        for (int kk = 0; kk < C::NKK; kk++) k_off[kk] = l32 * C::RB + (chunk_pos<D>(l32, 2 * kk + h) << 4);
         const int sl = lane & 15, j = sl >> 2, q = sl & 3, g = (lane >> 4) & 1;
         const int r = 4 * h + j;
-        const int slo = swz_sigma<D>(r), shi = swz_sigma<D>(r + 8);
 #pragma unroll
         for (int dm = 0; dm < C::NDM; dm++) {
             const int cc = 4 * dm + 2 * g + (q >> 1);
-            kt_lo[dm] = r * C::RB + ((cc ^ slo) << 4) + (q & 1) * 8;
-            kt_hi[dm] = (r + 8) * C::RB + ((cc ^ shi) << 4) + (q & 1) * 8;
+            kt_lo[dm] = r * C::RB + (chunk_pos<D>(r, cc) << 4) + (q & 1) * 8;
+            kt_hi[dm] = (r + 8) * C::RB + (chunk_pos<D>(r + 8, cc) << 4) + (q & 1) * 8;
         }
     }
 
@@ -693,7 +694,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
             for (int w = 1; w < C::NKK; w <<= 1)
 #pragma unroll
-                for (int kk = 0; kk < C::NKK; kk += 2 * w) cs[kk] = cs[kk] + cs[kk + w];
+                for (int kk = 0; kk + w < C::NKK; kk += 2 * w) cs[kk] = cs[kk] + cs[kk + w];
             dd = cs[0];
             const float l = __uint_as_float(
                 __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4),
@@ -847,7 +848,7 @@ hipError_t launch_main(const BwdArgs& a) {
 template <int D>
 hipError_t launch_prep(const BwdArgs& a) {
     const long rows = (long)a.BH * a.N;
-    const long nthr = rows * (D / 8);
+    const long nthr = rows * rowdot_lanes<D>();
     hipLaunchKernelGGL(rowdot_kernel<D>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, a.stream,
                        (const bf16*)a.o, (const bf16*)a.dO, a.lse, a.ws_D, a.ws_lse2, rows, a.d);
     return hipGetLastError();
@@ -869,6 +870,12 @@ hipError_t launch_dq_all(const BwdArgs& a, bool fused) {
 
 hipError_t launch_dq_any(const BwdArgs& a, bool fused);
 
+// The tile width that holds a row: 64, 96 or 128.
+template <typename F, typename... A>
+hipError_t by_width(const BwdArgs& a, F w64, F w96, F w128, A... rest) {
+    return a.d <= 64 ? w64(a, rest...) : a.d <= 96 ? w96(a, rest...) : w128(a, rest...);
+}
+
 // The ALiBi bias is linear in the key over the live pairs only when they all
 // precede their query; the key-outer kernel also divides the slope by c.
 int variant_kind(const BwdArgs& a, bool divides_by_c) {
@@ -881,23 +888,23 @@ int variant_kind(const BwdArgs& a, bool divides_by_c) {
 }  // namespace
 
 hipError_t launch_bwd_prep_bf16(const BwdArgs& a) {
-    return a.d > 64 ? launch_prep<128>(a) : launch_prep<64>(a);
+    return a.d <= 64 ? launch_prep<64>(a) : a.d <= 96 ? launch_prep<96>(a) : launch_prep<128>(a);
 }
 
 hipError_t launch_bwd_main_bf16(const BwdArgs& a) {
     switch (variant_kind(a, true)) {
-        case 0: return a.d > 64 ? launch_main_all<128, 0>(a) : launch_main_all<64, 0>(a);
-        case 1: return a.d > 64 ? launch_main_all<128, 1>(a) : launch_main_all<64, 1>(a);
-        default: return a.d > 64 ? launch_main_all<128, 2>(a) : launch_main_all<64, 2>(a);
+        case 0: return by_width(a, launch_main_all<64, 0>, launch_main_all<96, 0>, launch_main_all<128, 0>);
+        case 1: return by_width(a, launch_main_all<64, 1>, launch_main_all<96, 1>, launch_main_all<128, 1>);
+        default: return by_width(a, launch_main_all<64, 2>, launch_main_all<96, 2>, launch_main_all<128, 2>);
     }
 }
 
 namespace {
 hipError_t launch_dq_any(const BwdArgs& a, bool fused) {
     switch (variant_kind(a, false)) {
-        case 0: return a.d > 64 ? launch_dq_all<128, 0>(a, fused) : launch_dq_all<64, 0>(a, fused);
-        case 1: return a.d > 64 ? launch_dq_all<128, 1>(a, fused) : launch_dq_all<64, 1>(a, fused);
-        default: return a.d > 64 ? launch_dq_all<128, 2>(a, fused) : launch_dq_all<64, 2>(a, fused);
+        case 0: return by_width(a, launch_dq_all<64, 0>, launch_dq_all<96, 0>, launch_dq_all<128, 0>, fused);
+        case 1: return by_width(a, launch_dq_all<64, 1>, launch_dq_all<96, 1>, launch_dq_all<128, 1>, fused);
+        default: return by_width(a, launch_dq_all<64, 2>, launch_dq_all<96, 2>, launch_dq_all<128, 2>, fused);
     }
 }
 }  // namespace

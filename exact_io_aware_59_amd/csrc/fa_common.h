@@ -100,6 +100,32 @@ __device__ __forceinline__ int swz_sigma(int r) {
     if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
     else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
+// Chunk position of logical 16-byte chunk c in row r of a swizzled tile, and
+// its inverse.  64- and 128-wide rows XOR the chunk index with sigma(r).
+// 96-wide rows (12 chunks, not a power of two) rotate it by (r >> 2) mod 4
+// instead: for 16 consecutive rows and one chunk, rows r = 4a + b sit at
+// 16-byte units 12r + pos = 4(3b mod 4) + (c + a) mod 12 (mod 16), which are
+// all distinct; for the 4 rows 4h .. 4h+3 of a transposing read (one shared
+// rotation) and 4 consecutive chunks, the 4 positions have distinct residues
+// mod 4 and the rows distinct multiples of 4, again 16 distinct units.
+template <int D>
+__device__ __forceinline__ int chunk_pos(int r, int c) {
+    if constexpr (D == 96) {
+        const int p = c + ((r >> 2) & 3);
+        return p >= 12 ? p - 12 : p;
+    } else {
+        return c ^ swz_sigma<D>(r & 15);
+    }
+}
+template <int D>
+__device__ __forceinline__ int chunk_at(int r, int p) {
+    if constexpr (D == 96) {
+        const int c = p - ((r >> 2) & 3);
+        return c < 0 ? c + 12 : c;
+    } else {
+        return p ^ swz_sigma<D>(r & 15);
+    }
+}
 // Element offset of logical (row, col) in a D-wide swizzled tile.
 template <int D>
 __device__ __forceinline__ int swz(int row, int col) {
