@@ -291,8 +291,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(
 }
 
 // Per query row: merge the key ranges' (O, max, sum).  One wave per row: the
-// lanes take the ranges' maxima in parallel (wave max), then every lane owns
-// D/64 output columns and sums the ranges' partial rows with their weights.
+// lanes take the ranges' maxima in parallel (wave max) and then one range's
+// weight and weighted sum each; every lane owns D/64 output columns and sums
+// the ranges' partial rows, sixteen rows' loads in flight at a time, with
+// the weights passed between lanes.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ ws_o,
                                                            const float* __restrict__ ws_ml,
@@ -307,6 +309,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     const int L = max(0, min(seqlens[b], max_keys));
     const int nvalid = min(n_parts, (L + kpp - 1) / kpp);
     const float* ml = ws_ml + (size_t)row * n_parts * 2;
+    // the ranges' maxima, a lane per range (64 at a time)
     float M = -INFINITY;
     for (int p = lane; p < nvalid; p += 64) M = fmaxf(M, ml[2 * p]);
 #pragma unroll
@@ -317,29 +320,30 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     float lsum = 0.f;
     if (M != -INFINITY) {
         const float* src = ws_o + (size_t)row * n_parts * D + lane * PER;
-        int p = 0;
-        for (; p + 4 <= nvalid; p += 4) {  // four ranges' loads in flight
-            float w[4], ov[4][PER];
+        for (int p0 = 0; p0 < nvalid; p0 += 64) {
+            // lane q: range p0 + q's weight 2^(m - M) (0 for a range with no allowed key) and its sum
+            const int pq = p0 + lane;
+            const float wq = pq < nvalid ? exp2f_hw(ml[2 * pq] - M) : 0.f;
+            lsum += pq < nvalid ? wq * ml[2 * pq + 1] : 0.f;
+            const int n = min(64, nvalid - p0);
+            for (int u0 = 0; u0 < n; u0 += 16) {
+                // sixteen ranges' partial rows in flight at once, weights by lane exchange
+                float ov[16][PER];
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                w[u] = ml[2 * (p + u)];
+                for (int u = 0; u < 16; u++)
 #pragma unroll
-                for (int e = 0; e < PER; e++) ov[u][e] = src[(size_t)(p + u) * D + e];
-            }
+                    for (int e = 0; e < PER; e++)
+                        ov[u][e] = u0 + u < n ? src[(size_t)(p0 + u0 + u) * D + e] : 0.f;
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const float wu = exp2f_hw(w[u] - M);  // 0 for a range with no allowed key
-                lsum += wu * ml[2 * (p + u) + 1];
+                for (int u = 0; u < 16; u++) {
+                    const float wu = __shfl(wq, u0 + u);
 #pragma unroll
-                for (int e = 0; e < PER; e++) acc[e] += wu * ov[u][e];
+                    for (int e = 0; e < PER; e++) acc[e] += wu * ov[u][e];
+                }
             }
         }
-        for (; p < nvalid; p++) {
-            const float wu = exp2f_hw(ml[2 * p] - M);
-            lsum += wu * ml[2 * p + 1];
 #pragma unroll
-            for (int e = 0; e < PER; e++) acc[e] += wu * src[(size_t)p * D + e];
-        }
+        for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
     }
     FA_CHECK(M == -INFINITY || lsum > 0.f, kDbgRowSum);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
