@@ -59,7 +59,7 @@ def kernel_sources(w) -> list:
     if getattr(w, "precision", "bf16") == "fp8":
         return ["fa_common.h", "fa_fp8.hip"]
     return ["fa_common.h", "fa_fwd.h", "fa_fwd.hip", "fa_fwd_64.hip", "fa_fwd_96.hip", "fa_fwd_128.hip",
-            "fa_fwd_256.hip", "fa_bwd.hip"]
+            "fa_fwd_192.hip", "fa_fwd_256.hip", "fa_bwd.hip"]
 
 # kernel-name substring -> entry point that launches it
 # (the benchmarked step launches the dQ kernel through fa_bwd_dq_first, before fa_bwd_main)

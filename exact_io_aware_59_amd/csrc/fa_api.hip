@@ -479,7 +479,8 @@ int fa_debug_flags(int clear) {
 #ifdef FA_DEBUG_CHECK
     if (hipDeviceSynchronize() != hipSuccess) return -1;
     const unsigned f = fa::debug_flags_fwd_w64(clear) | fa::debug_flags_fwd_w96(clear) |
-                       fa::debug_flags_fwd_w128(clear) | fa::debug_flags_fwd_w256(clear) | fa::debug_flags_bwd(clear) |
+                       fa::debug_flags_fwd_w128(clear) | fa::debug_flags_fwd_w192(clear) | fa::debug_flags_fwd_w256(clear) |
+                       fa::debug_flags_bwd(clear) |
                        fa::debug_flags_f32(clear) | fa::debug_flags_decode(clear) | fa::debug_flags_fp8(clear);
     return f == ~0u ? -1 : (int)f;
 #else

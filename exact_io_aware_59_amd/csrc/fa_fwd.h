@@ -231,14 +231,14 @@ __device__ __forceinline__ void tile_pv(const bf16* vl, const bf16x8 (&pb)[FwdCf
 // the online-softmax rescale ("FlashAttention 深度解析" section 二) and writes
 // the block.
 //
-// D is the tile width: 64, 96, 128 or 256.  The tensors' rows hold hd <= D
+// D is the tile width: 64, 96, 128, 192 or 256.  The tensors' rows hold hd <= D
 // elements (a multiple of 16); Q columns from hd on are zero in registers, so
 // the padded columns of the K and V tiles never reach a score.  PAD = false
 // when hd == D: the row length is then the compile-time D (a runtime length
 // costs registers the plain kernels do not have).  D = 256 runs one
 // workgroup of four waves per CU (its tiles take 141 KB of LDS).
 template <int D, bool CAUSAL, bool MASK, int VK, int KS, bool PAD>
-__global__ __launch_bounds__(64 * kWaves * KS, D == 256 ? 1 : 2 / KS) void fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * kWaves * KS, D >= 192 ? 1 : 2 / KS) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int hd_arg, float c, uint32_t qsign,
     const uint8_t* __restrict__ mask, int nb, int nqb, int n_items, int H, int wl, int wr,
@@ -684,7 +684,7 @@ hipError_t launch(const FwdArgs& a) {
     const int per_head = CAUSAL ? (nqb + 1) / 2 : nqb;
     const int n_items = a.BH * per_head;
     const bool pad = a.d != D;
-    if constexpr (D == 256 || D == 96) {  // two tile groups: LDS (256) or the O exchange (96) would not fit
+    if constexpr (D >= 192 || D == 96) {  // two tile groups: LDS (192, 256) or the O exchange (96) would not fit
         return pad ? launch_ks<D, CAUSAL, MASK, VK, 1, true>(a, nqb, n_items)
                    : launch_ks<D, CAUSAL, MASK, VK, 1, false>(a, nqb, n_items);
     } else {

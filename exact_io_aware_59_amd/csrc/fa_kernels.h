@@ -116,6 +116,7 @@ hipError_t launch_fwd_fp8(const F8FwdArgs& a);
 // unless built with FA_DEBUG_CHECK); synchronous, `clear` resets them.
 unsigned debug_flags_fwd_w64(bool clear);
 unsigned debug_flags_fwd_w96(bool clear);
+unsigned debug_flags_fwd_w192(bool clear);
 unsigned debug_flags_f32(bool clear);
 unsigned debug_flags_decode(bool clear);
 unsigned debug_flags_fp8(bool clear);

@@ -176,16 +176,24 @@ def test_unsupported_head_sizes_raise():
     assert e.value.status == 2
 
 
-def test_full_size_d256_fwd_sampled_rows():
+@pytest.mark.parametrize("d", [256, 160])
+def test_full_size_wide_fwd_sampled_rows(d):
+    """Causal B=1 H=8 N=8192 forward at d = 256 (the benchmark workload) and
+    d = 160 (a 192-wide tile with padded columns): 512 sampled rows."""
     w = W.WORKLOADS["bf16_causal_fwd_b1h8n8192d256"]
-    say(f"[full fwd] {w.name}")
-    x = W.workload_inputs(w, seed=0)
+    say(f"[full fwd] B={w.B} H={w.H} N={w.N} d={d} causal")
+    if d == w.d:
+        x = W.workload_inputs(w, seed=0)
+        scale = w.scale
+    else:
+        x = W.make_inputs(w.B, w.H, w.N, d, "bf16", seed=0)
+        scale = float(np.float32(1 / math.sqrt(d)))
     q, k, v = (to_device(x[n], "bf16") for n in "qkv")
-    o, lse = fa.forward(q, k, v, w.scale, w.causal)
+    o, lse = fa.forward(q, k, v, scale, w.causal)
     torch.cuda.synchronize()
     rows = W.sample_rows(w.B * w.H, w.N, 512, seed=W.SEED_ROWS)
-    o_ref, l_ref = oracle.attn_fwd_rows(x["q"].values, x["k"].values, x["v"].values, w.scale, rows, w.causal)
-    of = o.reshape(w.B * w.H, w.N, w.d)
+    o_ref, l_ref = oracle.attn_fwd_rows(x["q"].values, x["k"].values, x["v"].values, scale, rows, w.causal)
+    of = o.reshape(w.B * w.H, w.N, d)
     lf = lse.reshape(w.B * w.H, w.N)
     i0 = torch.from_numpy(rows[:, 0]).to("cuda:0")
     i1 = torch.from_numpy(rows[:, 1]).to("cuda:0")
