@@ -8,14 +8,18 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dK = scale dS^T Q,  dQ = scale dS K
 // -- the five matrix products of "FlashAttention 深度解析" section 四.
 //
-// Three launches on one stream:
-//   1. rowdot:  D_i = rowsum(dO o O) and lse_i * log2(e), fp32;
-//   2. main:    one workgroup per (batch, head, block of 128 keys); dK and dV
-//               accumulate in registers while it sweeps the query tiles its mask
-//               allows (the K/V-outer order of the IO-Awareness page section 2.3);
-//   3. dq:      one workgroup per (batch, head, block of 128 queries) sweeping
-//               the key tiles (Q-outer), recomputing S and dP and accumulating
-//               dQ = dS K in registers.
+// Kernels:
+//   rowdot: D_i = rowsum(dO o O) and lse_i * log2(e), fp32 (the preprocessing
+//           stage on its own);
+//   main:   one workgroup per (batch, head, block of 128 keys); dK and dV
+//           accumulate in registers while it sweeps the query tiles its mask
+//           allows (the K/V-outer order of the IO-Awareness page section 2.3);
+//   dq:     one workgroup per (batch, head, block of 128 queries) sweeping the
+//           key tiles (Q-outer), recomputing S and dP and accumulating
+//           dQ = dS K in registers; given O and lse it also does the
+//           preprocessing of its own rows.
+// fa_bwd launches dq (with the preprocessing) and then main; the stages can
+// also run as rowdot, main, dq, with the same bits.
 // Splitting dQ off costs two extra tile products (S and dP are recomputed) but
 // replaces fp32 atomic accumulation of dQ, which measured slower than the
 // extra matrix work on this part; every output is deterministic ("FlashAttention
