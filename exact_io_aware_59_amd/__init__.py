@@ -31,7 +31,7 @@ __all__ = [
     "forward", "backward", "workspace", "fa_decode_workspace_size", "fa_decode_paged", "decode_workspace",
     "decode_paged", "fa_fp8_quantize", "fa_fwd_fp8", "quantize_fp8", "forward_fp8", "FP8_BLOCK",
     "MASK_BLOCK", "ABI_VERSION", "fa_bwd_noalloc", "NOALLOC_MAX_ROWS", "load_debug", "debug_library_path",
-    "fa_debug_flags", "DEBUG_ROW_SUM", "DEBUG_NON_FINITE",
+    "fa_debug_flags", "DEBUG_ROW_SUM", "DEBUG_NON_FINITE", "attention",
 ]
 
 MASK_BLOCK = 128
@@ -594,3 +594,50 @@ def backward(q, k, v, o, do, lse, scale: Optional[float] = None, causal: bool = 
         fn = fa_bwd_ex if q.dtype == torch.bfloat16 else fa_bwd_f32_ex
         fn(q, k, v, o, do, lse, dq, dk, dv, scale, causal, blockmask, window, alibi_slopes, ws, stream)
     return dq, dk, dv
+
+
+_attention_fn = None
+
+
+def _attention_function():
+    """The autograd Function behind ``attention`` (built on first use, so that
+    importing the binding does not import torch)."""
+    global _attention_fn
+    if _attention_fn is None:
+        import torch
+
+        class _Attention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, scale, causal, blockmask, window, alibi_slopes):
+                o, lse = forward(q, k, v, scale, causal, blockmask, window=window, alibi_slopes=alibi_slopes)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.args = (scale, causal, blockmask, window, alibi_slopes)
+                ctx.mark_non_differentiable(lse)
+                return o, lse
+
+            @staticmethod
+            def backward(ctx, do, _dlse):
+                q, k, v, o, lse = ctx.saved_tensors
+                scale, causal, blockmask, window, alibi_slopes = ctx.args
+                dq, dk, dv = backward(q, k, v, o, do.contiguous(), lse, scale, causal, blockmask,
+                                      window=window, alibi_slopes=alibi_slopes)
+                return dq, dk, dv, None, None, None, None, None
+
+        _attention_fn = _Attention
+    return _attention_fn
+
+
+def attention(q, k, v, scale: Optional[float] = None, causal: bool = False, blockmask=None, window=None,
+              alibi_slopes=None, return_lse: bool = False):
+    """Exact attention softmax(scale Q K^T [+ mask / window / ALiBi]) V with autograd.
+
+    q, k, v: contiguous [B, H, N, d] bf16 (bf16 kernels) or float32 (fp32
+    kernels) tensors on the GPU; scale defaults to 1/sqrt(d).  The forward
+    runs ``forward`` and saves (q, k, v, O, lse); the backward runs
+    ``backward`` on the incoming dO (made contiguous), so the gradients are
+    those of fa_bwd(_ex) / fa_bwd_f32(_ex).  lse (float32 [B, H, N], natural
+    log) is returned too with ``return_lse`` and carries no gradient."""
+    d = q.shape[-1]
+    scale = _default_scale(d) if scale is None else scale
+    o, lse = _attention_function().apply(q, k, v, scale, causal, blockmask, window, alibi_slopes)
+    return (o, lse) if return_lse else o
