@@ -402,11 +402,14 @@ __global__ __launch_bounds__(64 * kWaves * KS, D >= 192 ? 1 : 2 / KS) void fwd_b
 
         // this group's m-th tile and the number of steps (the same for every
         // group, so that all waves pass the same barriers); a group's tiles past
-        // the list start at row N: they read as zero and are masked out
+        // the list start at row N: they read as zero and are masked out.  The
+        // variant kernels (exact running max) take the tiles from the last one
+        // down: with a causal ALiBi bias the largest scores sit at the diagonal,
+        // so the max is found on the first tiles and O is rarely rescaled after.
         const int n_steps = (tl.n + KS - 1) / KS;
         auto kvg = [&](int m) -> int {
             const int t = KS * m + group;
-            return t < tl.n ? tl.kv0(t) : N;
+            return t < tl.n ? tl.kv0(VK != 0 ? tl.n - 1 - t : t) : N;
         };
 
         // ---- prologue: K0, V0, K1 in flight; S(0) and its max ----
